@@ -1,0 +1,228 @@
+"""Python face of the CPU oracle (``oracle/oracle.c``).
+
+TEST INFRASTRUCTURE, NOT PRODUCT CODE: only the test suite, the smoke check
+and the benchmark's CPU-baseline leg import this module.  It shares no code
+with the HIP library in ``expert_ffn_amd`` and never imports it.
+
+The wrappers below only marshal numpy arrays into the C routines; every step of
+the method is computed in ``oracle.c``.  Enumerations are this module's own
+(same numbering as the library's public header, which is a format both sides
+state independently).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "oracle.c")
+LIB = os.path.join(HERE, "liboracle.so")
+
+W_BF16, W_INT8_ROW, W_INT4_G64 = 0, 1, 2
+ACT_GELU_TANH, ACT_SILU = 0, 1
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile liboracle.so with gcc (no FMA contraction, no fast-math)."""
+    if force or not os.path.exists(LIB) or os.path.getmtime(LIB) < os.path.getmtime(SRC):
+        tmp = LIB + ".tmp%d" % os.getpid()
+        cmd = ["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fopenmp",
+               "-fPIC", "-shared", SRC, "-o", tmp, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, LIB)
+    return LIB
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB) or os.path.getmtime(LIB) < os.path.getmtime(SRC):
+            build(force=False)
+        _lib = ctypes.CDLL(LIB)
+        _declare(_lib)
+    return _lib
+
+
+def _declare(L):
+    P = ctypes.c_void_p
+    i32, i64, u64 = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64
+    L.oracle_f32_to_bf16.argtypes = [P, P, i64]
+    L.oracle_bf16_to_f32.argtypes = [P, P, i64]
+    L.oracle_route_topk.argtypes = [P, i32, i32, i32, i32, P, P]
+    L.oracle_route_topk.restype = ctypes.c_int
+    L.oracle_permute.argtypes = [P, i32, i32, i32, P, P, P, P, P]
+    L.oracle_permute.restype = ctypes.c_int
+    L.oracle_quantize_int8.argtypes = [P, i32, i32, P, P]
+    L.oracle_quantize_int4.argtypes = [P, i32, i32, P, P]
+    L.oracle_blob_layout.argtypes = [i32, i32, i32, P]
+    L.oracle_blob_layout.restype = ctypes.c_int
+    L.oracle_pack_expert.argtypes = [i32, P, P, i32, i32, P]
+    L.oracle_pack_expert.restype = ctypes.c_int
+    L.oracle_dequant.argtypes = [P, i32, i32, i32, i32, P]
+    L.oracle_dequant.restype = ctypes.c_int
+    L.oracle_act.argtypes = [i32, P, P, i64]
+    L.oracle_expert_ffn.argtypes = [P, u64, P, i32, i32, i32, i32, i32, P, i32, i32, P, P, i32, P, P]
+    L.oracle_expert_ffn.restype = ctypes.c_int
+    L.oracle_combine.argtypes = [P, P, P, i32, i32, P, i32, P]
+    L.oracle_combine.restype = ctypes.c_int
+
+
+def _p(a: np.ndarray):
+    assert a.flags["C_CONTIGUOUS"], "oracle inputs must be C-contiguous"
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _check(rc, what):
+    if rc != 0:
+        raise ValueError(f"oracle {what}: invalid arguments (status {rc})")
+
+
+# ---------------------------------------------------------------- bf16 ----
+def f32_to_bf16(x) -> np.ndarray:
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.empty(x.shape, dtype=np.uint16)
+    lib().oracle_f32_to_bf16(_p(x), _p(out), x.size)
+    return out
+
+
+def bf16_to_f32(h) -> np.ndarray:
+    h = np.ascontiguousarray(h, dtype=np.uint16)
+    out = np.empty(h.shape, dtype=np.float32)
+    lib().oracle_bf16_to_f32(_p(h), _p(out), h.size)
+    return out
+
+
+# ------------------------------------------------------------- routing ----
+def route_topk(logits, k: int, renorm: int = 1):
+    logits = np.ascontiguousarray(logits, dtype=np.float32)
+    T, E = logits.shape
+    ids = np.empty((T, k), dtype=np.int32)
+    w = np.empty((T, k), dtype=np.float32)
+    _check(lib().oracle_route_topk(_p(logits), T, E, k, renorm, _p(ids), _p(w)), "route_topk")
+    return ids, w
+
+
+def permute(ids, E: int, slot_of):
+    ids = np.ascontiguousarray(ids, dtype=np.int32)
+    T, k = ids.shape
+    slot_of = np.ascontiguousarray(slot_of, dtype=np.int32)
+    assert slot_of.shape == (E,)
+    offsets = np.empty(E + 1, dtype=np.int32)
+    sorted_route = np.empty(T * k, dtype=np.int32)
+    route_pos = np.empty(T * k, dtype=np.int32)
+    nd = np.zeros(1, dtype=np.int32)
+    _check(lib().oracle_permute(_p(ids), T, k, E, _p(slot_of), _p(offsets), _p(sorted_route),
+                                _p(route_pos), _p(nd)), "permute")
+    return offsets, sorted_route, route_pos, int(nd[0])
+
+
+# -------------------------------------------------------- quantisation ----
+def quantize_int8(w_bf16):
+    w = np.ascontiguousarray(w_bf16, dtype=np.uint16)
+    N, K = w.shape
+    q = np.empty((N, K), dtype=np.int8)
+    s = np.empty(N, dtype=np.float32)
+    lib().oracle_quantize_int8(_p(w), N, K, _p(q), _p(s))
+    return q, s
+
+
+def quantize_int4(w_bf16):
+    w = np.ascontiguousarray(w_bf16, dtype=np.uint16)
+    N, K = w.shape
+    assert K % 64 == 0
+    q = np.empty((N, K // 2), dtype=np.uint8)
+    s = np.empty((N, K // 64), dtype=np.uint16)
+    lib().oracle_quantize_int4(_p(w), N, K, _p(q), _p(s))
+    return q, s
+
+
+def blob_layout(fmt: int, H: int, FF: int):
+    off = np.zeros(5, dtype=np.uint64)
+    _check(lib().oracle_blob_layout(fmt, H, FF, _p(off)), "blob_layout")
+    return [int(v) for v in off]
+
+
+def expert_bytes(fmt: int, H: int, FF: int) -> int:
+    return blob_layout(fmt, H, FF)[4]
+
+
+def pack_expert(fmt: int, w13_bf16, w2_bf16, H: int, FF: int) -> np.ndarray:
+    w13 = np.ascontiguousarray(w13_bf16, dtype=np.uint16)
+    w2 = np.ascontiguousarray(w2_bf16, dtype=np.uint16)
+    assert w13.shape == (2 * FF, H) and w2.shape == (H, FF)
+    blob = np.empty(expert_bytes(fmt, H, FF), dtype=np.uint8)
+    _check(lib().oracle_pack_expert(fmt, _p(w13), _p(w2), H, FF, _p(blob)), "pack_expert")
+    return blob
+
+
+def dequant(blob, fmt: int, H: int, FF: int, which: int) -> np.ndarray:
+    blob = np.ascontiguousarray(blob, dtype=np.uint8)
+    rows, K = (H, FF) if which else (2 * FF, H)
+    out = np.empty((rows, K), dtype=np.float64)
+    _check(lib().oracle_dequant(_p(blob), fmt, H, FF, which, _p(out)), "dequant")
+    return out
+
+
+def act(kind: int, g) -> np.ndarray:
+    g = np.ascontiguousarray(g, dtype=np.float64)
+    out = np.empty_like(g)
+    lib().oracle_act(kind, _p(g), _p(out), g.size)
+    return out
+
+
+# ---------------------------------------------------------- expert FFN ----
+def expert_ffn(pool, slot_bytes: int, slot_of, E: int, H: int, FF: int, fmt: int, act_kind: int,
+               x_f32, ids, routes):
+    """fp64 outputs o[len(routes), H] of the listed routes, and a kept flag per route."""
+    pool = np.ascontiguousarray(pool, dtype=np.uint8)
+    slot_of = np.ascontiguousarray(slot_of, dtype=np.int32)
+    x = np.ascontiguousarray(x_f32, dtype=np.float32)
+    ids = np.ascontiguousarray(ids, dtype=np.int32)
+    T, k = ids.shape
+    assert x.shape == (T, H)
+    routes = np.ascontiguousarray(routes, dtype=np.int32)
+    o = np.empty((routes.size, H), dtype=np.float64)
+    ok = np.empty(routes.size, dtype=np.int32)
+    _check(lib().oracle_expert_ffn(_p(pool), slot_bytes, _p(slot_of), E, H, FF, fmt, act_kind, _p(x),
+                                   T, k, _p(ids), _p(routes), routes.size, _p(o), _p(ok)),
+           "expert_ffn")
+    return o, ok
+
+
+def combine(o_rows, route_row, w, tokens):
+    """y[len(tokens), H] = sum_j w[t, j] * o_rows[route_row[q, j]] (row -1 = dropped)."""
+    o_rows = np.ascontiguousarray(o_rows, dtype=np.float64)
+    route_row = np.ascontiguousarray(route_row, dtype=np.int32)
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    tokens = np.ascontiguousarray(tokens, dtype=np.int32)
+    k = w.shape[1]
+    H = o_rows.shape[1]
+    assert route_row.shape == (tokens.size, k)
+    y = np.empty((tokens.size, H), dtype=np.float64)
+    _check(lib().oracle_combine(_p(o_rows), _p(route_row), _p(w), k, H, _p(tokens), tokens.size,
+                                _p(y)), "combine")
+    return y
+
+
+def moe_layer(logits, x_f32, pool, slot_bytes: int, slot_of, H: int, FF: int, fmt: int,
+              act_kind: int, k: int, renorm: int = 1, tokens=None):
+    """The whole layer for the listed tokens (all by default): route, permute,
+    expert FFN of those tokens' routes, combine.  Returns a dict of every step."""
+    T, E = logits.shape
+    ids, w = route_topk(logits, k, renorm)
+    offsets, sorted_route, route_pos, n_dropped = permute(ids, E, slot_of)
+    if tokens is None:
+        tokens = np.arange(T, dtype=np.int32)
+    tokens = np.asarray(tokens, dtype=np.int32)
+    routes = (tokens[:, None] * k + np.arange(k, dtype=np.int32)[None, :]).reshape(-1)
+    o, ok = expert_ffn(pool, slot_bytes, slot_of, E, H, FF, fmt, act_kind, x_f32, ids, routes)
+    route_row = np.where(ok.reshape(tokens.size, k) > 0,
+                         np.arange(routes.size, dtype=np.int32).reshape(tokens.size, k), -1)
+    y = combine(o, route_row, w, tokens)
+    return dict(ids=ids, w=w, offsets=offsets, sorted_route=sorted_route, route_pos=route_pos,
+                n_dropped=n_dropped, routes=routes, o=o, kept=ok, tokens=tokens, y=y)
