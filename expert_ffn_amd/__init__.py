@@ -1,0 +1,163 @@
+"""Python binding of libexpert_ffn.so (the C ABI in include/expert_ffn.h).
+
+Argument marshalling only: every function passes torch tensors' device
+pointers, sizes and torch's current HIP stream to the C entry point of the same
+name and raises MoeError on a non-OK status.  There is no fallback: without the
+built library, importing the first entry point raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libexpert_ffn.so")
+
+F32, BF16 = 0, 1
+W_BF16, W_INT8_ROW, W_INT4_G64 = 0, 1, 2
+ACT_GELU_TANH, ACT_SILU = 0, 1
+FMT_NAMES = {"bf16": W_BF16, "int8": W_INT8_ROW, "int4": W_INT4_G64}
+
+_lib = None
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(f"status {status}: {message}")
+        self.status = status
+
+
+def lib():
+    """The loaded library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                              "(there is no CPU fallback)")
+        L = ctypes.CDLL(LIB_PATH)
+        P, i32, u64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint64, ctypes.c_size_t
+        L.moe_last_error.restype = ctypes.c_char_p
+        L.moe_expert_bytes.argtypes = [i32, i32, i32]
+        L.moe_expert_bytes.restype = u64
+        L.moe_blob_layout.argtypes = [i32, i32, i32, P]
+        L.moe_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
+        L.moe_workspace_bytes.restype = sz
+        L.moe_route_topk.argtypes = [P, i32, i32, i32, i32, P, P, P]
+        L.moe_permute.argtypes = [P, i32, i32, i32, P, P, P, P, P, P]
+        ffn = [P, u64, P, i32, i32, i32, i32, i32, P, i32, i32, i32, P, P, P, i32, P, sz, P]
+        for name in ("moe_expert_ffn", "moe_ffn_gate_up", "moe_ffn_down"):
+            getattr(L, name).argtypes = ffn
+        L.moe_combine.argtypes = [P, i32, P, P, i32, i32, i32, P, i32, P]
+        L.moe_quantize.argtypes = [i32, P, i32, i32, P, P, P]
+        L.moe_pack_expert.argtypes = [i32, P, P, i32, i32, P, P]
+        L.moe_set_ffn_path.argtypes = [i32]
+        for name in ("moe_blob_layout", "moe_route_topk", "moe_permute", "moe_expert_ffn",
+                     "moe_ffn_gate_up", "moe_ffn_down", "moe_combine", "moe_quantize",
+                     "moe_pack_expert", "moe_set_ffn_path"):
+            getattr(L, name).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _check(status):
+    if status != 0:
+        raise MoeError(status, lib().moe_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dt(t):
+    import torch
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+# ------------------------------------------------------------ host queries --
+def expert_bytes(fmt: int, H: int, FF: int) -> int:
+    return int(lib().moe_expert_bytes(fmt, H, FF))
+
+
+def blob_layout(fmt: int, H: int, FF: int):
+    off = (ctypes.c_uint64 * 5)()
+    _check(lib().moe_blob_layout(fmt, H, FF, off))
+    return [int(v) for v in off]
+
+
+def workspace_bytes(T: int, k: int, E: int, H: int, FF: int, fmt: int) -> int:
+    return int(lib().moe_workspace_bytes(T, k, E, H, FF, fmt))
+
+
+def set_ffn_path(path: int):
+    _check(lib().moe_set_ffn_path(path))
+
+
+# ------------------------------------------------------------- the steps --
+def route_topk(logits, k: int, topk_ids, topk_w, renorm: int = 1, stream=None):
+    T, E = logits.shape
+    _check(lib().moe_route_topk(_ptr(logits), T, E, k, renorm, _ptr(topk_ids), _ptr(topk_w),
+                                _stream(stream)))
+
+
+def permute(topk_ids, E: int, slot_of, expert_offsets, sorted_route, route_pos, n_dropped,
+            stream=None):
+    T, k = topk_ids.shape
+    _check(lib().moe_permute(_ptr(topk_ids), T, k, E, _ptr(slot_of), _ptr(expert_offsets),
+                             _ptr(sorted_route), _ptr(route_pos), _ptr(n_dropped), _stream(stream)))
+
+
+def _ffn(name, pool, slot_bytes, slot_of, E, H, FF, fmt, act, x, T, k, expert_offsets,
+         sorted_route, out_routes, ws, stream):
+    x_dt = _dt(x) if x is not None else BF16
+    o_dt = _dt(out_routes) if out_routes is not None else F32
+    _check(getattr(lib(), name)(_ptr(pool), slot_bytes, _ptr(slot_of), E, H, FF, fmt, act, _ptr(x),
+                                x_dt, T, k, _ptr(expert_offsets), _ptr(sorted_route),
+                                _ptr(out_routes), o_dt, _ptr(ws), ws.numel() * ws.element_size(),
+                                _stream(stream)))
+
+
+def expert_ffn(pool, slot_bytes, slot_of, E, H, FF, fmt, act, x, k, expert_offsets, sorted_route,
+               out_routes, ws, stream=None):
+    _ffn("moe_expert_ffn", pool, slot_bytes, slot_of, E, H, FF, fmt, act, x, x.shape[0], k,
+         expert_offsets, sorted_route, out_routes, ws, stream)
+
+
+def ffn_gate_up(pool, slot_bytes, slot_of, E, H, FF, fmt, act, x, k, expert_offsets,
+                sorted_route, ws, stream=None):
+    _ffn("moe_ffn_gate_up", pool, slot_bytes, slot_of, E, H, FF, fmt, act, x, x.shape[0], k,
+         expert_offsets, sorted_route, None, ws, stream)
+
+
+def ffn_down(pool, slot_bytes, slot_of, E, H, FF, fmt, T, k, expert_offsets, sorted_route,
+             out_routes, ws, stream=None):
+    _ffn("moe_ffn_down", pool, slot_bytes, slot_of, E, H, FF, fmt, ACT_GELU_TANH, None, T, k,
+         expert_offsets, sorted_route, out_routes, ws, stream)
+
+
+def combine(out_routes, topk_w, route_pos, y, stream=None):
+    T, H = y.shape
+    k = topk_w.numel() // T if T else 1
+    _check(lib().moe_combine(_ptr(out_routes), _dt(out_routes), _ptr(topk_w), _ptr(route_pos), T, k,
+                             H, _ptr(y), _dt(y), _stream(stream)))
+
+
+def quantize(fmt: int, w_bf16, q, scales, stream=None):
+    N, K = w_bf16.shape
+    _check(lib().moe_quantize(fmt, _ptr(w_bf16), N, K, _ptr(q), _ptr(scales), _stream(stream)))
+
+
+def pack_expert(fmt: int, w13_bf16, w2_bf16, blob, stream=None):
+    H = w13_bf16.shape[1]
+    FF = w2_bf16.shape[1]
+    _check(lib().moe_pack_expert(fmt, _ptr(w13_bf16), _ptr(w2_bf16), H, FF, _ptr(blob),
+                                 _stream(stream)))

@@ -1,0 +1,242 @@
+// C ABI of the routed expert FFN library: argument checks on the host, then
+// one or more kernel launches on the caller's stream.  Nothing is enqueued when
+// a check fails; the reason is kept per thread for moe_last_error().
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "../../include/expert_ffn.h"
+#include "common.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+int g_ffn_path = 0;
+
+moe_status fail(moe_status st, const char* fn, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = std::string(fn) + ": " + buf;
+    return st;
+}
+
+moe_status hip_status(const char* fn, hipError_t e) {
+    if (e == hipSuccess) return MOE_OK;
+    return fail(MOE_E_HIP, fn, "%s", hipGetErrorString(e));
+}
+
+bool fmt_ok(int32_t f) { return f == MOE_W_BF16 || f == MOE_W_INT8_ROW || f == MOE_W_INT4_G64; }
+bool dt_ok(int32_t d) { return d == MOE_F32 || d == MOE_BF16; }
+
+uint64_t up256(uint64_t x) { return (x + 255u) / 256u * 256u; }
+
+// layout of a blob; false if the shape does not fit the format
+bool layout(int32_t wfmt, int32_t H, int32_t FF, uint64_t* off) {
+    if (H < 1 || FF < 1 || !fmt_ok(wfmt)) return false;
+    const uint64_t n13 = 2ull * FF * H, n2 = static_cast<uint64_t>(H) * FF;
+    if (wfmt == MOE_W_BF16) {
+        off[0] = 0;
+        off[1] = off[2] = up256(n13 * 2);
+        off[3] = off[4] = up256(off[2] + n2 * 2);
+    } else if (wfmt == MOE_W_INT8_ROW) {
+        off[0] = 0;
+        off[1] = up256(n13);
+        off[2] = up256(off[1] + 2ull * FF * 4);
+        off[3] = up256(off[2] + n2);
+        off[4] = up256(off[3] + static_cast<uint64_t>(H) * 4);
+    } else {
+        if (H % 64 || FF % 64) return false;
+        off[0] = 0;
+        off[1] = up256(n13 / 2);
+        off[2] = up256(off[1] + 2ull * FF * (H / 64) * 2);
+        off[3] = up256(off[2] + n2 / 2);
+        off[4] = up256(off[3] + static_cast<uint64_t>(H) * (FF / 64) * 2);
+    }
+    return true;
+}
+
+// shape rules of the expert FFN kernels
+moe_status check_ffn_shape(const char* fn, int32_t E, int32_t H, int32_t FF, int32_t wfmt,
+                           int32_t T, int32_t k) {
+    if (!fmt_ok(wfmt)) return fail(MOE_E_ARG, fn, "unknown weight format %d", wfmt);
+    if (E < 1 || E > 512) return fail(MOE_E_SHAPE, fn, "E=%d outside [1, 512]", E);
+    if (k < 1 || k > 32 || k > E) return fail(MOE_E_SHAPE, fn, "k=%d outside [1, min(E=%d, 32)]", k, E);
+    if (T < 0) return fail(MOE_E_SHAPE, fn, "T=%d < 0", T);
+    if (H < 64 || H % 64) return fail(MOE_E_SHAPE, fn, "H=%d is not a positive multiple of 64", H);
+    const int ffq = wfmt == MOE_W_BF16 ? 32 : 64;
+    if (FF < ffq || FF % ffq)
+        return fail(MOE_E_SHAPE, fn, "FF=%d is not a positive multiple of %d for this format", FF, ffq);
+    if (static_cast<int64_t>(T) * k > (1ll << 30)) return fail(MOE_E_SHAPE, fn, "T*k too large");
+    return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_last_error(void) { return g_last_error.c_str(); }
+
+uint64_t moe_expert_bytes(int32_t wfmt, int32_t H, int32_t FF) {
+    uint64_t off[5];
+    return layout(wfmt, H, FF, off) ? off[4] : 0;
+}
+
+moe_status moe_blob_layout(int32_t wfmt, int32_t H, int32_t FF, uint64_t* off) {
+    if (!off) return fail(MOE_E_ARG, "moe_blob_layout", "off is NULL");
+    if (!fmt_ok(wfmt)) return fail(MOE_E_ARG, "moe_blob_layout", "unknown weight format %d", wfmt);
+    if (!layout(wfmt, H, FF, off))
+        return fail(MOE_E_SHAPE, "moe_blob_layout", "H=%d FF=%d invalid for format %d", H, FF, wfmt);
+    return MOE_OK;
+}
+
+size_t moe_workspace_bytes(int32_t T, int32_t k, int32_t E, int32_t H, int32_t FF, int32_t wfmt) {
+    (void)E;
+    (void)wfmt;
+    if (T < 0 || k < 1 || H < 1 || FF < 1) return 0;
+    return moe::ffn_workspace(T, k, H, FF).bytes;
+}
+
+moe_status moe_set_ffn_path(int32_t path) {
+    if (path < 0 || path > 2) return fail(MOE_E_ARG, "moe_set_ffn_path", "path=%d not in {0,1,2}", path);
+    g_ffn_path = path;
+    return MOE_OK;
+}
+
+moe_status moe_route_topk(const float* logits, int32_t T, int32_t E, int32_t k, int32_t renorm,
+                          int32_t* topk_ids, float* topk_w, void* stream) {
+    const char* fn = "moe_route_topk";
+    if (!logits || !topk_ids || !topk_w) return fail(MOE_E_ARG, fn, "null pointer argument");
+    if (T < 0) return fail(MOE_E_SHAPE, fn, "T=%d < 0", T);
+    if (E < 1 || E > 512) return fail(MOE_E_SHAPE, fn, "E=%d outside [1, 512]", E);
+    if (k < 1 || k > 32 || k > E) return fail(MOE_E_SHAPE, fn, "k=%d outside [1, min(E=%d, 32)]", k, E);
+    if (T == 0) return MOE_OK;
+    return hip_status(fn, moe::launch_route_topk(logits, T, E, k, renorm, topk_ids, topk_w,
+                                                 static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_permute(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E,
+                       const int32_t* slot_of, int32_t* expert_offsets, int32_t* sorted_route,
+                       int32_t* route_pos, int32_t* n_dropped, void* stream) {
+    const char* fn = "moe_permute";
+    if (!slot_of || !expert_offsets || !n_dropped) return fail(MOE_E_ARG, fn, "null pointer argument");
+    if (T < 0) return fail(MOE_E_SHAPE, fn, "T=%d < 0", T);
+    if (T > 0 && (!topk_ids || !sorted_route || !route_pos)) return fail(MOE_E_ARG, fn, "null pointer argument");
+    if (E < 1 || E > 512) return fail(MOE_E_SHAPE, fn, "E=%d outside [1, 512]", E);
+    if (k < 1 || k > 32 || k > E) return fail(MOE_E_SHAPE, fn, "k=%d outside [1, min(E=%d, 32)]", k, E);
+    if (static_cast<int64_t>(T) * k > (1ll << 30)) return fail(MOE_E_SHAPE, fn, "T*k too large");
+    return hip_status(fn, moe::launch_permute(topk_ids, T * k, E, slot_of, expert_offsets, sorted_route,
+                                              route_pos, n_dropped, static_cast<hipStream_t>(stream)));
+}
+
+static moe_status ffn_entry(const char* fn, int phases, const void* pool, uint64_t slot_bytes,
+                            const int32_t* slot_of, int32_t E, int32_t H, int32_t FF, int32_t wfmt,
+                            int32_t act, const void* x, int32_t x_dtype, int32_t T, int32_t k,
+                            const int32_t* expert_offsets, const int32_t* sorted_route,
+                            void* out_routes, int32_t out_dtype, void* ws, size_t ws_bytes,
+                            void* stream) {
+    moe_status st = check_ffn_shape(fn, E, H, FF, wfmt, T, k);
+    if (st != MOE_OK) return st;
+    if (!pool || !slot_of || !expert_offsets || !sorted_route || !ws)
+        return fail(MOE_E_ARG, fn, "null pointer argument");
+    if ((phases & 1) && !x) return fail(MOE_E_ARG, fn, "x is NULL");
+    if ((phases & 2) && !out_routes) return fail(MOE_E_ARG, fn, "out_routes is NULL");
+    if (act != MOE_ACT_GELU_TANH && act != MOE_ACT_SILU) return fail(MOE_E_ARG, fn, "unknown activation %d", act);
+    if (!dt_ok(x_dtype) || !dt_ok(out_dtype)) return fail(MOE_E_ARG, fn, "unknown dtype");
+    uint64_t off[5];
+    layout(wfmt, H, FF, off);
+    if (slot_bytes < off[4] || slot_bytes % 256)
+        return fail(MOE_E_ARG, fn, "slot_bytes=%llu must be a multiple of 256 and >= %llu",
+                    static_cast<unsigned long long>(slot_bytes), static_cast<unsigned long long>(off[4]));
+    if (reinterpret_cast<uintptr_t>(pool) % 256) return fail(MOE_E_ARG, fn, "pool is not 256-byte aligned");
+    if (reinterpret_cast<uintptr_t>(ws) % 256) return fail(MOE_E_ARG, fn, "ws is not 256-byte aligned");
+    if ((phases & 1) && reinterpret_cast<uintptr_t>(x) % 16) return fail(MOE_E_ARG, fn, "x is not 16-byte aligned");
+    if ((phases & 2) && reinterpret_cast<uintptr_t>(out_routes) % 16)
+        return fail(MOE_E_ARG, fn, "out_routes is not 16-byte aligned");
+    const moe::FfnWorkspace wl = moe::ffn_workspace(T, k, H, FF);
+    if (ws_bytes < wl.bytes)
+        return fail(MOE_E_WORKSPACE, fn, "ws_bytes=%zu < %zu needed", ws_bytes, wl.bytes);
+    if (T == 0) return MOE_OK;
+    moe::FfnParams P{};
+    P.pool = static_cast<const uint8_t*>(pool);
+    P.slot_bytes = slot_bytes;
+    P.slot_of = slot_of;
+    P.E = E; P.H = H; P.FF = FF; P.fmt = wfmt; P.act = act; P.T = T; P.k = k;
+    P.offsets = expert_offsets;
+    P.sorted_route = sorted_route;
+    P.x = x;
+    P.x_dt = x_dtype;
+    P.xq = nullptr;
+    P.xq_out = reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(ws) + wl.xq_off);
+    P.h = reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(ws) + wl.h_off);
+    P.out = out_routes;
+    P.out_dt = out_dtype;
+    P.o13 = off[0]; P.os13 = off[1]; P.o2 = off[2]; P.os2 = off[3];
+    return hip_status(fn, moe::launch_ffn(P, phases, g_ffn_path, static_cast<hipStream_t>(stream)));
+}
+
+#define FFN_ARGS pool, slot_bytes, slot_of, E, H, FF, wfmt, act, x, x_dtype, T, k, expert_offsets, \
+                 sorted_route, out_routes, out_dtype, ws, ws_bytes, stream
+#define FFN_PARAMS const void *pool, uint64_t slot_bytes, const int32_t *slot_of, int32_t E, int32_t H, \
+                   int32_t FF, int32_t wfmt, int32_t act, const void *x, int32_t x_dtype, int32_t T,  \
+                   int32_t k, const int32_t *expert_offsets, const int32_t *sorted_route,             \
+                   void *out_routes, int32_t out_dtype, void *ws, size_t ws_bytes, void *stream
+
+moe_status moe_expert_ffn(FFN_PARAMS) { return ffn_entry("moe_expert_ffn", 3, FFN_ARGS); }
+moe_status moe_ffn_gate_up(FFN_PARAMS) { return ffn_entry("moe_ffn_gate_up", 1, FFN_ARGS); }
+moe_status moe_ffn_down(FFN_PARAMS) { return ffn_entry("moe_ffn_down", 2, FFN_ARGS); }
+
+moe_status moe_combine(const void* out_routes, int32_t out_dtype, const float* topk_w,
+                       const int32_t* route_pos, int32_t T, int32_t k, int32_t H, void* y,
+                       int32_t y_dtype, void* stream) {
+    const char* fn = "moe_combine";
+    if (!out_routes || !topk_w || !route_pos || !y) return fail(MOE_E_ARG, fn, "null pointer argument");
+    if (!dt_ok(out_dtype) || !dt_ok(y_dtype)) return fail(MOE_E_ARG, fn, "unknown dtype");
+    if (T < 0) return fail(MOE_E_SHAPE, fn, "T=%d < 0", T);
+    if (k < 1 || k > 32) return fail(MOE_E_SHAPE, fn, "k=%d outside [1, 32]", k);
+    if (H < 8 || H % 8) return fail(MOE_E_SHAPE, fn, "H=%d is not a positive multiple of 8", H);
+    if (reinterpret_cast<uintptr_t>(out_routes) % 16 || reinterpret_cast<uintptr_t>(y) % 16)
+        return fail(MOE_E_ARG, fn, "out_routes and y must be 16-byte aligned");
+    if (T == 0) return MOE_OK;
+    return hip_status(fn, moe::launch_combine(out_routes, out_dtype, topk_w, route_pos, T, k, H, y,
+                                              y_dtype, static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_quantize(int32_t wfmt, const uint16_t* w_bf16, int32_t N, int32_t K, void* q,
+                        void* scales, void* stream) {
+    const char* fn = "moe_quantize";
+    if (!w_bf16 || !q || !scales) return fail(MOE_E_ARG, fn, "null pointer argument");
+    if (wfmt != MOE_W_INT8_ROW && wfmt != MOE_W_INT4_G64)
+        return fail(MOE_E_ARG, fn, "format %d is not a quantised format", wfmt);
+    if (N < 0 || K < 1) return fail(MOE_E_SHAPE, fn, "N=%d K=%d", N, K);
+    if (wfmt == MOE_W_INT4_G64 && K % 64) return fail(MOE_E_SHAPE, fn, "K=%d is not a multiple of 64", K);
+    return hip_status(fn, moe::launch_quantize(wfmt, w_bf16, N, K, q, scales,
+                                               static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_pack_expert(int32_t wfmt, const uint16_t* w13_bf16, const uint16_t* w2_bf16,
+                           int32_t H, int32_t FF, void* blob, void* stream) {
+    const char* fn = "moe_pack_expert";
+    if (!w13_bf16 || !w2_bf16 || !blob) return fail(MOE_E_ARG, fn, "null pointer argument");
+    if (!fmt_ok(wfmt)) return fail(MOE_E_ARG, fn, "unknown weight format %d", wfmt);
+    uint64_t off[5];
+    if (!layout(wfmt, H, FF, off)) return fail(MOE_E_SHAPE, fn, "H=%d FF=%d invalid for format %d", H, FF, wfmt);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    uint8_t* b = static_cast<uint8_t*>(blob);
+    hipError_t e = hipMemsetAsync(blob, 0, off[4], s);
+    if (e != hipSuccess) return hip_status(fn, e);
+    if (wfmt == MOE_W_BF16) {
+        e = hipMemcpyAsync(b + off[0], w13_bf16, 2ull * FF * H * 2, hipMemcpyDeviceToDevice, s);
+        if (e == hipSuccess)
+            e = hipMemcpyAsync(b + off[2], w2_bf16, static_cast<uint64_t>(H) * FF * 2, hipMemcpyDeviceToDevice, s);
+        return hip_status(fn, e);
+    }
+    e = moe::launch_quantize(wfmt, w13_bf16, 2 * FF, H, b + off[0], b + off[1], s);
+    if (e == hipSuccess) e = moe::launch_quantize(wfmt, w2_bf16, H, FF, b + off[2], b + off[3], s);
+    return hip_status(fn, e);
+}
+
+}  // extern "C"

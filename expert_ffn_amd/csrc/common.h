@@ -1,0 +1,48 @@
+// Internal helpers shared by the HIP kernels of the routed expert FFN (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+// format / dtype / activation codes (same values as the public enums)
+enum { F32 = 0, BF16 = 1 };
+enum { W_BF16 = 0, W_INT8 = 1, W_INT4 = 2 };
+enum { ACT_GELU_TANH = 0, ACT_SILU = 1 };
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+
+// bf16 <-> fp32 on bit patterns.  Narrowing is round to nearest, ties to even;
+// NaN becomes the quiet NaN 0x7FC0.
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+    return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0;
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return static_cast<uint16_t>(u >> 16);
+}
+// two fp32 -> packed bf16x2 (RNE) with the gfx950 conversion instruction
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+    bf16x2_t v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ f32x4 mfma16x16x32(const u32x4& a, const u32x4& b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float act_fn(int act, float g) {
+    if (act == ACT_SILU) return g / (1.0f + __expf(-g));
+    const float c = 0.7978845608028654f;  // sqrt(2/pi)
+    return 0.5f * g * (1.0f + tanhf(c * (g + 0.044715f * g * g * g)));
+}
+
+}  // namespace moe

@@ -1,0 +1,46 @@
+// Launch functions of the HIP kernels (internal; the C ABI is in include/expert_ffn.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+hipError_t launch_route_topk(const float* logits, int T, int E, int k, int renorm, int* ids,
+                             float* w, hipStream_t s);
+hipError_t launch_permute(const int* ids, int R, int E, const int* slot_of, int* offsets,
+                          int* sorted_route, int* route_pos, int* n_dropped, hipStream_t s);
+hipError_t launch_combine(const void* out_routes, int out_dt, const float* w, const int* route_pos,
+                          int T, int k, int H, void* y, int y_dt, hipStream_t s);
+hipError_t launch_quantize(int fmt, const uint16_t* w, int N, int K, void* q, void* scales,
+                           hipStream_t s);
+
+// Everything the expert-FFN kernels read and write.
+struct FfnParams {
+    const uint8_t* pool;
+    uint64_t slot_bytes;
+    const int* slot_of;
+    int E, H, FF, fmt, act, T, k;
+    const int* offsets;       // [E+1]
+    const int* sorted_route;  // [T*k]
+    const void* x;            // [T, H] fp32 or bf16 (x_dt)
+    int x_dt;
+    const uint16_t* xq;       // [T, H] bf16 in the w13 operand order (may alias x)
+    uint16_t* xq_out;         // where the preparation kernel writes xq (workspace)
+    uint16_t* h;              // [T*k, FF] bf16 in the w2 operand order (workspace)
+    void* out;                // [T*k, H] fp32 or bf16 (out_dt)
+    int out_dt;
+    uint64_t o13, os13, o2, os2;  // blob sub-block offsets
+};
+
+// Workspace layout of the expert FFN.
+struct FfnWorkspace {
+    size_t xq_off, h_off, bytes;
+};
+FfnWorkspace ffn_workspace(int T, int k, int H, int FF);
+
+// 0 = choose by token count, 1 = streaming kernels, 2 = LDS-tiled kernels
+hipError_t launch_ffn(const FfnParams& p, int phases /*1 gate_up, 2 down, 3 both*/, int path,
+                      hipStream_t s);
+
+}  // namespace moe

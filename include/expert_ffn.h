@@ -1,0 +1,226 @@
+/*
+ * expert_ffn.h -- C ABI of the MI355X (gfx950) routed expert FFN library
+ * (expert_ffn_amd/libexpert_ffn.so).
+ *
+ * One MoE layer's routed expert FFN, as the prain README describes the serving
+ * problem (sections "Expert formats" and "int4 experts on RDNA2"): each token
+ * picks its top-k experts from router logits; routes are grouped per expert;
+ * each expert applies a gated FFN (w13 = gate and up projections stacked,
+ * then the w2 down projection); the outputs are combined back into token
+ * order, weighted by the router's renormalised softmax.  Expert weights are
+ * bf16, int8 with an fp32 scale per row, or int4 with a bf16 scale per 64
+ * elements; experts are found through a per-layer expert -> slot table into a
+ * pool of equally sized slots (prain's VRAM cache slots; Winery-Strata's
+ * RemoteExperts::begin looks experts up the same way, slot_of / device_slot).
+ *
+ * Conventions for every entry point:
+ *   - Pointers marked "device" are device memory owned by the caller; the
+ *     library keeps no pointer after a call returns and never allocates or
+ *     frees device memory in the compute calls.  "host" pointers are host
+ *     memory.
+ *   - stream is a hipStream_t (NULL = the legacy default stream).  Every call
+ *     only enqueues work on that stream and returns; nothing synchronises.
+ *   - Arguments are checked on the host before anything is enqueued.  A call
+ *     that returns a status other than MOE_OK has enqueued nothing, and
+ *     moe_last_error() describes why as "<function>: <what>".  MOE_E_HIP
+ *     reports a failed launch with the HIP runtime's error string.
+ *   - Shape rules: 1 <= k <= min(E, 32), E <= 512, T >= 0 (T = 0 enqueues
+ *     nothing), H % 64 == 0, FF % 32 == 0 (bf16 weights) or FF % 64 == 0
+ *     (int8/int4 weights).
+ */
+#ifndef EXPERT_FFN_H
+#define EXPERT_FFN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_E_ARG = 1,          /* a null pointer, negative size or unknown enum    */
+    MOE_E_SHAPE = 2,        /* sizes that break a shape rule above              */
+    MOE_E_UNSUPPORTED = 3,  /* a combination this build does not implement      */
+    MOE_E_WORKSPACE = 4,    /* workspace smaller than moe_workspace_bytes()     */
+    MOE_E_HIP = 5           /* the HIP runtime reported an error                */
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+/* Expert weight formats (prain README, "Expert formats" table). */
+typedef enum {
+    MOE_W_BF16 = 0,      /* weights as trained                                   */
+    MOE_W_INT8_ROW = 1,  /* int8 codes, one fp32 scale per output row (w8a16)    */
+    MOE_W_INT4_G64 = 2   /* int4 codes, one bf16 scale per 64 elements (w4a16)   */
+} moe_wfmt;
+
+/* Gated activation applied to the gate projection (the pages do not name it). */
+typedef enum { MOE_ACT_GELU_TANH = 0, MOE_ACT_SILU = 1 } moe_act;
+
+/* Text of the last non-OK status returned on the calling thread ("" if none). */
+const char* moe_last_error(void);
+
+/*
+ * Bytes of one packed expert blob (the slot size a pool needs), 0 if the shape
+ * is invalid for the format.  Gemma-4-26B-A4B (H = 2816, FF = 704): 11,894,784
+ * (bf16), 5,964,288 (int8), 3,159,552 (int4) -- 11.34 / 5.69 / 3.01 MiB, the
+ * sizes of prain's "Expert formats" table.
+ */
+uint64_t moe_expert_bytes(int32_t wfmt, int32_t H, int32_t FF);
+
+/*
+ * Layout of a blob (host call).  off (host, 5 entries) receives the byte
+ * offsets of: w13 codes, w13 scales, w2 codes, w2 scales, and the blob size.
+ * Each sub-block starts on a 256-byte boundary; the size is rounded up to 256.
+ *   bf16: w13 bf16 [2FF, H] | w2 bf16 [H, FF]  (the scale offsets equal the
+ *         next block's start)
+ *   int8: w13 int8 [2FF, H] | fp32 [2FF] | w2 int8 [H, FF] | fp32 [H]
+ *   int4: w13 [2FF, H/2] | bf16 [2FF, H/64] | w2 [H, FF/2] | bf16 [H, FF/64]
+ * Rows are K-contiguous (K = H for w13, FF for w2).  w13 rows 0..FF-1 are the
+ * gate projection, FF..2FF-1 the up projection.  int4 byte b of a row holds
+ * element 2b in its low nibble and 2b+1 in its high nibble, each as q + 8.
+ */
+moe_status moe_blob_layout(int32_t wfmt, int32_t H, int32_t FF, uint64_t* off);
+
+/*
+ * Workspace bytes moe_expert_ffn / moe_ffn_gate_up / moe_ffn_down need for T
+ * tokens with top-k routing (bf16 activations in the kernels' operand layout
+ * and the gated hidden rows h [T*k, FF]).
+ */
+size_t moe_workspace_bytes(int32_t T, int32_t k, int32_t E, int32_t H, int32_t FF, int32_t wfmt);
+
+/*
+ * Router top-k with softmax weights (prain README, "Trading quality for speed":
+ * a token's router weight is shared among its experts; the tie rule is that of
+ * rlx_runtime/expert_pool.rs, target_gpu_from_counts: equal values go to the
+ * lower expert id first).
+ *   logits   device fp32 [T, E], row-major.  Larger logit = preferred.  NaN
+ *            ranks below every number; -0 equals +0.  Logits should be finite
+ *            for meaningful weights.
+ *   topk_ids device int32 [T, k] out: the k chosen experts, best first.
+ *   topk_w   device fp32 [T, k] out: renorm != 0: softmax over the chosen k
+ *            logits (the full softmax renormalised over the chosen experts);
+ *            renorm == 0: the full softmax over E at the chosen experts.
+ */
+moe_status moe_route_topk(const float* logits, int32_t T, int32_t E, int32_t k, int32_t renorm,
+                          int32_t* topk_ids, float* topk_w, void* stream);
+
+/*
+ * Group routes by expert (Winery-Strata remote_experts.cpp, RemoteExperts::
+ * begin: per expert group, the routes in route order, token = route / k;
+ * rlx_runtime/expert_pool.rs count_hits: the per-expert histogram).
+ * Route i = t*k + j is kept when 0 <= topk_ids[i] < E and slot_of[that] >= 0;
+ * otherwise it is dropped (its expert is not resident) and counted.
+ *   topk_ids       device int32 [T*k]
+ *   slot_of        device int32 [E], the layer's expert -> slot table, -1 =
+ *                  not resident
+ *   expert_offsets device int32 [E+1] out: group e is positions
+ *                  [offsets[e], offsets[e+1]); offsets[E] = kept routes
+ *   sorted_route   device int32 [T*k] out: route index at each position,
+ *                  experts ascending, route index ascending inside a group;
+ *                  -1 from offsets[E] on
+ *   route_pos      device int32 [T*k] out: position of each route, -1 if dropped
+ *   n_dropped      device int32 [1] out: number of dropped routes
+ * Deterministic: no result depends on thread timing.
+ */
+moe_status moe_permute(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E,
+                       const int32_t* slot_of, int32_t* expert_offsets, int32_t* sorted_route,
+                       int32_t* route_pos, int32_t* n_dropped, void* stream);
+
+/*
+ * The expert FFN of every kept route (prain README, "Expert formats": an
+ * expert is its w13 and w2; weights are dequantised inside the kernels):
+ *   for the route at position p (route i = sorted_route[p], token t = i / k,
+ *   expert e):  g = W1_e x_t,  u = W3_e x_t,  h = act(g) * u,  o_p = W2_e h.
+ *   pool        device, the slot pool; expert e's blob starts at
+ *               pool + slot_of[e] * slot_bytes (slot_bytes >= moe_expert_bytes,
+ *               a multiple of 256)
+ *   slot_of     device int32 [E] (the table moe_permute was given)
+ *   x           device [T, H], fp32 or bf16 (x_dtype); the kernels multiply in
+ *               bf16 with fp32 accumulation (fp32 x is rounded to bf16)
+ *   expert_offsets, sorted_route: device, from moe_permute
+ *   out_routes  device [T*k, H] out, fp32 or bf16 (out_dtype): row p is the
+ *               output of the route at position p; rows from offsets[E] on are
+ *               not written
+ *   ws          device workspace of ws_bytes >= moe_workspace_bytes(...)
+ * moe_ffn_gate_up and moe_ffn_down are its two halves, for callers that time
+ * or schedule them apart: gate_up leaves h in ws, down reads it from there;
+ * gate_up ignores out_routes, down ignores x (both accept NULL for them).
+ */
+moe_status moe_expert_ffn(const void* pool, uint64_t slot_bytes, const int32_t* slot_of, int32_t E,
+                          int32_t H, int32_t FF, int32_t wfmt, int32_t act, const void* x,
+                          int32_t x_dtype, int32_t T, int32_t k, const int32_t* expert_offsets,
+                          const int32_t* sorted_route, void* out_routes, int32_t out_dtype,
+                          void* ws, size_t ws_bytes, void* stream);
+
+moe_status moe_ffn_gate_up(const void* pool, uint64_t slot_bytes, const int32_t* slot_of, int32_t E,
+                           int32_t H, int32_t FF, int32_t wfmt, int32_t act, const void* x,
+                           int32_t x_dtype, int32_t T, int32_t k, const int32_t* expert_offsets,
+                           const int32_t* sorted_route, void* out_routes, int32_t out_dtype,
+                           void* ws, size_t ws_bytes, void* stream);
+
+moe_status moe_ffn_down(const void* pool, uint64_t slot_bytes, const int32_t* slot_of, int32_t E,
+                        int32_t H, int32_t FF, int32_t wfmt, int32_t act, const void* x,
+                        int32_t x_dtype, int32_t T, int32_t k, const int32_t* expert_offsets,
+                        const int32_t* sorted_route, void* out_routes, int32_t out_dtype,
+                        void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Weighted scatter-combine back to token order (Winery-Strata
+ * RemoteExperts::finish scatters each computed row back to its route; prain
+ * README, "Trading quality for speed": a token's result is its routes weighted
+ * by their router share):
+ *   y[t] = sum over j = 0..k-1 with route_pos[t*k+j] >= 0 of
+ *          topk_w[t*k+j] * out_routes[route_pos[t*k+j]]
+ * accumulated in fp32 in ascending j; dropped routes add nothing and the
+ * others are not rescaled.
+ *   out_routes device [T*k, H] fp32 or bf16 (out_dtype)
+ *   topk_w     device fp32 [T*k];  route_pos device int32 [T*k]
+ *   y          device [T, H] out, fp32 or bf16 (y_dtype, rounded to nearest
+ *              even)
+ */
+moe_status moe_combine(const void* out_routes, int32_t out_dtype, const float* topk_w,
+                       const int32_t* route_pos, int32_t T, int32_t k, int32_t H, void* y,
+                       int32_t y_dtype, void* stream);
+
+/*
+ * Quantise a bf16 matrix W [N, K] (device, row-major) into a packed format,
+ * bit-exactly as the format defines (prain README, "Expert formats": int8 with
+ * an fp32 scale per row; int4 with a bf16 scale per 64 elements chosen by an
+ * MSE clip search).
+ *   MOE_W_INT8_ROW: a = max |row|; s = a / 127 (fp32, IEEE division; 0 for a
+ *     zero row); q = clamp(rint(w / s), -127, 127).  q device int8 [N, K],
+ *     scales device fp32 [N].
+ *   MOE_W_INT4_G64 (K % 64 == 0): per 64-element group with absmax a, try
+ *     s_i = bf16(fp32(a * (20 - i)) / 140) for i = 0..9 (clip 1.00 down to
+ *     0.55 of a / 7), codes q = clamp(rint(w / s_i), -8, 7) (0 if s_i = 0),
+ *     squared error summed in fp64 in element order; keep the first smallest.
+ *     q device uint8 [N, K/2] (low nibble = even element, value q + 8),
+ *     scales device bf16 bits [N, K/64].
+ */
+moe_status moe_quantize(int32_t wfmt, const uint16_t* w_bf16, int32_t N, int32_t K, void* q,
+                        void* scales, void* stream);
+
+/*
+ * Write one expert's blob (layout of moe_blob_layout) from its bf16 w13
+ * [2FF, H] and w2 [H, FF] (device), quantising as moe_quantize does.  blob is
+ * device memory of moe_expert_bytes() bytes; padding bytes are zeroed.
+ */
+moe_status moe_pack_expert(int32_t wfmt, const uint16_t* w13_bf16, const uint16_t* w2_bf16,
+                           int32_t H, int32_t FF, void* blob, void* stream);
+
+/*
+ * Kernel family moe_expert_ffn uses: 0 = by token count (default), 1 = the
+ * streaming kernels for small per-expert groups, 2 = the LDS-tiled kernels for
+ * large groups.  Process-wide setting for tests and measurement; not
+ * synchronised with concurrent calls.  Returns MOE_E_ARG for other values.
+ */
+moe_status moe_set_ffn_path(int32_t path);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EXPERT_FFN_H */

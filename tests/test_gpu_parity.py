@@ -1,0 +1,258 @@
+"""GPU parity of the whole path against the oracle, through the C ABI.
+
+Bit-exact: expert ids, group offsets, sorted routes, route positions, dropped
+count and every packed byte of the experts the oracle packs itself.  Within
+tolerance: router weights (1e-5 absolute) and the layer output y (max
+row-relative error 2e-2 for bf16 weights, 3e-2 for int8/int4, against the
+fp64 oracle on the same dequantised weights).
+"""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from gpu_common import (FMT, TOL, build_pool, log, oracle_layer, row_rel_err, sample_tokens,
+                        to_np)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def L():
+    import expert_ffn_amd as lib
+    lib.lib()
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return lib
+
+
+def _x(seed, layer, T, H, kind):
+    if kind == "f32":
+        xh = synth.x_f32(seed, layer, T, H)
+        import oracle as ora
+        return torch.from_numpy(xh).cuda(), xh
+    bits = synth.x_bf16(seed, layer, T, H)
+    import oracle as ora
+    return torch.from_numpy(bits.view(np.int16)).cuda().view(torch.bfloat16), ora.bf16_to_f32(bits)
+
+
+def run_case(L, name, *, E, k, H, FF, fmt, T, act=0, x_kind="bf16", y_dtype=torch.bfloat16,
+             zipf=None, slot_of=None, n_sample=16, seed=0, layer=0, out_dtype=torch.float32, path=0):
+    from expert_ffn_amd.layer import MoeLayer
+    log(f"[case] {name}: E={E} k={k} H={H} FF={FF} fmt={fmt} T={T} act={act} zipf={zipf}")
+    f = FMT[fmt]
+    if slot_of is None:
+        slot_of = np.arange(E, dtype=np.int32)
+    slot_of = np.asarray(slot_of, np.int32)
+    logits = synth.logits(seed, layer, T, E, zipf)
+    x_d, x_f32 = _x(seed, layer, T, H, x_kind)
+    pool, sb = build_pool(seed, layer, E, H, FF, f, slot_of)
+    slot_d = torch.from_numpy(slot_of).cuda()
+    L.set_ffn_path(path)
+    try:
+        ml = MoeLayer(E, k, H, FF, f, max(T, 1), act=act, y_dtype=y_dtype, out_dtype=out_dtype)
+        ml.bind(pool, sb, slot_d)
+        y = ml.run(torch.from_numpy(logits).cuda(), x_d)
+        torch.cuda.synchronize()
+    finally:
+        L.set_ffn_path(0)
+    v = ml.views(T)
+    tokens = sample_tokens(T, n_sample)
+    ref = oracle_layer(seed, layer, E, k, H, FF, f, act, logits, x_f32, slot_of, tokens)
+    assert np.array_equal(to_np(v["topk_ids"]), ref["ids"]), "topk ids differ"
+    assert np.max(np.abs(to_np(v["topk_w"]) - ref["w"])) <= 1e-5, "router weights differ"
+    assert np.array_equal(to_np(v["offsets"]), ref["offsets"]), "expert offsets differ"
+    assert np.array_equal(to_np(v["sorted_route"]), ref["sorted_route"]), "sorted routes differ"
+    assert np.array_equal(to_np(v["route_pos"]), ref["route_pos"]), "route positions differ"
+    assert int(to_np(v["n_dropped"])[0]) == ref["n_dropped"]
+    for e, blob in ref["blobs"].items():
+        got = to_np(pool[slot_of[e] * sb:slot_of[e] * sb + blob.size])
+        assert np.array_equal(got, blob), f"packed bytes of expert {e} differ"
+    err, med = row_rel_err(to_np(y)[tokens], ref["y"])
+    log(f"    y: max row-rel err {err:.3e}, median {med:.3e} over {tokens.size} tokens "
+        f"(tolerance {TOL[f]:.0e})")
+    assert err <= TOL[f], f"{name}: y error {err} > {TOL[f]}"
+    return ml, pool, sb, y
+
+
+# ------------------------------------------------------------ tiny layer ----
+@pytest.mark.parametrize("act", [0, 1])
+def test_tiny_bf16(L, act):
+    c = synth.CONFIGS["tiny"]
+    run_case(L, "tiny", E=c["E"], k=c["k"], H=c["H"], FF=c["FF"], fmt="bf16", T=c["T"], act=act,
+             x_kind="f32", y_dtype=torch.float32, slot_of=[2, 0, 3, 1])
+
+
+def test_tiny_dropped_expert(L):
+    c = synth.CONFIGS["tiny"]
+    run_case(L, "tiny-dropped", E=c["E"], k=c["k"], H=c["H"], FF=c["FF"], fmt="bf16", T=c["T"],
+             x_kind="f32", y_dtype=torch.float32, slot_of=[1, -1, 0, 2])
+
+
+@pytest.mark.parametrize("fmt", ["int8", "int4"])
+@pytest.mark.parametrize("act", [0, 1])
+def test_tiny_quantised(L, fmt, act):
+    run_case(L, f"tiny-{fmt}", E=4, k=2, H=128, FF=64, fmt=fmt, T=8, act=act, x_kind="f32",
+             y_dtype=torch.float32, slot_of=[3, 1, 0, 2])
+
+
+def test_ragged_shapes(L):
+    # E, T not multiples of anything; two experts not resident; several groups of 17+ routes
+    slot_of = np.array([4, -1, 0, 6, 2, -1, 1], np.int32)
+    for fmt in ("bf16", "int8", "int4"):
+        run_case(L, f"ragged-{fmt}", E=7, k=3, H=192, FF=128, fmt=fmt, T=37, slot_of=slot_of,
+                 n_sample=37, seed=3)
+
+
+def test_all_dropped(L):
+    ml, _, _, y = run_case(L, "all-dropped", E=4, k=2, H=64, FF=32, fmt="bf16", T=5,
+                           slot_of=[-1, -1, -1, -1], x_kind="f32", y_dtype=torch.float32)
+    assert int(to_np(ml.n_dropped)[0]) == 10
+    assert not to_np(y).any()
+
+
+# -------------------------------------------------- Gemma-shaped layers ----
+G = synth.GEMMA
+
+
+@pytest.mark.parametrize("T", [1, 4, 16, 64])
+def test_gemma_bf16_decode(L, T):
+    run_case(L, f"gemma-bf16-T{T}", E=G["E"], k=G["k"], H=G["H"], FF=G["FF"], fmt="bf16", T=T,
+             n_sample=16)
+
+
+def test_gemma_bf16_silu(L):
+    run_case(L, "gemma-bf16-silu", E=G["E"], k=G["k"], H=G["H"], FF=G["FF"], fmt="bf16", T=16, act=1)
+
+
+def test_gemma_int8_decode_zipf(L):
+    run_case(L, "gemma-int8-zipf-T16", E=G["E"], k=G["k"], H=G["H"], FF=G["FF"], fmt="int8", T=16,
+             zipf=1.1)
+
+
+def test_gemma_int4_decode(L):
+    slot_of = synth.slot_table(0, 1, G["E"])[0]
+    run_case(L, "gemma-int4-T16", E=G["E"], k=G["k"], H=G["H"], FF=G["FF"], fmt="int4", T=16,
+             slot_of=slot_of)
+
+
+@pytest.mark.parametrize("zipf", [None, 1.1])
+def test_gemma_int4_prefill(L, zipf):
+    run_case(L, f"gemma-int4-T1024-zipf{zipf}", E=G["E"], k=G["k"], H=G["H"], FF=G["FF"], fmt="int4",
+             T=1024, zipf=zipf, n_sample=12)
+
+
+# ------------------------------------------------------------ invariants ----
+def test_determinism_and_slot_shuffle(L):
+    from expert_ffn_amd.layer import MoeLayer
+    E, k, H, FF, T = 16, 4, 256, 128, 64
+    log("[case] determinism + slot shuffle int4")
+    logits = torch.from_numpy(synth.logits(5, 0, T, E, 1.1)).cuda()
+    x_d, _ = _x(5, 0, T, H, "bf16")
+    s1 = np.arange(E, dtype=np.int32)
+    s2 = np.random.default_rng(1).permutation(E).astype(np.int32) + 3
+    outs = []
+    for so in (s1, s1, s2):
+        pool, sb = build_pool(5, 0, E, H, FF, 2, so)
+        ml = MoeLayer(E, k, H, FF, 2, T).bind(pool, sb, torch.from_numpy(so).cuda())
+        outs.append(to_np(ml.run(logits, x_d).clone()))
+    assert np.array_equal(outs[0], outs[1]), "repeat run differs"
+    assert np.array_equal(outs[0], outs[2]), "slot shuffle changes y"
+
+
+def test_split_halves_equal_whole(L):
+    from expert_ffn_amd.layer import MoeLayer
+    E, k, H, FF, T = 8, 2, 128, 64, 24
+    log("[case] gate_up + down == expert_ffn")
+    for f in (0, 1, 2):
+        logits = torch.from_numpy(synth.logits(6, 0, T, E)).cuda()
+        x_d, _ = _x(6, 0, T, H, "bf16")
+        so = np.arange(E, dtype=np.int32)
+        pool, sb = build_pool(6, 0, E, H, FF, f, so)
+        ml = MoeLayer(E, k, H, FF, f, T).bind(pool, sb, torch.from_numpy(so).cuda())
+        whole = to_np(ml.run(logits, x_d).clone())
+        ml.out_routes.zero_()
+        ml.gate_up(x_d)
+        ml.down(T)
+        ml.combine(T)
+        assert np.array_equal(to_np(ml.y[:T]), whole)
+
+
+def test_bf16_out_routes_and_renorm0(L):
+    import expert_ffn_amd as lib
+    import oracle as ora
+    run_case(L, "out-bf16", E=8, k=2, H=128, FF=64, fmt="int4", T=20, out_dtype=torch.bfloat16)
+    T, E, k = 33, 128, 8
+    logits = synth.logits(9, 0, T, E)
+    ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    lib.route_topk(torch.from_numpy(logits).cuda(), k, ids, w, renorm=0)
+    torch.cuda.synchronize()
+    rid, rw = ora.route_topk(logits, k, renorm=0)
+    assert np.array_equal(to_np(ids), rid)
+    assert np.max(np.abs(to_np(w) - rw)) <= 1e-6
+
+
+def test_route_ties_and_nan(L):
+    import expert_ffn_amd as lib
+    import oracle as ora
+    r = np.random.default_rng(2)
+    for E, k in ((4, 2), (100, 7), (300, 32)):
+        l = r.integers(-3, 3, size=(50, E)).astype(np.float32)
+        l[3, :] = 0.0
+        l[4, ::2] = -0.0
+        l[5, 1] = np.nan
+        l[6, :] = -np.inf
+        ids = torch.empty((50, k), dtype=torch.int32, device="cuda")
+        w = torch.empty((50, k), dtype=torch.float32, device="cuda")
+        lib.route_topk(torch.from_numpy(l).cuda(), k, ids, w)
+        torch.cuda.synchronize()
+        rid, _ = ora.route_topk(l, k)
+        assert np.array_equal(to_np(ids), rid)
+
+
+def test_permute_large_and_empty(L):
+    import expert_ffn_amd as lib
+    import oracle as ora
+    r = np.random.default_rng(4)
+    for T, k, E in ((4096, 8, 128), (1000, 3, 512), (0, 8, 128)):
+        ids = r.integers(0, E, size=(T, k)).astype(np.int32)
+        so = r.permutation(E).astype(np.int32)
+        so[r.choice(E, E // 10, replace=False)] = -1
+        d = lambda a: torch.from_numpy(a).cuda()
+        off = torch.full((E + 1,), 7, dtype=torch.int32, device="cuda")
+        sr = torch.empty(max(T * k, 1), dtype=torch.int32, device="cuda")
+        rp = torch.empty(max(T * k, 1), dtype=torch.int32, device="cuda")
+        nd = torch.empty(1, dtype=torch.int32, device="cuda")
+        lib.permute(d(ids), E, d(so), off, sr[:T * k], rp[:T * k], nd)
+        torch.cuda.synchronize()
+        ro, rs, rr, rn = ora.permute(ids, E, so)
+        assert np.array_equal(to_np(off), ro)
+        assert np.array_equal(to_np(sr[:T * k]), rs) and np.array_equal(to_np(rp[:T * k]), rr)
+        assert int(to_np(nd)[0]) == rn
+
+
+def test_quantize_bit_exact_specials(L):
+    import expert_ffn_amd as lib
+    import oracle as ora
+    r = np.random.default_rng(8)
+    w = (r.standard_normal((64, 256)) * 0.02).astype(np.float32)
+    w[0] = 0.0                                  # zero row / zero groups
+    w[1, :64] = 1e-39                           # subnormal group
+    w[2] *= 1e4                                 # large values
+    w[3, 5] = 7.0                               # one outlier
+    bits = synth.to_bf16_bits(w)
+    wd = torch.from_numpy(bits.view(np.int16)).cuda()
+    for fmt in (1, 2):
+        N, K = bits.shape
+        if fmt == 1:
+            q = torch.empty((N, K), dtype=torch.int8, device="cuda")
+            s = torch.empty(N, dtype=torch.float32, device="cuda")
+            rq, rs = ora.quantize_int8(bits)
+        else:
+            q = torch.empty((N, K // 2), dtype=torch.uint8, device="cuda")
+            s = torch.empty((N, K // 64), dtype=torch.int16, device="cuda")
+            rq, rs = ora.quantize_int4(bits)
+        lib.quantize(fmt, wd, q, s)
+        torch.cuda.synchronize()
+        assert np.array_equal(to_np(q).view(rq.dtype), rq)
+        assert np.array_equal(to_np(s).view(rs.dtype), rs)
