@@ -1,0 +1,320 @@
+"""Benchmark: one MI355X, a stack of 30 Gemma-4-26B-A4B-shaped MoE layers with
+128 int4 experts each (11.3 GiB of packed experts resident in HBM, each layer's
+experts found through its own expert -> slot table in shuffled slot order).
+
+A step is one pass of the whole path -- router top-k, permutation, gated w13
+(gate+up) + activation, w2 down, weighted combine -- over all 30 layers for a
+decode batch of T = 16 tokens (fresh synthetic logits and activations per
+layer).  The step is captured once in a HIP graph and replayed; the timed
+region brackets K replays with a device synchronisation on both sides.
+
+Printed: one JSON line with tokens/s (value), ms per step, the achieved HBM
+GB/s of the step, the roofline of the dominant kernel (the gate/up half of the
+expert FFN, timed with HIP events on its own stream in an instrumented pass of
+the same steps), the 1024-token prefill chunk through the same stack (MFMA
+utilisation), and the CPU oracle timed on a bounded sample on this host.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+G = synth.GEMMA
+L_LAYERS = 30
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def build_stack(lib, seed, L, E, H, FF, fmt, device):
+    """Pool of L*E slots; expert e of layer l at slot pi[l*E + e]."""
+    import torch
+    sb = lib.expert_bytes(fmt, H, FF)
+    slots = synth.slot_table(seed, L, E)
+    pool = torch.empty(L * E * sb, dtype=torch.uint8, device=device)
+    for l in range(L):
+        w13, w2 = synth.layer_weights_cuda(seed, l, E, H, FF, device)
+        w13i, w2i = w13.view(torch.int16), w2.view(torch.int16)
+        for e in range(E):
+            s = int(slots[l, e])
+            lib.pack_expert(fmt, w13i[e], w2i[e], pool[s * sb:(s + 1) * sb])
+        del w13, w2, w13i, w2i
+    torch.cuda.synchronize()
+    return pool, sb, slots
+
+
+def layer_inputs(seed, L, T, E, H, device, zipf=None):
+    import torch
+    logits = [torch.from_numpy(synth.logits(seed, l, T, E, zipf)).to(device) for l in range(L)]
+    xs = [torch.from_numpy(synth.x_bf16(seed, l, T, H).view(np.int16)).to(device).view(torch.bfloat16)
+          for l in range(L)]
+    return logits, xs
+
+
+class StackRunner:
+    """Raw C calls with every argument prepared once (no per-call marshalling)."""
+
+    def __init__(self, lib, pool, sb, slots, T, E, k, H, FF, fmt, logits, xs, stream):
+        import ctypes
+        import torch
+        from expert_ffn_amd.layer import MoeLayer
+        self.L = len(logits)
+        self.T = T
+        self.ml = MoeLayer(E, k, H, FF, fmt, T, device=pool.device)
+        ml = self.ml
+        self.slot_d = [torch.from_numpy(slots[l].copy()).to(pool.device) for l in range(self.L)]
+        c = lib.lib()
+        P = lambda t: ctypes.c_void_p(t.data_ptr())
+        s = ctypes.c_void_p(stream.cuda_stream)
+        R = T * k
+        ws = ml.ws.numel()
+        self.calls = []
+        for l in range(self.L):
+            slot = P(self.slot_d[l])
+            route = (c.moe_route_topk, (P(logits[l]), T, E, k, 1, P(ml.topk_ids), P(ml.topk_w), s))
+            perm = (c.moe_permute, (P(ml.topk_ids), T, k, E, slot, P(ml.offsets), P(ml.sorted_route),
+                                    P(ml.route_pos), P(ml.n_dropped), s))
+            ffn_args = (P(pool), sb, slot, E, H, FF, fmt, 0, P(xs[l]), 1, T, k, P(ml.offsets),
+                        P(ml.sorted_route), P(ml.out_routes), 0, P(ml.ws), ws, s)
+            gu = (c.moe_ffn_gate_up, ffn_args)
+            dn = (c.moe_ffn_down, ffn_args)
+            comb = (c.moe_combine, (P(ml.out_routes), 0, P(ml.topk_w), P(ml.route_pos), T, k, H,
+                                    P(ml.y), 1, s))
+            self.calls.append((route, perm, gu, dn, comb))
+        del R
+
+    def step(self, events=None):
+        for l, (route, perm, gu, dn, comb) in enumerate(self.calls):
+            for f, a in (route, perm):
+                if f(*a):
+                    raise RuntimeError("launch failed")
+            if events is not None:
+                events[l][0].record()
+            if gu[0](*gu[1]):
+                raise RuntimeError("launch failed")
+            if events is not None:
+                events[l][1].record()
+            for f, a in (dn, comb):
+                if f(*a):
+                    raise RuntimeError("launch failed")
+
+
+def realised_routing(lib, runner, logits):
+    """Distinct experts and routes per layer (read once, outside any timing)."""
+    import torch
+    out = []
+    for l, (route, perm, _, _, _) in enumerate(runner.calls):
+        route[0](*route[1])
+        perm[0](*perm[1])
+        torch.cuda.synchronize()
+        off = runner.ml.offsets.cpu().numpy()
+        counts = np.diff(off)
+        out.append((int((counts > 0).sum()), int(off[-1])))
+    return out
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(os.path.join(ROOT, "expert_ffn_amd", "csrc"))):
+        with open(os.path.join(ROOT, "expert_ffn_amd", "csrc", name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel_hash):
+    """HBM bytes per gate/up launch from the committed rocprofv3 counter runs,
+    if they were taken on the current kernel sources (else None)."""
+    path = os.path.join(ROOT, "profiles", "traffic_gate_up_int4_T16.json")
+    try:
+        with open(path) as f:
+            d = json.load(f)
+    except (OSError, ValueError):
+        return None
+    return d.get("bytes_per_launch") if d.get("kernel_hash") == kernel_hash else None
+
+
+def cpu_baseline(seed, T, budget_s=20.0):
+    """The oracle on one layer of the same stack (layer 0, decode T tokens),
+    repeated until about budget_s of CPU work; scaled to the 30-layer step."""
+    import torch
+
+    import oracle as ora
+    E, k, H, FF = G["E"], G["k"], G["H"], G["FF"]
+    logits = synth.logits(seed, 0, T, E)
+    x = ora.bf16_to_f32(synth.x_bf16(seed, 0, T, H))
+    ids, _ = ora.route_topk(logits, k)
+    need = sorted(set(int(e) for e in ids.reshape(-1)))
+    w13, w2 = synth.layer_weights_cuda(seed, 0, E, H, FF, "cuda")
+    w13 = w13.view(torch.int16).cpu().numpy().view(np.uint16)
+    w2 = w2.view(torch.int16).cpu().numpy().view(np.uint16)
+    sb = ora.expert_bytes(2, H, FF)
+    pool = np.zeros(E * sb, np.uint8)
+    for e in need:                       # packing is not timed
+        pool[e * sb:(e + 1) * sb] = ora.pack_expert(2, w13[e], w2[e], H, FF)
+    slot_of = np.arange(E, dtype=np.int32)    # expert e in slot e (only routed ones packed)
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        ora.moe_layer(logits, x, pool, sb, slot_of, H, FF, 2, 0, k)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or reps >= 50:
+            break
+    per_layer = el / reps
+    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    return dict(value=round(T / (per_layer * L_LAYERS), 3), unit="tokens/s", cores=cores,
+                kind="oracle",
+                sample=f"layer 0 of 30 at T={T} (int4, {len(need)} distinct experts), {reps} runs "
+                       f"of route+permute+FFN+combine, {per_layer * 1e3:.1f} ms per layer, "
+                       f"scaled x30 to the stack step")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--tokens", type=int, default=16)
+    ap.add_argument("--prefill-steps", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(see DESIGN.md for how the path would shard); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import expert_ffn_amd as lib
+    lib.lib()
+    dev = torch.device("cuda:0")
+    E, k, H, FF = G["E"], G["k"], G["H"], G["FF"]
+    fmt = lib.W_INT4_G64
+    T = args.tokens
+
+    t0 = time.time()
+    log(f"building the {L_LAYERS}-layer int4 stack ...")
+    pool, sb, slots = build_stack(lib, args.seed, L_LAYERS, E, H, FF, fmt, dev)
+    log(f"  pool {pool.numel() / 2**30:.2f} GiB, slot {sb} B, built in {time.time() - t0:.1f} s")
+
+    stream = torch.cuda.Stream()
+    logits, xs = layer_inputs(args.seed, L_LAYERS, T, E, H, dev)
+    with torch.cuda.stream(stream):
+        run = StackRunner(lib, pool, sb, slots, T, E, k, H, FF, fmt, logits, xs, stream)
+        routing = realised_routing(lib, run, logits)
+        for _ in range(args.warmup):
+            run.step()
+        torch.cuda.synchronize()
+        graph = None
+        if not args.no_graph:
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph, stream=stream):
+                run.step()
+            for _ in range(3):
+                graph.replay()
+        torch.cuda.synchronize()
+        # timed region: K steps
+        t_start = time.perf_counter()
+        for _ in range(args.steps):
+            graph.replay() if graph is not None else run.step()
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t_start
+        # instrumented pass (same steps, eager): per-launch gate/up durations
+        ev = [[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
+              for _ in range(L_LAYERS)]
+        gu_ms = []
+        for _ in range(max(3, min(args.steps, 20))):
+            run.step(events=ev)
+            torch.cuda.synchronize()
+            gu_ms.append([ev[l][0].elapsed_time(ev[l][1]) for l in range(L_LAYERS)])
+        t_e = time.perf_counter()
+        for _ in range(args.steps):
+            run.step()
+        torch.cuda.synchronize()
+        eager_ms = (time.perf_counter() - t_e) / args.steps * 1e3
+    ms_per_step = elapsed / args.steps * 1e3
+    tok_s = T * args.steps / elapsed
+
+    # algorithmic bytes (SURVEY's units): distinct experts' packed bytes + x, y, logits, indices
+    off = lib.blob_layout(fmt, H, FF)
+    w13_bytes = off[2]                    # w13 codes + scales (+ alignment, none at this shape)
+    per_layer_io = T * H * 2 * 2 + T * E * 4 + T * k * 4 * 4 + (E + 1) * 4
+    step_bytes = sum(d * sb + per_layer_io for d, _ in routing)
+    step_gbs = step_bytes / (ms_per_step * 1e-3) / 1e9
+    gu = np.array(gu_ms)                  # [reps, L] ms
+    gu_bytes = np.array([d * w13_bytes + T * H * 2 for d, _ in routing], np.float64)
+    achieved = float(gu_bytes.sum() / (gu.mean(0).sum() * 1e-3) / 1e9)
+    khash = kernel_source_hash()
+    traffic = measured_traffic(khash)
+    roofline = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=round(achieved / HBM_PEAK_GBS, 4), traffic=traffic,
+                    kernel="gate_up_stream_kernel<int4> (moe_ffn_gate_up)",
+                    avg_launch_us=round(float(gu.mean()) * 1e3, 2),
+                    bytes_per_launch=round(float(gu_bytes.mean())))
+
+    # prefill chunk through the same stack
+    prefill = None
+    if args.prefill_steps > 0:
+        Tp = 1024
+        lp, xp = layer_inputs(args.seed + 1, L_LAYERS, Tp, E, H, dev)
+        with torch.cuda.stream(stream):
+            runp = StackRunner(lib, pool, sb, slots, Tp, E, k, H, FF, fmt, lp, xp, stream)
+            rp = realised_routing(lib, runp, lp)
+            runp.step()
+            torch.cuda.synchronize()
+            tp = time.perf_counter()
+            for _ in range(args.prefill_steps):
+                runp.step()
+            torch.cuda.synchronize()
+            pms = (time.perf_counter() - tp) / args.prefill_steps * 1e3
+        flops = sum(r for _, r in rp) * 6.0 * H * FF
+        prefill = dict(T=Tp, ms_per_chunk=round(pms, 3), tokens_per_s=round(Tp / (pms * 1e-3), 1),
+                       mfma_tflops=round(flops / (pms * 1e-3) / 1e12, 1),
+                       mfma_frac=round(flops / (pms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4))
+        del runp
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a sample ...")
+        cpu = cpu_baseline(args.seed, T)
+
+    out = {
+        "metric": "expert-FFN tokens/s + HBM GB/s (int4 decode T=16) and MFMA util (T=1024 prefill)",
+        "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) logits and activations, N(0,0.02) weights; "
+                "random-init Gemma-4-26B-A4B expert shapes)",
+        "config": {"workload": "int4_stack_decode: 30 MoE layers x 128 int4 experts (w4a16, bf16 scale "
+                               "per 64, MSE clip), H=2816, FF=704, top-8 renormalised, T=16 decode, "
+                               "shuffled per-layer slot tables, 11.3 GiB resident",
+                   "layers": L_LAYERS, "experts": E, "top_k": k, "hidden": H, "ffn": FF,
+                   "tokens": T, "weights": "int4_g64", "graph": graph is not None},
+        "hbm_gbs": round(step_gbs, 1), "hbm_frac": round(step_gbs / HBM_PEAK_GBS, 4),
+        "eager_ms_per_step": round(eager_ms, 4),
+        "distinct_experts_per_layer": round(float(np.mean([d for d, _ in routing])), 2),
+        "roofline": roofline,
+        "prefill": prefill,
+        "cpu_baseline": cpu,
+        "kernel_hash": khash,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

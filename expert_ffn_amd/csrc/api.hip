@@ -71,6 +71,9 @@ moe_status check_ffn_shape(const char* fn, int32_t E, int32_t H, int32_t FF, int
     if (FF < ffq || FF % ffq)
         return fail(MOE_E_SHAPE, fn, "FF=%d is not a positive multiple of %d for this format", FF, ffq);
     if (static_cast<int64_t>(T) * k > (1ll << 30)) return fail(MOE_E_SHAPE, fn, "T*k too large");
+    // the kernels address activations and h with 31-bit buffer offsets
+    if (static_cast<int64_t>(T) * H * 2 >= (1ll << 31) || static_cast<int64_t>(T) * k * FF * 2 >= (1ll << 31))
+        return fail(MOE_E_SHAPE, fn, "T=%d too large for this H/FF (activation or h buffer >= 2 GiB)", T);
     return MOE_OK;
 }
 
@@ -171,6 +174,8 @@ static moe_status ffn_entry(const char* fn, int phases, const void* pool, uint64
     P.x_dt = x_dtype;
     P.xq = nullptr;
     P.xq_out = reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(ws) + wl.xq_off);
+    P.xsum = nullptr;
+    P.xsum_out = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + wl.xsum_off);
     P.h = reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(ws) + wl.h_off);
     P.out = out_routes;
     P.out_dt = out_dtype;

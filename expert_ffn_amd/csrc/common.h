@@ -39,10 +39,27 @@ __device__ __forceinline__ f32x4 mfma16x16x32(const u32x4& a, const u32x4& b, co
                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
+// Raw buffer loads: a lane whose byte offset is at or past num_records reads
+// zeros without touching memory, so lanes without work pass NO_LANE.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr uint32_t NO_LANE = 0x80000000u;
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
+                                             static_cast<int>(bytes), 0x00020000);
+}
+__device__ __forceinline__ u32x4 bload16(rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ u32x2 bload8(rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+}
+
+// Gated activations.  GELU (tanh form) uses 0.5 (1 + tanh(u)) = 1 / (1 + e^(-2u)):
+//   gelu(g) = g / (1 + exp(-2 sqrt(2/pi) (g + 0.044715 g^3)));  silu(g) = g / (1 + exp(-g)).
+// One exponential and one reciprocal; both limits are exact (exp overflow gives 0).
 __device__ __forceinline__ float act_fn(int act, float g) {
-    if (act == ACT_SILU) return g / (1.0f + __expf(-g));
-    const float c = 0.7978845608028654f;  // sqrt(2/pi)
-    return 0.5f * g * (1.0f + tanhf(c * (g + 0.044715f * g * g * g)));
+    const float z = act == ACT_SILU ? -g : -1.5957691216057308f * (g + 0.044715f * g * g * g);
+    return g * __frcp_rn(1.0f + __expf(z));
 }
 
 }  // namespace moe

@@ -53,12 +53,21 @@ template <int FMT> __device__ __forceinline__ int b_off(int s, int q) {
     return FMT == W_BF16 ? s * 32 + q * 8 : s * 64 + q * 16;
 }
 
+// (a & mask) | magic in one VALU op.  gfx9 VOP3 encodings take no literal, so
+// without this the compiler emits a separate v_and and v_or per pair.
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t mask, uint32_t magic) {
+    uint32_t r;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "s"(mask), "v"(magic));
+    return r;
+}
+
 __device__ __forceinline__ u32x4 deq_int4(uint32_t d) {
+    const uint32_t M = 0x000F000Fu, C = 0x43004300u;
     u32x4 r;
-    r[0] = (d & 0x000F000Fu) | 0x43004300u;
-    r[1] = ((d >> 4) & 0x000F000Fu) | 0x43004300u;
-    r[2] = ((d >> 8) & 0x000F000Fu) | 0x43004300u;
-    r[3] = ((d >> 12) & 0x000F000Fu) | 0x43004300u;
+    r[0] = and_or(d, M, C);
+    r[1] = and_or(d >> 4, M, C);
+    r[2] = and_or(d >> 8, M, C);
+    r[3] = and_or(d >> 12, M, C);
     return r;
 }
 
@@ -116,7 +125,7 @@ __global__ __launch_bounds__(256) void prep_x_kernel(const void* __restrict__ x,
 // (i & 8) | perm8(i & 7), so that the four h values a lane ends with are four
 // consecutive entries of h in the w2 operand order.
 template <int FMT, int KSPLIT, int NGC>
-__global__ __launch_bounds__(64 * KSPLIT) void gate_up_stream_kernel(FfnParams P) {
+__global__ __launch_bounds__(64 * KSPLIT) void gate_up_generic_kernel(FfnParams P) {
     using G = Geo<FMT>;
     using AF = typename G::A;
     constexpr bool PERM_H = (FMT == W_INT4);
@@ -240,7 +249,7 @@ __global__ __launch_bounds__(64 * KSPLIT) void gate_up_stream_kernel(FfnParams P
 // Workgroup = 4 waves on one (expert, 64 rows of H); wave w owns 16 rows and
 // the whole K = FF.  B rows are the h rows of the expert's route positions.
 template <int FMT, int NGC>
-__global__ __launch_bounds__(256) void down_stream_kernel(FfnParams P) {
+__global__ __launch_bounds__(256) void down_generic_kernel(FfnParams P) {
     using G = Geo<FMT>;
     using AF = typename G::A;
     extern __shared__ float smem[];
@@ -323,42 +332,754 @@ __global__ __launch_bounds__(256) void down_stream_kernel(FfnParams P) {
     }
 }
 
+// ------------------------------------------------- streaming, prefetched --
+// The decode kernels (at most 64 tokens, so no expert has more than four
+// tiles of 16 routes; blockIdx.y picks the tile).  A wavefront owns NG steps
+// of K for its row tiles and issues every weight load of that range at once;
+// the route index is loaded first so that the activation loads can follow, D
+// steps ahead of the MFMAs.  Scale staging into LDS happens while the weight
+// loads are in flight.  Lanes past the group's last route read the group's
+// first route: their D columns are computed and never stored.
+
+// (rows of the tile held by D row i) for the w2 operand order of int4 h
+__device__ __forceinline__ int tile_row(bool perm, int i) { return perm ? ((i & 8) | perm8(i & 7)) : i; }
+
+// one step of the gate/up MFMAs for both tiles
+template <int FMT>
+__device__ __forceinline__ void step_gu(const typename Geo<FMT>::A& ag, const typename Geo<FMT>::A& au,
+                                        const u32x4* b, const f32x4& sg, const f32x4& su, f32x4& accg,
+                                        f32x4& accu, f32x4& cc) {
+    const f32x4 zero = {0, 0, 0, 0};
+    if constexpr (FMT == W_INT4) {
+        const u32x4 kb = splat(0xC308C308u);  // bf16 -136
+        f32x4 c = mfma16x16x32(kb, b[0], zero);
+        c = mfma16x16x32(kb, b[1], c);
+        f32x4 t = mfma16x16x32(deq_int4(ag[0]), b[0], c);
+        t = mfma16x16x32(deq_int4(ag[1]), b[1], t);
+        accg += sg * t;
+        t = mfma16x16x32(deq_int4(au[0]), b[0], c);
+        t = mfma16x16x32(deq_int4(au[1]), b[1], t);
+        accu += su * t;
+    } else if constexpr (FMT == W_INT8) {
+        const u32x4 kb = splat(0xC300C300u);  // bf16 -128
+        cc = mfma16x16x32(kb, b[0], cc);
+        cc = mfma16x16x32(kb, b[1], cc);
+        accg = mfma16x16x32(deq_int8(ag[0], ag[1]), b[0], accg);
+        accg = mfma16x16x32(deq_int8(ag[2], ag[3]), b[1], accg);
+        accu = mfma16x16x32(deq_int8(au[0], au[1]), b[0], accu);
+        accu = mfma16x16x32(deq_int8(au[2], au[3]), b[1], accu);
+    } else {
+        accg = mfma16x16x32(ag, b[0], accg);
+        accu = mfma16x16x32(au, b[0], accu);
+    }
+}
+
+template <int FMT, int NG, int KSPLIT>
+__global__ __launch_bounds__(64 * KSPLIT) __attribute__((amdgpu_waves_per_eu(3)))
+void gate_up_fast_kernel(FfnParams P) {
+    using G = Geo<FMT>;
+    using AF = typename G::A;
+    constexpr int MF = G::MF;
+    constexpr bool PERM_H = (FMT == W_INT4);
+    constexpr int D = NG < 3 ? NG : 3;          // activation prefetch depth (steps)
+    constexpr int SPL = (32 * NG + 63) / 64;     // scale values staged per lane (int4)
+    extern __shared__ float smem[];
+    const int ntile = P.FF >> 4;
+    const int e = blockIdx.x / ntile, tile = blockIdx.x - e * ntile;
+    const int beg = P.offsets[e] + 16 * static_cast<int>(blockIdx.y), end = P.offsets[e + 1];
+    if (beg >= end) return;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, r = lane & 15, q = lane >> 4;
+    const uint8_t* blob = P.pool + static_cast<uint64_t>(P.slot_of[e]) * P.slot_bytes;
+    const int n0 = tile << 4;
+    const int s0 = wave * NG;
+    const int64_t rs = row_bytes<FMT>(P.H);
+    const uint8_t* ag_row = blob + P.o13 + static_cast<int64_t>(n0 + tile_row(PERM_H, r)) * rs;
+    const uint8_t* au_row = ag_row + static_cast<int64_t>(P.FF) * rs;
+
+    // 1. route of this lane's column (invalid columns read route beg: their D
+    //    column is computed from real data and never stored)
+    const int p = beg + r;
+    const bool valid = p < end;
+    const int route = P.sorted_route[valid ? p : beg];
+    // 2. every weight fragment of this wave's K range
+    AF ag[NG], au[NG];
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+        ag[g] = *reinterpret_cast<const AF*>(ag_row + a_off<FMT>(s0 + g, q));
+        au[g] = *reinterpret_cast<const AF*>(au_row + a_off<FMT>(s0 + g, q));
+    }
+    // 3. scales: int4 staged to LDS as [tile][step][D row], int8 per row
+    float* s_sc = smem + wave * (32 * NG);
+    float* s_red = smem + (FMT == W_INT4 ? KSPLIT * 32 * NG : 0);
+    f32x4 sg_row = {0, 0, 0, 0}, su_row = {0, 0, 0, 0};
+    if constexpr (FMT == W_INT4) {
+        const int Gr = P.H / 64;
+        const uint16_t* sc = reinterpret_cast<const uint16_t*>(blob + P.os13);
+        float sv[SPL];
+#pragma unroll
+        for (int m = 0; m < SPL; ++m) {
+            const int idx = lane + 64 * m;
+            sv[m] = 0.0f;
+            if (idx < 32 * NG) {
+                const int rowi = idx / NG, g = idx - rowi * NG;   // rowi: tile*16 + D row
+                const int row = (rowi >> 4) * P.FF + n0 + tile_row(true, rowi & 15);
+                sv[m] = bf16_to_f32(sc[static_cast<int64_t>(row) * Gr + s0 + g]);
+            }
+        }
+#pragma unroll
+        for (int m = 0; m < SPL; ++m) {
+            const int idx = lane + 64 * m;
+            if (idx < 32 * NG) {
+                const int rowi = idx / NG, g = idx - rowi * NG;
+                s_sc[((rowi >> 4) * NG + g) * 16 + (rowi & 15)] = sv[m];
+            }
+        }
+    } else if constexpr (FMT == W_INT8) {
+        const float* sc = reinterpret_cast<const float*>(blob + P.os13);
+        sg_row = *reinterpret_cast<const f32x4*>(sc + n0 + 4 * q);
+        su_row = *reinterpret_cast<const f32x4*>(sc + P.FF + n0 + 4 * q);
+    }
+    // 4. activations, D steps ahead of the MFMAs
+    const uint16_t* xrow = P.xq + static_cast<int64_t>(route / P.k) * P.H;
+    u32x4 b[D][MF];
+#pragma unroll
+    for (int g = 0; g < D; ++g)
+#pragma unroll
+        for (int m = 0; m < MF; ++m) b[g][m] = *reinterpret_cast<const u32x4*>(xrow + b_off<FMT>(s0 + g, q) + 8 * m);
+    __syncthreads();
+
+    const f32x4 zero = {0, 0, 0, 0};
+    f32x4 accg = zero, accu = zero, cc = zero;
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+        f32x4 sg = zero, su = zero;
+        if constexpr (FMT == W_INT4) {
+            sg = *reinterpret_cast<const f32x4*>(s_sc + g * 16 + 4 * q);
+            su = *reinterpret_cast<const f32x4*>(s_sc + (NG + g) * 16 + 4 * q);
+        }
+        step_gu<FMT>(ag[g], au[g], b[g % D], sg, su, accg, accu, cc);
+        if (g + D < NG) {
+#pragma unroll
+            for (int m = 0; m < MF; ++m)
+                b[g % D][m] = *reinterpret_cast<const u32x4*>(xrow + b_off<FMT>(s0 + g + D, q) + 8 * m);
+        }
+    }
+    if constexpr (FMT == W_INT8) {
+        accg = sg_row * (accg + cc);
+        accu = su_row * (accu + cc);
+    }
+    if constexpr (KSPLIT > 1) {
+        if (wave > 0) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                s_red[((wave - 1) * 8 + j) * 64 + lane] = accg[j];
+                s_red[((wave - 1) * 8 + 4 + j) * 64 + lane] = accu[j];
+            }
+        }
+        __syncthreads();
+        if (wave != 0) return;
+#pragma unroll
+        for (int w = 1; w < KSPLIT; ++w)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                accg[j] += s_red[((w - 1) * 8 + j) * 64 + lane];
+                accu[j] += s_red[((w - 1) * 8 + 4 + j) * 64 + lane];
+            }
+    }
+    if (valid) {
+        const uint32_t h0 = pack_bf16x2(act_fn(P.act, accg[0]) * accu[0], act_fn(P.act, accg[1]) * accu[1]);
+        const uint32_t h1 = pack_bf16x2(act_fn(P.act, accg[2]) * accu[2], act_fn(P.act, accg[3]) * accu[3]);
+        *reinterpret_cast<u32x2*>(P.h + static_cast<int64_t>(p) * P.FF + n0 + 4 * q) = u32x2{h0, h1};
+    }
+}
+
+// Workgroup = 4 waves = (4 / KS) tiles of 16 rows of H x KS parts of K = FF,
+// one tile of 16 routes (blockIdx.y).
+template <int FMT, int NG, int KS>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3)))
+void down_fast_kernel(FfnParams P) {
+    using G = Geo<FMT>;
+    using AF = typename G::A;
+    constexpr int MF = G::MF;
+    constexpr int RTW = 4 / KS;
+    constexpr int D = NG < 3 ? NG : 3;
+    constexpr int SPL = (16 * NG + 63) / 64;
+    extern __shared__ float smem[];
+    const int nblk = P.H / (16 * RTW);
+    const int e = blockIdx.x / nblk, blk = blockIdx.x - e * nblk;
+    const int beg = P.offsets[e] + 16 * static_cast<int>(blockIdx.y), end = P.offsets[e + 1];
+    if (beg >= end) return;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, r = lane & 15, q = lane >> 4;
+    const int rt = wave / KS, kp = wave - rt * KS;
+    const uint8_t* blob = P.pool + static_cast<uint64_t>(P.slot_of[e]) * P.slot_bytes;
+    const int m0 = (blk * RTW + rt) * 16;
+    const int s0 = kp * NG;
+    const uint8_t* a_row = blob + P.o2 + static_cast<int64_t>(m0 + r) * row_bytes<FMT>(P.FF);
+
+    const int p = beg + r;
+    const bool valid = p < end;
+    AF a[NG];
+#pragma unroll
+    for (int g = 0; g < NG; ++g) a[g] = *reinterpret_cast<const AF*>(a_row + a_off<FMT>(s0 + g, q));
+    float* s_sc = smem + wave * (16 * NG);
+    float* s_red = smem + (FMT == W_INT4 ? 4 * 16 * NG : 0);
+    f32x4 s_row = {0, 0, 0, 0};
+    if constexpr (FMT == W_INT4) {
+        const int Gr = P.FF / 64;
+        const uint16_t* sc = reinterpret_cast<const uint16_t*>(blob + P.os2);
+        float sv[SPL];
+#pragma unroll
+        for (int m = 0; m < SPL; ++m) {
+            const int idx = lane + 64 * m;
+            sv[m] = 0.0f;
+            if (idx < 16 * NG) {
+                const int i = idx / NG, g = idx - i * NG;
+                sv[m] = bf16_to_f32(sc[static_cast<int64_t>(m0 + i) * Gr + s0 + g]);
+            }
+        }
+#pragma unroll
+        for (int m = 0; m < SPL; ++m) {
+            const int idx = lane + 64 * m;
+            if (idx < 16 * NG) {
+                const int i = idx / NG, g = idx - i * NG;
+                s_sc[g * 16 + i] = sv[m];
+            }
+        }
+    } else if constexpr (FMT == W_INT8) {
+        s_row = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(blob + P.os2) + m0 + 4 * q);
+    }
+    const uint16_t* hrow = P.h + static_cast<int64_t>(valid ? p : beg) * P.FF;
+    u32x4 b[D][MF];
+#pragma unroll
+    for (int g = 0; g < D; ++g)
+#pragma unroll
+        for (int m = 0; m < MF; ++m) b[g][m] = *reinterpret_cast<const u32x4*>(hrow + b_off<FMT>(s0 + g, q) + 8 * m);
+    __syncthreads();
+
+    const f32x4 zero = {0, 0, 0, 0};
+    f32x4 acc = zero, cc = zero;
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+        const u32x4* bg = b[g % D];
+        if constexpr (FMT == W_INT4) {
+            const u32x4 kb = splat(0xC308C308u);
+            f32x4 t = mfma16x16x32(kb, bg[0], zero);
+            t = mfma16x16x32(kb, bg[1], t);
+            t = mfma16x16x32(deq_int4(a[g][0]), bg[0], t);
+            t = mfma16x16x32(deq_int4(a[g][1]), bg[1], t);
+            acc += *reinterpret_cast<const f32x4*>(s_sc + g * 16 + 4 * q) * t;
+        } else if constexpr (FMT == W_INT8) {
+            const u32x4 kb = splat(0xC300C300u);
+            cc = mfma16x16x32(kb, bg[0], cc);
+            cc = mfma16x16x32(kb, bg[1], cc);
+            acc = mfma16x16x32(deq_int8(a[g][0], a[g][1]), bg[0], acc);
+            acc = mfma16x16x32(deq_int8(a[g][2], a[g][3]), bg[1], acc);
+        } else {
+            acc = mfma16x16x32(a[g], bg[0], acc);
+        }
+        if (g + D < NG) {
+#pragma unroll
+            for (int m = 0; m < MF; ++m)
+                b[g % D][m] = *reinterpret_cast<const u32x4*>(hrow + b_off<FMT>(s0 + g + D, q) + 8 * m);
+        }
+    }
+    if constexpr (FMT == W_INT8) acc = s_row * (acc + cc);
+    if constexpr (KS > 1) {
+        if (kp > 0) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) s_red[((wave - 1) * 4 + j) * 64 + lane] = acc[j];
+        }
+        __syncthreads();
+        if (kp != 0) return;
+#pragma unroll
+        for (int w = 1; w < KS; ++w)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[j] += s_red[((wave + w - 1) * 4 + j) * 64 + lane];
+    }
+    if (valid) {
+        const int64_t o = static_cast<int64_t>(p) * P.H + m0 + 4 * q;
+        if (P.out_dt == F32) {
+            *reinterpret_cast<f32x4*>(static_cast<float*>(P.out) + o) = acc;
+        } else {
+            *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(P.out) + o) =
+                u32x2{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
+        }
+    }
+}
+
+// ------------------------------------------------------------ int4 paths --
+// An int4 lane loads 16 bytes = 32 elements of its row per instruction, so a
+// 16-row tile moves 64 contiguous bytes per row (two 64-element groups).  Two
+// v_permlane32_swap exchanges then give every lane two dwords of each group:
+// dwords 0,1 hold group A (elements 0..63 of the 128-element block), dwords
+// 2,3 group B.  MFMA m uses dword m of every lane, so lane group q supplies
+// block elements 64(m/2) + 8(m%2) + 16(q/2) + 32(q%2) + perm8(0..7).  A row
+// whose length K is an odd number of groups ends with one 64-element group
+// read the plain way (8 bytes per lane, elements 16q + 8m + perm8(0..7)).
+// Activations and h are stored in this position order ("operand order"):
+// position p = 128 G + 32 q + 8 m + j holds element int4_pos_to_k(p, K).
+__host__ __device__ __forceinline__ int perm8h(int j) { return (j >> 1) | ((j & 1) << 2); }
+__host__ __device__ __forceinline__ int int4_pos_to_k(int p, int K) {
+    const int full = K & ~127;
+    if (p < full) {
+        const int w = p & 127, q = w >> 5, m = (w >> 3) & 3, j = w & 7;
+        return (p & ~127) + ((m >> 1) << 6) + ((m & 1) << 3) + ((q >> 1) << 4) + ((q & 1) << 5) + perm8h(j);
+    }
+    const int w = p - full, q = w >> 4, m = (w >> 3) & 1, j = w & 7;
+    return full + (q << 4) + (m << 3) + perm8h(j);
+}
+// rows of the 16 positions [16u, 16u+16): base + (i & 8) + perm8(i & 7)
+__device__ __forceinline__ int int4_tile_base(int u, int K) { return int4_pos_to_k(16 * u, K) & ~15; }
+
+__device__ __forceinline__ u32x4 regroup(u32x4 v) {
+    const auto x = __builtin_amdgcn_permlane32_swap(v[0], v[2], false, false);
+    const auto y = __builtin_amdgcn_permlane32_swap(v[1], v[3], false, false);
+    return u32x4{x[0], y[0], x[1], y[1]};
+}
+
+// acc += s_grp * (A . B - 136 * sum B) for one 64-element group given as two
+// MFMA operands (one per dword)
+__device__ __forceinline__ void int4_group(uint32_t d0, uint32_t d1, const u32x4& b0, const u32x4& b1,
+                                           const f32x4& s, f32x4& acc) {
+    const f32x4 zero = {0, 0, 0, 0};
+    const u32x4 kb = splat(0xC308C308u);  // bf16 -136
+    f32x4 t = mfma16x16x32(kb, b0, zero);
+    t = mfma16x16x32(kb, b1, t);
+    t = mfma16x16x32(deq_int4(d0), b0, t);
+    t = mfma16x16x32(deq_int4(d1), b1, t);
+    acc += s * t;
+}
+
+// One wave: 16 rows of a w13 or w2 tile over the K range [k0, k0 + Kw) of a
+// row of K elements; rows a_row (this lane's row, already offset to k0/2),
+// activations brow (this lane's column, at position k0), scales s_sc [group][16].
+template <int CH>
+__device__ __forceinline__ f32x4 int4_tile(const uint8_t* a_row, rsrc_t bres, uint32_t boff, const float* s_sc,
+                                           int nds, bool tail, int q) {
+    // boff: byte offset of this lane's activation row at the K range start, or NO_LANE
+    f32x4 acc = {0, 0, 0, 0};
+    for (int c = 0; c < nds; c += CH) {
+        u32x4 a[CH];
+#pragma unroll
+        for (int i = 0; i < CH; ++i)
+            if (c + i < nds) a[i] = *reinterpret_cast<const u32x4*>(a_row + 64 * (c + i) + 16 * q);
+        u32x4 b[2][4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) b[0][m] = bload16(bres, boff + 2 * (128 * c + 32 * q + 8 * m));
+#pragma unroll
+        for (int i = 0; i < CH; ++i) {
+            if (c + i < nds) {
+                if (i + 1 < CH && c + i + 1 < nds) {
+#pragma unroll
+                    for (int m = 0; m < 4; ++m)
+                        b[(i + 1) & 1][m] = bload16(bres, boff + 2 * (128 * (c + i + 1) + 32 * q + 8 * m));
+                }
+                const u32x4 v = regroup(a[i]);
+                const u32x4* bb = b[i & 1];
+                const int g = 2 * (c + i);
+                int4_group(v[0], v[1], bb[0], bb[1], *reinterpret_cast<const f32x4*>(s_sc + g * 16 + 4 * q), acc);
+                int4_group(v[2], v[3], bb[2], bb[3], *reinterpret_cast<const f32x4*>(s_sc + (g + 1) * 16 + 4 * q), acc);
+            }
+        }
+    }
+    if (tail) {
+        const u32x2 a = *reinterpret_cast<const u32x2*>(a_row + 64 * nds + 8 * q);
+        const u32x4 b0 = bload16(bres, boff + 2 * (128 * nds + 16 * q));
+        const u32x4 b1 = bload16(bres, boff + 2 * (128 * nds + 16 * q + 8));
+        int4_group(a[0], a[1], b0, b1, *reinterpret_cast<const f32x4*>(s_sc + 2 * nds * 16 + 4 * q), acc);
+    }
+    return acc;
+}
+
+// stage the scales of 16 rows (rows16[i]) x ng groups starting at group g0
+// into s_sc[g][i] as fp32.  SPL > 0: all loads first (SPL per lane, so
+// 16 * ng <= 64 * SPL), then the LDS stores; SPL == 0: a plain loop.
+template <int SPL>
+__device__ __forceinline__ void stage_scales(const uint16_t* sc_rows, int row_stride, int g0, int ng,
+                                             const int* rows16, float* s_sc, int lane) {
+    if constexpr (SPL > 0) {
+        float sv[SPL];
+#pragma unroll
+        for (int m = 0; m < SPL; ++m) {
+            const int idx = lane + 64 * m;
+            sv[m] = 0.0f;
+            if (idx < 16 * ng) {
+                const int i = idx / ng, g = idx - i * ng;
+                sv[m] = bf16_to_f32(sc_rows[static_cast<int64_t>(rows16[i]) * row_stride + g0 + g]);
+            }
+        }
+#pragma unroll
+        for (int m = 0; m < SPL; ++m) {
+            const int idx = lane + 64 * m;
+            if (idx < 16 * ng) {
+                const int i = idx / ng, g = idx - i * ng;
+                s_sc[g * 16 + i] = sv[m];
+            }
+        }
+    } else {
+        for (int idx = lane; idx < 16 * ng; idx += 64) {
+            const int i = idx / ng, g = idx - i * ng;
+            s_sc[g * 16 + i] = bf16_to_f32(sc_rows[static_cast<int64_t>(rows16[i]) * row_stride + g0 + g]);
+        }
+    }
+}
+
+// gate/up, int4: workgroup = 2*KH waves on one (expert, 16 positions of h,
+// 16 routes); wave w = (tile t = w / KH: gate or up, K part w % KH).
+template <int KH, int CH, int SPL>
+__global__ __launch_bounds__(128 * KH) void gate_up_int4_kernel(FfnParams P) {
+    extern __shared__ float smem[];
+    const int ntile = P.FF >> 4;
+    const int e = blockIdx.x / ntile, u = blockIdx.x - e * ntile;
+    const int beg = P.offsets[e] + 16 * static_cast<int>(blockIdx.y), end = P.offsets[e + 1];
+    if (beg >= end) return;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, r = lane & 15, q = lane >> 4;
+    const int t = wave / KH, hp = wave - t * KH;
+    const uint8_t* blob = P.pool + static_cast<uint64_t>(P.slot_of[e]) * P.slot_bytes;
+    const int n0 = int4_tile_base(u, P.FF);
+    const int Kw = P.H / KH, k0 = hp * Kw;
+    const int rowbase = t * P.FF + n0;
+    const uint8_t* a_row = blob + P.o13 + static_cast<int64_t>(rowbase + (r & 8) + perm8(r & 7)) * (P.H / 2) + k0 / 2;
+    const int p = beg + r;
+    const bool valid = p < end;
+    const int route = P.sorted_route[valid ? p : beg];
+    const int ngw = Kw / 64;   // groups per wave
+    float* s_sc = smem + wave * (16 * ngw);
+    float* s_red = smem + 2 * KH * 16 * ngw;
+    {
+        int rows16[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) rows16[i] = rowbase + (i & 8) + perm8(i & 7);
+        stage_scales<SPL>(reinterpret_cast<const uint16_t*>(blob + P.os13), P.H / 64, k0 / 64, Kw / 64, rows16,
+                           s_sc, lane);
+    }
+    __syncthreads();
+    const rsrc_t xres = make_rsrc(P.xq, static_cast<uint32_t>(P.T) * P.H * 2);
+    const uint32_t xoff = valid ? static_cast<uint32_t>(((route / P.k) * P.H + k0) * 2) : NO_LANE;
+    const f32x4 acc = int4_tile<CH>(a_row, xres, xoff, s_sc, Kw >> 7, (Kw & 127) != 0, q);
+    if (wave > 0) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) s_red[((wave - 1) * 4 + j) * 64 + lane] = acc[j];
+    }
+    __syncthreads();
+    if (wave != 0) return;
+    f32x4 g = acc, uu = {0, 0, 0, 0};
+#pragma unroll
+    for (int w = 1; w < 2 * KH; ++w)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float v = s_red[((w - 1) * 4 + j) * 64 + lane];
+            if (w < KH) g[j] += v; else uu[j] += v;
+        }
+    if (valid) {
+        const uint32_t h0 = pack_bf16x2(act_fn(P.act, g[0]) * uu[0], act_fn(P.act, g[1]) * uu[1]);
+        const uint32_t h1 = pack_bf16x2(act_fn(P.act, g[2]) * uu[2], act_fn(P.act, g[3]) * uu[3]);
+        *reinterpret_cast<u32x2*>(P.h + static_cast<int64_t>(p) * P.FF + 16 * u + 4 * q) = u32x2{h0, h1};
+    }
+}
+
+// down, int4: workgroup = 4 waves x 16 rows of H, whole K = FF, 16 routes.
+template <int CH, int SPL>
+__global__ __launch_bounds__(256) void down_int4_kernel(FfnParams P) {
+    extern __shared__ float smem[];
+    const int nblk = P.H >> 6;
+    const int e = blockIdx.x / nblk, blk = blockIdx.x - e * nblk;
+    const int beg = P.offsets[e] + 16 * static_cast<int>(blockIdx.y), end = P.offsets[e + 1];
+    if (beg >= end) return;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, r = lane & 15, q = lane >> 4;
+    const uint8_t* blob = P.pool + static_cast<uint64_t>(P.slot_of[e]) * P.slot_bytes;
+    const int m0 = blk * 64 + wave * 16;
+    const uint8_t* a_row = blob + P.o2 + static_cast<int64_t>(m0 + r) * (P.FF / 2);
+    const int p = beg + r;
+    const bool valid = p < end;
+    float* s_sc = smem + wave * (16 * (P.FF / 64));
+    {
+        int rows16[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) rows16[i] = m0 + i;
+        stage_scales<SPL>(reinterpret_cast<const uint16_t*>(blob + P.os2), P.FF / 64, 0, P.FF / 64, rows16, s_sc,
+                           lane);
+    }
+    __syncthreads();
+    const rsrc_t hres = make_rsrc(P.h, static_cast<uint32_t>(P.T) * P.k * P.FF * 2);
+    const uint32_t hoff = valid ? static_cast<uint32_t>(p) * P.FF * 2 : NO_LANE;
+    const f32x4 acc = int4_tile<CH>(a_row, hres, hoff, s_sc, P.FF >> 7, (P.FF & 127) != 0, q);
+    if (valid) {
+        const int64_t o = static_cast<int64_t>(p) * P.H + m0 + 4 * q;
+        if (P.out_dt == F32) {
+            *reinterpret_cast<f32x4*>(static_cast<float*>(P.out) + o) = acc;
+        } else {
+            *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(P.out) + o) =
+                u32x2{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
+        }
+    }
+}
+
+// gate/up, int4, decode fast path (H = 256 * NDS): workgroup = 4 waves =
+// (tile t: gate or up) x (K half hp), each 16 rows x NDS double steps.
+// Issue order keeps the in-order load counter from serialising the wave:
+// route indices (uniform, scalar loads), then this lane's row scales, the
+// first two weight fragments, the first activations, then the remaining
+// weights.  The -136 bias of the expanded codes is folded into each group's
+// MFMA accumulator as -136 * (sum of the group's bf16 activations), which the
+// preparation kernel stores per token and group (xsum).
+template <int NDS>
+__global__ __launch_bounds__(256) void gate_up_int4_fast_kernel(FfnParams P) {
+    constexpr int NG = 2 * NDS;                 // groups per wave (<= 32)
+    static_assert(NG <= 32, "the bias MFMA takes 32 groups");
+    extern __shared__ float smem[];             // s_sc [4][NG][16], s_red [3][4][64]
+    const int ntile = P.FF >> 4;
+    const int e = blockIdx.x / ntile, u = blockIdx.x - e * ntile;
+    const int beg = P.offsets[e] + 16 * static_cast<int>(blockIdx.y), end = P.offsets[e + 1];
+    if (beg >= end) return;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, r = lane & 15, q = lane >> 4;
+    const int t = wave >> 1, hp = wave & 1;
+    const uint8_t* blob = P.pool + static_cast<uint64_t>(P.slot_of[e]) * P.slot_bytes;
+    const int n0 = int4_tile_base(u, P.FF);
+    const int row = t * P.FF + n0 + (r & 8) + perm8(r & 7);
+    const int k0 = hp * (P.H / 2);
+    const int G = P.H / 64;
+
+    int routes[16];
+#pragma unroll
+    for (int c = 0; c < 16; ++c) routes[c] = P.sorted_route[min(beg + c, end - 1)];
+    // scales of this lane's row, groups 8q..8q+7 of the wave's range (bf16
+    // pairs, natural order): the A operand of the bias MFMA and the source of
+    // the per-group scale staging.  Groups past NG are zeroed.
+    const uint32_t* srow = reinterpret_cast<const uint32_t*>(blob + P.os13) + (static_cast<int64_t>(row) * G + k0 / 64) / 2;
+    u32x4 sa = *reinterpret_cast<const u32x4*>(srow + 4 * (q < 3 ? q : 0));
+    const uint8_t* a_row = blob + P.o13 + static_cast<int64_t>(row) * (P.H / 2) + k0 / 2 + 16 * q;
+    u32x4 a[NDS];
+    a[0] = *reinterpret_cast<const u32x4*>(a_row);
+    if (NDS > 1) a[1] = *reinterpret_cast<const u32x4*>(a_row + 64);
+    int route = routes[0];
+#pragma unroll
+    for (int c = 1; c < 16; ++c) route = (r == c) ? routes[c] : route;
+    const int p = beg + r;
+    const bool valid = p < end;
+    const int tok = route / P.k;
+    // only lanes holding a route load activations (the others read zeros
+    // without a memory access; their D columns are never stored)
+    const rsrc_t xres = make_rsrc(P.xq, static_cast<uint32_t>(P.T) * P.H * 2);
+    const uint32_t xoff = valid ? static_cast<uint32_t>((tok * P.H + k0 + 32 * q) * 2) : NO_LANE;
+    u32x4 b[2][4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) b[0][m] = bload16(xres, xoff + 16 * m);
+    const rsrc_t sres = make_rsrc(P.xsum, static_cast<uint32_t>(P.T) * G * 4);
+    const uint32_t soff = valid ? static_cast<uint32_t>((tok * G + k0 / 64 + 8 * q) * 2) : NO_LANE;
+    const u32x4 xhi = bload16(sres, soff), xlo = bload16(sres, soff + static_cast<uint32_t>(P.T) * G * 2);
+#pragma unroll
+    for (int i = 2; i < NDS; ++i) a[i] = *reinterpret_cast<const u32x4*>(a_row + 64 * i);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        if (8 * q + 2 * j >= NG) sa[j] = 0u;
+    // scales -> wave-private LDS in the D-row layout (row r of this lane is D row r)
+    float* s_sc = smem + wave * (16 * NG);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int g = 8 * q + 2 * j;
+        if (g < NG) {
+            s_sc[g * 16 + r] = __uint_as_float(sa[j] << 16);
+            s_sc[(g + 1) * 16 + r] = __uint_as_float(sa[j] & 0xFFFF0000u);
+        }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+    // bias of the expanded codes: -136 * sum_g s[row][g] * X[col][g]
+    const f32x4 zero = {0, 0, 0, 0};
+    f32x4 corr = mfma16x16x32(sa, xhi, zero);
+    corr = mfma16x16x32(sa, xlo, corr);
+    f32x4 acc = corr * -136.0f;
+#pragma unroll
+    for (int i = 0; i < NDS; ++i) {
+        if (i + 1 < NDS) {
+#pragma unroll
+            for (int m = 0; m < 4; ++m) b[(i + 1) & 1][m] = bload16(xres, xoff + 256 * (i + 1) + 16 * m);
+        }
+        const u32x4 v = regroup(a[i]);
+        const u32x4* bb = b[i & 1];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            f32x4 tt = mfma16x16x32(deq_int4(v[2 * h]), bb[2 * h], zero);
+            tt = mfma16x16x32(deq_int4(v[2 * h + 1]), bb[2 * h + 1], tt);
+            acc += *reinterpret_cast<const f32x4*>(s_sc + (2 * i + h) * 16 + 4 * q) * tt;
+        }
+    }
+    float* s_red = smem + 4 * 16 * NG;
+    if (wave > 0) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) s_red[((wave - 1) * 4 + j) * 64 + lane] = acc[j];
+    }
+    __syncthreads();
+    if (wave != 0) return;
+    f32x4 g = acc, uu;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        g[j] += s_red[(0 * 4 + j) * 64 + lane];
+        uu[j] = s_red[(1 * 4 + j) * 64 + lane] + s_red[(2 * 4 + j) * 64 + lane];
+    }
+    if (valid) {
+        const uint32_t h0 = pack_bf16x2(act_fn(P.act, g[0]) * uu[0], act_fn(P.act, g[1]) * uu[1]);
+        const uint32_t h1 = pack_bf16x2(act_fn(P.act, g[2]) * uu[2], act_fn(P.act, g[3]) * uu[3]);
+        *reinterpret_cast<u32x2*>(P.h + static_cast<int64_t>(p) * P.FF + 16 * u + 4 * q) = u32x2{h0, h1};
+    }
+}
+
+// x -> xq in the int4 operand order of K = H (one thread per 8 positions)
+template <int XT>
+__global__ __launch_bounds__(256) void prep_x_int4_kernel(const void* __restrict__ x, int T, int H,
+                                                          uint16_t* __restrict__ xq, float* __restrict__ xsum) {
+    // xsum (H % 128 == 0 only): per token and 64-element group, the sum of the
+    // bf16 values in that group, as bf16 hi [T, H/64] followed by bf16 lo [T, H/64]
+    const int64_t b = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    if (b >= static_cast<int64_t>(T) * (H / 8)) return;   // T * H / 8 is a multiple of 16: whole groups exit together
+    const int64_t t = b / (H / 8);
+    const int p0 = static_cast<int>(b - t * (H / 8)) * 8;
+    const int k0 = int4_pos_to_k(p0, H);   // elements k0 + perm8(j), j = 0..7
+    float v[8];
+    if (XT == F32) {
+        const f32x4* src = reinterpret_cast<const f32x4*>(static_cast<const float*>(x) + t * H + k0);
+        const f32x4 a = src[0], c = src[1];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            v[j] = a[j];
+            v[4 + j] = c[j];
+        }
+    } else {
+        const u32x4 a = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(x) + t * H + k0);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            v[2 * j] = __uint_as_float(a[j] << 16);
+            v[2 * j + 1] = __uint_as_float(a[j] & 0xFFFF0000u);
+        }
+    }
+    u32x4 o;
+    float sum = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const uint16_t lo = f32_to_bf16(v[perm8(2 * j)]), hi = f32_to_bf16(v[perm8(2 * j + 1)]);
+        o[j] = static_cast<uint32_t>(lo) | (static_cast<uint32_t>(hi) << 16);
+        sum += bf16_to_f32(lo) + bf16_to_f32(hi);
+    }
+    *reinterpret_cast<u32x4*>(xq + t * H + p0) = o;
+    if (xsum != nullptr) {
+        // the 8 blocks of a 64-element group are lanes whose block index differs
+        // in bits 0, 2 and 3 (bit 1 selects group A or B of the double step)
+        sum += __shfl_xor(sum, 1, 64);
+        sum += __shfl_xor(sum, 4, 64);
+        sum += __shfl_xor(sum, 8, 64);
+        const int blk = p0 >> 3;
+        if ((blk & 13) == 0) {
+            // stored as bf16 hi + lo (hi + lo = sum to ~16 bits) for a bf16 MFMA
+            const int64_t gi = t * (H / 64) + (blk >> 4) * 2 + ((blk >> 1) & 1);
+            const uint16_t hi = f32_to_bf16(sum);
+            uint16_t* xs = reinterpret_cast<uint16_t*>(xsum);
+            xs[gi] = hi;
+            xs[static_cast<int64_t>(T) * (H / 64) + gi] = f32_to_bf16(sum - bf16_to_f32(hi));
+        }
+    }
+}
+
+static void launch_int4(const FfnParams& P, int phases, hipStream_t s) {
+    const unsigned tiles_y = (P.T + 15) / 16;
+    if (phases & 1) {
+        if (P.xsum != nullptr && P.H == 2816) {   // two K halves of 11 double steps
+            const size_t smem = (4 * 16 * 22 + 3 * 4 * 64) * sizeof(float);
+            hipLaunchKernelGGL((gate_up_int4_fast_kernel<11>), dim3(P.E * (P.FF / 16), tiles_y), dim3(256), smem, s, P);
+        } else if (P.H % 256 == 0 && P.H <= 2816) {   // two K halves of <= 11 double steps, <= 22 groups each
+            const int ngw = P.H / 128;
+            const size_t smem = (4 * 16 * ngw + 3 * 4 * 64) * sizeof(float);
+            hipLaunchKernelGGL((gate_up_int4_kernel<2, 11, 6>), dim3(P.E * (P.FF / 16), tiles_y), dim3(256), smem, s, P);
+        } else {
+            const int ngw = P.H / 64;
+            const size_t smem = (2 * 16 * ngw + 1 * 4 * 64) * sizeof(float);
+            hipLaunchKernelGGL((gate_up_int4_kernel<1, 4, 0>), dim3(P.E * (P.FF / 16), tiles_y), dim3(128), smem, s, P);
+        }
+    }
+    if (phases & 2) {
+        const size_t smem = 4 * 16 * (P.FF / 64) * sizeof(float);
+        if (P.FF <= 704)   // <= 5 double steps and a tail, <= 11 groups
+            hipLaunchKernelGGL((down_int4_kernel<5, 3>), dim3(P.E * (P.H / 64), tiles_y), dim3(256), smem, s, P);
+        else
+            hipLaunchKernelGGL((down_int4_kernel<4, 0>), dim3(P.E * (P.H / 64), tiles_y), dim3(256), smem, s, P);
+    }
+}
+
 // ------------------------------------------------------------------ host --
 FfnWorkspace ffn_workspace(int T, int k, int H, int FF) {
     auto up = [](size_t v) { return (v + 255) / 256 * 256; };
     FfnWorkspace w;
     w.xq_off = 0;
-    w.h_off = up(static_cast<size_t>(T) * H * 2);
+    w.xsum_off = up(static_cast<size_t>(T) * H * 2);
+    w.h_off = w.xsum_off + up(static_cast<size_t>(T) * (H / 64) * 4);
     w.bytes = w.h_off + up(static_cast<size_t>(T) * k * FF * 2);
     return w;
 }
 
 template <int FMT, int KSPLIT>
-static void launch_gate_up_stream(const FfnParams& P, hipStream_t s) {
+static void launch_gate_up_generic(const FfnParams& P, hipStream_t s) {
     constexpr int KSTEP = Geo<FMT>::KSTEP;
     const int spw = P.H / KSTEP / KSPLIT;
     size_t smem = (KSPLIT - 1) * 8 * 64 * sizeof(float);
     if (FMT == W_INT4) smem += static_cast<size_t>(KSPLIT) * 2 * spw * 16 * sizeof(float);
     const dim3 grid(P.E * (P.FF / 16)), block(64 * KSPLIT);
-    hipLaunchKernelGGL((gate_up_stream_kernel<FMT, KSPLIT, 4>), grid, block, smem, s, P);
+    hipLaunchKernelGGL((gate_up_generic_kernel<FMT, KSPLIT, 4>), grid, block, smem, s, P);
+}
+
+// fast-path shapes: (steps per wave, waves splitting K) with steps * waves = the step count
+template <int FMT, int NG, int KSPLIT>
+static void launch_gate_up_fast(const FfnParams& P, hipStream_t s) {
+    size_t smem = (KSPLIT - 1) * 8 * 64 * sizeof(float);
+    if (FMT == W_INT4) smem += static_cast<size_t>(KSPLIT) * 32 * NG * sizeof(float);
+    hipLaunchKernelGGL((gate_up_fast_kernel<FMT, NG, KSPLIT>), dim3(P.E * (P.FF / 16), (P.T + 15) / 16), dim3(64 * KSPLIT),
+                       smem, s, P);
+}
+
+template <int FMT, int NG, int KS>
+static void launch_down_fast(const FfnParams& P, hipStream_t s) {
+    size_t smem = (KS > 1 ? 3 * 4 * 64 * sizeof(float) : 0);
+    if (FMT == W_INT4) smem += 4 * 16 * NG * sizeof(float);
+    hipLaunchKernelGGL((down_fast_kernel<FMT, NG, KS>), dim3(P.E * (P.H / (16 * (4 / KS))), (P.T + 15) / 16), dim3(256),
+                       smem, s, P);
+}
+
+template <int FMT>
+static bool try_fast(const FfnParams& P, int phases, hipStream_t s) {
+    constexpr int KSTEP = Geo<FMT>::KSTEP;
+    const int n1 = P.H / KSTEP, n2 = P.FF / KSTEP;
+    const bool ok1 = !(phases & 1) || (FMT == W_BF16 ? n1 == 88 : n1 == 44);
+    const bool ok2 = !(phases & 2) || (FMT == W_BF16 ? n2 == 22 : n2 == 11);
+    if (!ok1 || !ok2 || P.T > 64) return false;
+    if (phases & 1) {
+        if (FMT == W_BF16) launch_gate_up_fast<FMT, 11, 8>(P, s);
+        else launch_gate_up_fast<FMT, 11, 4>(P, s);
+    }
+    if (phases & 2) {
+        if (FMT == W_BF16) launch_down_fast<FMT, 11, 2>(P, s);
+        else launch_down_fast<FMT, 11, 1>(P, s);
+    }
+    return true;
 }
 
 template <int FMT>
 static void launch_phases(const FfnParams& P, int phases, hipStream_t s) {
     constexpr int KSTEP = Geo<FMT>::KSTEP;
+    if (try_fast<FMT>(P, phases, s)) return;
     if (phases & 1) {
         const int nsteps = P.H / KSTEP;
         if (nsteps % 4 == 0)
-            launch_gate_up_stream<FMT, 4>(P, s);
+            launch_gate_up_generic<FMT, 4>(P, s);
         else if (nsteps % 2 == 0)
-            launch_gate_up_stream<FMT, 2>(P, s);
+            launch_gate_up_generic<FMT, 2>(P, s);
         else
-            launch_gate_up_stream<FMT, 1>(P, s);
+            launch_gate_up_generic<FMT, 1>(P, s);
     }
     if (phases & 2) {
         const int nsteps = P.FF / KSTEP;
         const size_t smem = FMT == W_INT4 ? 4 * static_cast<size_t>(nsteps) * 16 * sizeof(float) : 0;
-        hipLaunchKernelGGL((down_stream_kernel<FMT, 4>), dim3(P.E * (P.H / 64)), dim3(256), smem, s, P);
+        hipLaunchKernelGGL((down_generic_kernel<FMT, 4>), dim3(P.E * (P.H / 64)), dim3(256), smem, s, P);
     }
 }
 
@@ -370,19 +1091,20 @@ hipError_t launch_ffn(const FfnParams& P0, int phases, int path, hipStream_t s) 
         if (perm || P.x_dt == F32) {
             const int64_t nblk = static_cast<int64_t>(P.T) * P.H / 8;
             const dim3 grid(static_cast<uint32_t>((nblk + 255) / 256)), block(256);
+            if (perm && P.H == 2816) P.xsum = P.xsum_out;   // the int4 fast gate/up path reads group sums
             if (P.x_dt == F32 && perm)
-                hipLaunchKernelGGL((prep_x_kernel<F32, true>), grid, block, 0, s, P.x, nblk, P.xq_out);
+                hipLaunchKernelGGL((prep_x_int4_kernel<F32>), grid, block, 0, s, P.x, P.T, P.H, P.xq_out, P.xsum);
             else if (P.x_dt == F32)
                 hipLaunchKernelGGL((prep_x_kernel<F32, false>), grid, block, 0, s, P.x, nblk, P.xq_out);
             else
-                hipLaunchKernelGGL((prep_x_kernel<BF16, true>), grid, block, 0, s, P.x, nblk, P.xq_out);
+                hipLaunchKernelGGL((prep_x_int4_kernel<BF16>), grid, block, 0, s, P.x, P.T, P.H, P.xq_out, P.xsum);
             P.xq = P.xq_out;
         } else {
             P.xq = static_cast<const uint16_t*>(P.x);
         }
     }
     if (P.fmt == W_INT4)
-        launch_phases<W_INT4>(P, phases, s);
+        launch_int4(P, phases, s);
     else if (P.fmt == W_INT8)
         launch_phases<W_INT8>(P, phases, s);
     else

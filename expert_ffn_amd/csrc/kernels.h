@@ -27,6 +27,8 @@ struct FfnParams {
     int x_dt;
     const uint16_t* xq;       // [T, H] bf16 in the w13 operand order (may alias x)
     uint16_t* xq_out;         // where the preparation kernel writes xq (workspace)
+    float* xsum;              // group sums of xq per (token, 64-group) as bf16 hi [T, H/64] then lo; int4 fast gate/up
+    float* xsum_out;          // where the preparation kernel may write them (workspace)
     uint16_t* h;              // [T*k, FF] bf16 in the w2 operand order (workspace)
     void* out;                // [T*k, H] fp32 or bf16 (out_dt)
     int out_dt;
@@ -35,7 +37,7 @@ struct FfnParams {
 
 // Workspace layout of the expert FFN.
 struct FfnWorkspace {
-    size_t xq_off, h_off, bytes;
+    size_t xq_off, xsum_off, h_off, bytes;
 };
 FfnWorkspace ffn_workspace(int T, int k, int H, int FF);
 
