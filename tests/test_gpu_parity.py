@@ -135,6 +135,18 @@ def test_gemma_int4_decode(L):
              slot_of=slot_of)
 
 
+@pytest.mark.parametrize("T,zipf", [(1, None), (5, None), (16, 1.1), (37, None)])
+def test_gemma_int4_decode_sizes(L, T, zipf):
+    slot_of = synth.slot_table(1, 1, G["E"])[0]
+    run_case(L, f"gemma-int4-T{T}-zipf{zipf}", E=G["E"], k=G["k"], H=G["H"], FF=G["FF"], fmt="int4", T=T,
+             zipf=zipf, slot_of=slot_of, seed=2)
+
+
+def test_gemma_int4_decode_f32_x(L):
+    run_case(L, "gemma-int4-T8-f32x", E=G["E"], k=G["k"], H=G["H"], FF=G["FF"], fmt="int4", T=8,
+             x_kind="f32", y_dtype=torch.float32, act=1)
+
+
 @pytest.mark.parametrize("zipf", [None, 1.1])
 def test_gemma_int4_prefill(L, zipf):
     run_case(L, f"gemma-int4-T1024-zipf{zipf}", E=G["E"], k=G["k"], H=G["H"], FF=G["FF"], fmt="int4",
