@@ -31,6 +31,10 @@ sys.path.insert(0, ROOT)
 import synth  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
+# the kernel moe_ffn_gate_up launches for int4 at H = 2816, T <= 16 (the whole call)
+GATE_UP_KERNEL = "gate_up_int4_persist_kernel"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gate_up_int4_T16.json")
+CALIB_BYTES = 512 << 20
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 G = synth.GEMMA
 L_LAYERS = 30
@@ -138,13 +142,101 @@ def kernel_source_hash():
 def measured_traffic(kernel_hash):
     """HBM bytes per gate/up launch from the committed rocprofv3 counter runs,
     if they were taken on the current kernel sources (else None)."""
-    path = os.path.join(ROOT, "profiles", "traffic_gate_up_int4_T16.json")
     try:
-        with open(path) as f:
+        with open(TRAFFIC_FILE) as f:
             d = json.load(f)
     except (OSError, ValueError):
         return None
     return d.get("bytes_per_launch") if d.get("kernel_hash") == kernel_hash else None
+
+
+def calibration_copies(device, reps=3):
+    """Plain copies of known size for scaling the HBM byte counters: a
+    device-to-device copy (the runtime's copy kernel) and a torch elementwise
+    copy (neg), CALIB_BYTES read and CALIB_BYTES written each."""
+    import torch
+    src = torch.ones(CALIB_BYTES // 4, dtype=torch.float32, device=device)
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
+
+
+def _counter_rows(d):
+    """(kernel name, counter, value) of every dispatch in a rocprofv3 --pmc
+    run written with -f csv under directory d."""
+    import csv
+    import glob
+    rows = []
+    for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        with open(path, newline="") as f:
+            for r in csv.DictReader(f):
+                rows.append((r["Kernel_Name"], r["Counter_Name"], float(r["Counter_Value"])))
+    if not rows:
+        raise SystemExit(f"no counter_collection.csv under {d}")
+    return rows
+
+
+def summarize_pmc(fetch_dir, write_dir, commands):
+    """HBM bytes per gate/up launch from a FETCH_SIZE run and a WRITE_SIZE run
+    (KiB per dispatch), each scaled by the reading of the same counter for the
+    calibration copy of CALIB_BYTES; written to TRAFFIC_FILE."""
+    out = dict(kernel=GATE_UP_KERNEL, kernel_hash=kernel_source_hash(), calib_bytes=CALIB_BYTES,
+               commands=commands)
+    for key, d, cname in (("fetch", fetch_dir, "FETCH_SIZE"), ("write", write_dir, "WRITE_SIZE")):
+        rows = [(k, v) for k, c, v in _counter_rows(d) if c == cname]
+        gate = [v for k, v in rows if GATE_UP_KERNEL in k]
+        for calib_name in ("copyBuffer", "neg_kernel"):
+            cal = [v for k, v in rows if calib_name in k and v * 1024 > CALIB_BYTES / 4]
+            if cal:
+                break
+        if not gate or not cal:
+            raise SystemExit(f"{cname}: {len(gate)} gate/up and {len(cal)} calibration dispatches")
+        factor = CALIB_BYTES / (float(np.median(cal)) * 1024.0)
+        out[key] = dict(counter=cname, kib_per_launch=float(np.mean(gate)), launches=len(gate),
+                        calib_kernel=calib_name, calib_kib=float(np.median(cal)), scale=factor,
+                        bytes_per_launch=float(np.mean(gate)) * 1024.0 * factor)
+    out["bytes_per_launch"] = round(out["fetch"]["bytes_per_launch"] + out["write"]["bytes_per_launch"])
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out, indent=1))
+
+
+def summarize_trace(trace_dir, dest, command):
+    """Per-kernel count / average / median duration from a rocprofv3
+    --kernel-trace --stats run written with -f csv, as a markdown table."""
+    import csv
+    import glob
+    paths = glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True)
+    if not paths:
+        raise SystemExit(f"no kernel_trace.csv under {trace_dir}")
+    by = {}
+    for path in paths:
+        with open(path, newline="") as f:
+            for r in csv.DictReader(f):
+                name = r["Kernel_Name"].split("(")[0].replace("void ", "")
+                key = (name, r.get("Grid_Size_Y") or r.get("Grid_Size", ""))
+                by.setdefault(key, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    tot = sum(sum(v) for v in by.values())
+    lines = ["# rocprofv3 kernel trace summary", "", "Command (from the repository root):", "",
+             "```", command, "```", "",
+             "| kernel | grid y | launches | avg us | median us | min us | max us | share |",
+             "|---|---|---|---|---|---|---|---|"]
+    for (name, grid), v in sorted(by.items(), key=lambda kv: -sum(kv[1])):
+        a = np.array(v)
+        lines.append(f"| `{name[:70]}` | {grid} | {len(a)} | {a.mean():.2f} | {np.median(a):.2f} | "
+                     f"{a.min():.2f} | {a.max():.2f} | {100 * a.sum() / tot:.1f} % |")
+    stats = glob.glob(os.path.join(trace_dir, "**", "*kernel_stats.csv"), recursive=True)
+    if stats:
+        lines += ["", "rocprofv3 --stats (kernel_stats.csv):", "", "```"]
+        with open(stats[0]) as f:
+            lines += [l.rstrip("\n") for l in f]
+        lines += ["```"]
+    with open(dest, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines[:40]))
 
 
 def cpu_baseline(seed, T, budget_s=20.0):
@@ -192,7 +284,20 @@ def main():
     ap.add_argument("--prefill-steps", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run the plain copies that scale the HBM byte counters")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write the gate/up traffic file from two rocprofv3 --pmc runs (no GPU)")
+    ap.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_DIR", "DEST"),
+                    help="write a kernel-trace summary from a rocprofv3 run (no GPU)")
+    ap.add_argument("--command", default="", help="the profiled command, recorded in summaries")
     args = ap.parse_args()
+    if args.summarize_pmc:
+        summarize_pmc(*args.summarize_pmc, commands=args.command)
+        return
+    if args.summarize_trace:
+        summarize_trace(*args.summarize_trace, command=args.command)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(see DESIGN.md for how the path would shard); run with --gpus 1", file=sys.stderr)
@@ -212,6 +317,8 @@ def main():
     pool, sb, slots = build_stack(lib, args.seed, L_LAYERS, E, H, FF, fmt, dev)
     log(f"  pool {pool.numel() / 2**30:.2f} GiB, slot {sb} B, built in {time.time() - t0:.1f} s")
 
+    if args.calib_copy:
+        calibration_copies(dev)
     stream = torch.cuda.Stream()
     logits, xs = layer_inputs(args.seed, L_LAYERS, T, E, H, dev)
     with torch.cuda.stream(stream):
@@ -263,7 +370,7 @@ def main():
     traffic = measured_traffic(khash)
     roofline = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                     frac=round(achieved / HBM_PEAK_GBS, 4), traffic=traffic,
-                    kernel="gate_up_stream_kernel<int4> (moe_ffn_gate_up)",
+                    kernel=GATE_UP_KERNEL + " (moe_ffn_gate_up)",
                     avg_launch_us=round(float(gu.mean()) * 1e3, 2),
                     bytes_per_launch=round(float(gu_bytes.mean())))
 
