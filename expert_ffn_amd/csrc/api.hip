@@ -177,6 +177,7 @@ static moe_status ffn_entry(const char* fn, int phases, const void* pool, uint64
     P.xsum = nullptr;
     P.xsum_out = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + wl.xsum_off);
     P.h = reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(ws) + wl.h_off);
+    P.hsum = reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(ws) + wl.hsum_off);
     P.out = out_routes;
     P.out_dt = out_dtype;
     P.o13 = off[0]; P.os13 = off[1]; P.o2 = off[2]; P.os2 = off[3];

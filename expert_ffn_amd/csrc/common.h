@@ -62,4 +62,25 @@ __device__ __forceinline__ float act_fn(int act, float g) {
     return g * __frcp_rn(1.0f + __expf(z));
 }
 
+// slot j of an int4 operand dword holds element perm8(j): 0,4,1,5,2,6,3,7
+__device__ __forceinline__ int perm8(int j) { return (j >> 1) | ((j & 1) << 2); }
+
+// int4 codes -> bf16 (128 + u): (d >> 4j) & 0x000F000F | 0x43004300.  The
+// constants pass through empty asm statements so that they stay in registers:
+// a literal cannot be a VOP3 operand here, and with one the compiler splits
+// each dword into v_and + v_or.  With the mask in an SGPR and the magic in a
+// VGPR it emits one v_and_or_b32 per dword and tracks the VALU -> MFMA operand
+// hazards itself (it does not for VGPRs written by inline asm instructions).
+__device__ __forceinline__ u32x4 deq_int4(uint32_t d) {
+    uint32_t M = 0x000F000Fu, C = 0x43004300u;
+    asm("" : "+s"(M));
+    asm("" : "+v"(C));
+    u32x4 r;
+    r[0] = (d & M) | C;
+    r[1] = ((d >> 4) & M) | C;
+    r[2] = ((d >> 8) & M) | C;
+    r[3] = ((d >> 12) & M) | C;
+    return r;
+}
+
 }  // namespace moe

@@ -32,9 +32,6 @@
 
 namespace moe {
 
-// slot j of an int4 operand dword holds element perm8(j): 0,4,1,5,2,6,3,7
-__device__ __forceinline__ int perm8(int j) { return (j >> 1) | ((j & 1) << 2); }
-
 template <int FMT> struct Geo;
 template <> struct Geo<W_INT4> { static constexpr int KSTEP = 64, MF = 2; using A = u32x2; };
 template <> struct Geo<W_INT8> { static constexpr int KSTEP = 64, MF = 2; using A = u32x4; };
@@ -51,24 +48,6 @@ template <int FMT> __device__ __forceinline__ int a_off(int s, int q) {
 // element offset of lane group q's B fragment of step s inside an activation row
 template <int FMT> __device__ __forceinline__ int b_off(int s, int q) {
     return FMT == W_BF16 ? s * 32 + q * 8 : s * 64 + q * 16;
-}
-
-// int4 codes -> bf16 (128 + u): (d >> 4j) & 0x000F000F | 0x43004300.  The
-// constants pass through empty asm statements so that they stay in registers:
-// a literal cannot be a VOP3 operand here, and with one the compiler splits
-// each dword into v_and + v_or.  With the mask in an SGPR and the magic in a
-// VGPR it emits one v_and_or_b32 per dword and tracks the VALU -> MFMA operand
-// hazards itself (it does not for VGPRs written by inline asm instructions).
-__device__ __forceinline__ u32x4 deq_int4(uint32_t d) {
-    uint32_t M = 0x000F000Fu, C = 0x43004300u;
-    asm("" : "+s"(M));
-    asm("" : "+v"(C));
-    u32x4 r;
-    r[0] = (d & M) | C;
-    r[1] = ((d >> 4) & M) | C;
-    r[2] = ((d >> 8) & M) | C;
-    r[3] = ((d >> 12) & M) | C;
-    return r;
 }
 
 __device__ __forceinline__ u32x4 deq_int8(uint32_t d0, uint32_t d1) {
@@ -1304,9 +1283,12 @@ FfnWorkspace ffn_workspace(int T, int k, int H, int FF) {
     auto up = [](size_t v) { return (v + 255) / 256 * 256; };
     FfnWorkspace w;
     w.xq_off = 0;
+    // group sums: bf16 hi + lo per (row, 64-group), rows padded to 16 groups
+    const size_t gx = static_cast<size_t>((H / 64 + 15) & ~15), gh = static_cast<size_t>((FF / 64 + 15) & ~15);
     w.xsum_off = up(static_cast<size_t>(T) * H * 2);
-    w.h_off = w.xsum_off + up(static_cast<size_t>(T) * (H / 64) * 4);
-    w.bytes = w.h_off + up(static_cast<size_t>(T) * k * FF * 2);
+    w.h_off = w.xsum_off + up(static_cast<size_t>(T) * gx * 4);
+    w.hsum_off = w.h_off + up(static_cast<size_t>(T) * k * FF * 2);
+    w.bytes = w.hsum_off + up(static_cast<size_t>(T) * k * gh * 4);
     return w;
 }
 
@@ -1377,6 +1359,9 @@ static void launch_phases(const FfnParams& P, int phases, hipStream_t s) {
 
 hipError_t launch_ffn(const FfnParams& P0, int phases, int path, hipStream_t s) {
     FfnParams P = P0;
+    // int4, large token groups: LDS-staged grouped GEMM (both halves, so that
+    // split calls with the same T agree on the layout of h)
+    if (int4_gemm_eligible(P) && (path == 2 || (path == 0 && P.T >= 256))) return launch_int4_gemm(P, phases, s);
     if ((phases & 1) && path != 2 && try_gate_up_persist(P, s)) {
         P.xq = nullptr;   // tells launch_int4 the first half is done
         if (phases == 1) return hipGetLastError();

@@ -1,0 +1,452 @@
+// int4 expert FFN for large token groups (prefill chunks): per expert, the
+// routes of the expert form the rows of a grouped GEMM against its packed
+// weights (prain README, "Expert formats": w13 = gate and up stacked, w2 down;
+// int4 with a bf16 scale per 64-element group, dequantised in the kernel).
+//
+// MFMA v_mfma_f32_32x32x16_bf16, operands:
+//   A = 32 routes x 16 K of bf16 activations, staged through LDS;
+//   B = 16 K x 32 weight rows, expanded from int4 in registers;
+//   D = 32 routes x 32 weight rows, fp32.  Lane l holds D column (l & 31) and
+//       rows 8 (v / 4) + 4 (l >> 5) + (v & 3) of its 16 values v.
+// Lane l holds A row / B column (l & 31) and the K slots 8 (l >> 5) + j.
+// A lane's 16-byte weight load covers the 32 codes 32 h + 0..31 of one
+// 64-group of its row (h = l >> 5): dword s feeds K step s, and its expansion
+// (d >> 4i) & 0x000F000F | 0x43004300 puts code 8 s + perm8(j) in slot j.
+// The activations are therefore stored in "M32 operand order": inside each
+// 64-group, position 16 s + 8 h + j holds element 32 h + 8 s + perm8(j), so an
+// A fragment is one 16-byte read.
+//
+// The expanded codes are 128 + (q + 8): each group's fp32 partial sum is
+// scaled by the group's bf16 scale, and the offset is removed once per tile
+// by an MFMA of the row scales with the activations' group sums (bf16 hi + lo),
+// -136 * sum_g s[n][g] * X[m][g].
+//
+// Work items are (expert, 128-route tile, N tile); one workgroup of 8 waves
+// per CU walks the items.  Wave (mh, nq): routes 64 mh .. 64 mh + 63 of the
+// tile (two 32-route blocks) times 64 weight rows (two 32-row blocks).  The K
+// loop runs over chunks of two 64-groups: the activations of a chunk are
+// loaded into registers one chunk ahead and written to one of two LDS
+// buffers; each wave keeps the weights of the next 2*DC groups in flight in
+// registers.
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+
+__device__ __forceinline__ f32x16 mfma32(const u32x4& a, const u32x4& b, const f32x16& c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                    0, 0, 0);
+}
+
+// position of element f (0..63) of a 64-group in the M32 operand order
+__host__ __device__ __forceinline__ int m32_pos(int f) {
+    const int h = f >> 5, s = (f >> 3) & 3, e = f & 7;
+    return 16 * s + 8 * h + (((e & 3) << 1) | (e >> 2));   // slot j with perm8(j) = e
+}
+
+constexpr int GM_ROWS = 128;   // routes per tile
+constexpr int GM_XBUF = 32768; // one LDS stage: [2 groups][4 K steps][4 route blocks] x 1 KB
+
+// ---------------------------------------------------------------- prep ----
+// x [T, H] (fp32 or bf16) -> xq [T, H] bf16 in M32 operand order, and the
+// per-(token, 64-group) sums of the bf16 values as bf16 hi + lo:
+// xs [0][T][GP] hi, xs [1][T][GP] lo, GP = H/64 rounded up to 16, padding 0.
+template <int XT>
+__global__ __launch_bounds__(256) void prep_x_m32_kernel(const void* __restrict__ x, int T, int H,
+                                                         uint16_t* __restrict__ xq, uint16_t* __restrict__ xs) {
+    const int nb = H / 8;   // a multiple of 8: the 8 threads of a group are lanes 8i..8i+7
+    const int64_t b = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    if (b >= static_cast<int64_t>(T) * nb) return;
+    const int t = static_cast<int>(b / nb), p0 = static_cast<int>(b - static_cast<int64_t>(t) * nb) * 8;
+    const int g = p0 >> 6, s = (p0 >> 4) & 3, h = (p0 >> 3) & 1;
+    const int k0 = 64 * g + 32 * h + 8 * s;
+    float v[8];
+    if (XT == F32) {
+        const f32x4* src = reinterpret_cast<const f32x4*>(static_cast<const float*>(x) + static_cast<int64_t>(t) * H + k0);
+        const f32x4 a = src[0], c = src[1];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            v[j] = a[j];
+            v[4 + j] = c[j];
+        }
+    } else {
+        const u32x4 a = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(x) + static_cast<int64_t>(t) * H + k0);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            v[2 * j] = __uint_as_float(a[j] << 16);
+            v[2 * j + 1] = __uint_as_float(a[j] & 0xFFFF0000u);
+        }
+    }
+    u32x4 o;
+    float sum = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const uint16_t lo = f32_to_bf16(v[perm8(2 * j)]), hi = f32_to_bf16(v[perm8(2 * j + 1)]);
+        o[j] = static_cast<uint32_t>(lo) | (static_cast<uint32_t>(hi) << 16);
+        sum += bf16_to_f32(lo) + bf16_to_f32(hi);
+    }
+    *reinterpret_cast<u32x4*>(xq + static_cast<int64_t>(t) * H + p0) = o;
+    sum += __shfl_xor(sum, 1, 64);
+    sum += __shfl_xor(sum, 2, 64);
+    sum += __shfl_xor(sum, 4, 64);
+    if ((p0 & 63) == 0) {
+        const int G = H / 64, GP = (G + 15) & ~15;
+        uint16_t* rh = xs + static_cast<int64_t>(t) * GP;
+        uint16_t* rl = xs + (static_cast<int64_t>(T) + t) * GP;
+        const uint16_t shi = f32_to_bf16(sum);
+        rh[g] = shi;
+        rl[g] = f32_to_bf16(sum - bf16_to_f32(shi));
+        if (g == G - 1)
+            for (int i = G; i < GP; ++i) rh[i] = rl[i] = 0;
+    }
+}
+
+// ---------------------------------------------------------------- GEMM ----
+// MODE 0: gate/up.  K = H.  N tile = 128 gate rows + the matching 128 up rows;
+//         wave nq owns gate rows n0 + 32 nq + c and up rows FF + n0 + 32 nq + c.
+//         Epilogue: h = act(gate) * up as bf16 in M32 operand order over FF,
+//         and the group sums of h (bf16 hi + lo) for the second half.
+// MODE 1: down.  K = FF.  N tile = 256 rows of w2; wave nq owns rows
+//         n0 + 64 nq + 32 nb + c.  Epilogue: the route rows of out (fp32/bf16).
+template <int MODE>
+struct GemmShape {
+    int K, G, GP, NC, NT, nrows, gp_a;
+};
+
+template <int MODE>
+__device__ __forceinline__ GemmShape<MODE> gemm_shape(const FfnParams& P) {
+    GemmShape<MODE> S;
+    S.K = MODE == 0 ? P.H : P.FF;
+    S.G = S.K / 64;
+    S.GP = (S.G + 15) & ~15;
+    S.NC = (S.G + 1) / 2;
+    S.NT = MODE == 0 ? (P.FF + 127) / 128 : (P.H + 255) / 256;
+    S.nrows = MODE == 0 ? 2 * P.FF : P.H;   // rows of the weight matrix
+    return S;
+}
+
+__host__ __device__ inline size_t gemm_lds_bytes(int E, int G) {
+    return 2 * GM_XBUF + static_cast<size_t>(256) * G * 2 + 16 + static_cast<size_t>(E + 1) * 4;
+}
+
+template <int MODE, int DC>
+__global__ __launch_bounds__(512) void ffn_int4_gemm_kernel(FfnParams P) {
+    constexpr int D = 2 * DC;                       // weight groups in flight per wave
+    constexpr int U = (DC % 2 == 0) ? DC : 2 * DC;  // chunks per unrolled body: multiple of DC and of 2
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    const GemmShape<MODE> S = gemm_shape<MODE>(P);
+    const int E = P.E, G = S.G, GP = S.GP, NC = S.NC, NT = S.NT;
+    uint8_t* xbuf = lds;                                                   // [2][GM_XBUF]
+    uint16_t* ssc = reinterpret_cast<uint16_t*>(lds + 2 * GM_XBUF);        // [256][G] bf16 scales of the tile
+    int* pre = reinterpret_cast<int*>(lds + 2 * GM_XBUF + ((256 * G * 2 + 15) & ~15));   // [E+1]
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, c32 = lane & 31, hh = lane >> 5;
+    const int mh = wave >> 2, nq = wave & 3;
+
+    // route tiles per expert -> prefix sums (wave 0)
+    if (wave == 0) {
+        int run = 0;
+        for (int e0 = 0; e0 < E; e0 += 64) {
+            const int e = e0 + lane;
+            const int cnt = e < E ? (P.offsets[e + 1] - P.offsets[e] + GM_ROWS - 1) / GM_ROWS : 0;
+            int incl = cnt;
+#pragma unroll
+            for (int d = 1; d < 64; d <<= 1) {
+                const int o = __shfl_up(incl, d, 64);
+                if (lane >= d) incl += o;
+            }
+            if (e < E) pre[e + 1] = run + incl;
+            run += __shfl(incl, 63, 64);
+        }
+        if (lane == 0) pre[0] = 0;
+    }
+    __syncthreads();
+    const int nitems = pre[E] * NT;
+
+    const uint64_t o_codes = MODE == 0 ? P.o13 : P.o2, o_scales = MODE == 0 ? P.os13 : P.os2;
+    const int arow_stride = MODE == 0 ? P.H : P.FF;                 // elements per A row
+    const uint16_t* abase = MODE == 0 ? P.xq : P.h;
+    const uint16_t* asum = MODE == 0 ? reinterpret_cast<const uint16_t*>(P.xsum) : P.hsum;
+    const int asum_rows = MODE == 0 ? P.T : P.T * P.k;
+
+    for (int item = blockIdx.x; item < nitems; item += gridDim.x) {
+        const int mtg = item / NT, nt = item - mtg * NT;
+        int lo = 0, hi = E;   // largest e with pre[e] <= mtg
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (pre[mid] <= mtg) lo = mid; else hi = mid;
+        }
+        const int e = lo, mt = mtg - pre[e];
+        const int beg = P.offsets[e] + GM_ROWS * mt;
+        const int end = min(P.offsets[e + 1], beg + GM_ROWS);
+        const uint8_t* blob = P.pool + static_cast<uint64_t>(P.slot_of[e]) * P.slot_bytes;
+        const int n0 = MODE == 0 ? 128 * nt : 256 * nt;
+
+        // ---- scales of the tile's 256 rows -> LDS (16-byte copies; rows past the matrix read as 0)
+        {
+            const uint8_t* sblk = blob + o_scales;
+            const int half = MODE == 0 ? 128 * G * 2 : 256 * G * 2;   // bytes of one contiguous row run
+            const int nruns = MODE == 0 ? 2 : 1;
+            for (int i = tid; i < nruns * half / 16; i += 512) {
+                const int run = i / (half / 16), o = (i - run * (half / 16)) * 16;
+                const int r0 = MODE == 0 ? run * P.FF + n0 : n0;            // first matrix row of the run
+                const int64_t src = static_cast<int64_t>(r0) * G * 2 + o;
+                const bool ok = src + 16 <= static_cast<int64_t>(S.nrows) * G * 2;
+                const u32x4 v = ok ? *reinterpret_cast<const u32x4*>(sblk + src) : u32x4{0, 0, 0, 0};
+                *reinterpret_cast<u32x4*>(reinterpret_cast<uint8_t*>(ssc) + run * half + o) = v;
+            }
+        }
+
+        // ---- this wave's weight rows and activation rows
+        const bool nact = MODE == 0 ? (n0 + 32 * nq < P.FF) : (n0 + 64 * nq < P.H);
+        const bool mact = beg + 64 * mh < end;
+        int wrow[2], lrow[2];
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+            if (MODE == 0) {
+                const int n = min(n0 + 32 * nq + c32, P.FF - 1);
+                wrow[nb] = nb * P.FF + n;
+                lrow[nb] = 128 * nb + 32 * nq + c32;
+            } else {
+                wrow[nb] = min(n0 + 64 * nq + 32 * nb + c32, P.H - 1);
+                lrow[nb] = 64 * nq + 32 * nb + c32;
+            }
+        }
+        const uint8_t* wp0 = blob + o_codes + static_cast<int64_t>(wrow[0]) * (S.K / 2) + 16 * hh;
+        const uint8_t* wp1 = blob + o_codes + static_cast<int64_t>(wrow[1]) * (S.K / 2) + 16 * hh;
+        // staging: wave w copies (group gi, K step s) = (w >> 2, w & 3) of the 4 route blocks
+        const int sgi = wave >> 2, ss = wave & 3;
+        const uint16_t* arow[4];
+#pragma unroll
+        for (int mb4 = 0; mb4 < 4; ++mb4) {
+            const int p = min(beg + 32 * mb4 + c32, end - 1);
+            const int r = MODE == 0 ? P.sorted_route[p] / P.k : p;
+            arow[mb4] = abase + static_cast<int64_t>(r) * arow_stride + 16 * ss + 8 * hh;
+        }
+        auto load_stage = [&](int c, u32x4* xr) {
+            const int g = min(2 * c + sgi, G - 1);
+#pragma unroll
+            for (int mb4 = 0; mb4 < 4; ++mb4) xr[mb4] = *reinterpret_cast<const u32x4*>(arow[mb4] + 64 * g);
+        };
+        auto store_stage = [&](int buf, const u32x4* xr) {
+#pragma unroll
+            for (int mb4 = 0; mb4 < 4; ++mb4)
+                *reinterpret_cast<u32x4*>(xbuf + buf * GM_XBUF + ((sgi * 4 + ss) * 4 + mb4) * 1024 + lane * 16) = xr[mb4];
+        };
+
+        u32x4 xr[4];
+        load_stage(0, xr);
+        u32x4 wr[D][2];
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            const int g = min(d, G - 1);
+            wr[d][0] = *reinterpret_cast<const u32x4*>(wp0 + 32 * g);
+            wr[d][1] = *reinterpret_cast<const u32x4*>(wp1 + 32 * g);
+        }
+        store_stage(0, xr);
+        load_stage(1, xr);
+        __syncthreads();   // scales and stage 0 in LDS
+
+        // ---- bias of the expanded codes: acc = -136 * sum_g X[m][g] s[n][g]
+        f32x16 acc[2][2];
+        {
+            const f32x16 z = {};
+            f32x16 corr[2][2] = {{z, z}, {z, z}};
+            for (int t = 0; t < GP / 16; ++t) {
+                u32x4 bs[2];
+#pragma unroll
+                for (int nb = 0; nb < 2; ++nb) {
+                    const uint16_t* sr = ssc + lrow[nb] * G;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int g0 = 16 * t + 8 * hh + 2 * j;
+                        const uint32_t a = g0 < G ? sr[g0] : 0u, b = g0 + 1 < G ? sr[g0 + 1] : 0u;
+                        bs[nb][j] = a | (b << 16);
+                    }
+                }
+#pragma unroll
+                for (int mb = 0; mb < 2; ++mb) {
+                    const int p = min(beg + 64 * mh + 32 * mb + c32, end - 1);
+                    const int r = MODE == 0 ? P.sorted_route[p] / P.k : p;
+                    const uint16_t* sh = asum + static_cast<int64_t>(r) * GP + 16 * t + 8 * hh;
+                    const uint16_t* sl = sh + static_cast<int64_t>(asum_rows) * GP;
+                    u32x4 ah = *reinterpret_cast<const u32x4*>(sh), al = *reinterpret_cast<const u32x4*>(sl);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {   // groups past G: zero (the padding is not trusted)
+                        const int g0 = 16 * t + 8 * hh + 2 * j;
+                        const uint32_t m = g0 >= G ? 0u : (g0 + 1 >= G ? 0x0000FFFFu : 0xFFFFFFFFu);
+                        ah[j] &= m;
+                        al[j] &= m;
+                    }
+#pragma unroll
+                    for (int nb = 0; nb < 2; ++nb) {
+                        corr[mb][nb] = mfma32(ah, bs[nb], corr[mb][nb]);
+                        corr[mb][nb] = mfma32(al, bs[nb], corr[mb][nb]);
+                    }
+                }
+            }
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+                for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = corr[mb][nb] * -136.0f;
+        }
+
+        // ---- K loop: U chunks per unrolled body
+        const int ncu = (NC + U - 1) / U * U;
+        for (int c0 = 0; c0 < ncu; c0 += U) {
+#pragma unroll
+            for (int cu = 0; cu < U; ++cu) {
+                const int c = c0 + cu;
+                const uint8_t* xb = xbuf + (cu & 1) * GM_XBUF;
+#pragma unroll
+                for (int gi = 0; gi < 2; ++gi) {
+                    const int g = 2 * c + gi;
+                    constexpr int dummy = 0;
+                    (void)dummy;
+                    const int slot = (2 * cu + gi) % D;
+                    if (nact && mact && g < G) {
+                        f32x16 part[2][2];
+#pragma unroll
+                        for (int s = 0; s < 4; ++s) {
+                            u32x4 a[2];
+#pragma unroll
+                            for (int mb = 0; mb < 2; ++mb)
+                                a[mb] = *reinterpret_cast<const u32x4*>(xb + ((gi * 4 + s) * 4 + 2 * mh + mb) * 1024 + lane * 16);
+                            const u32x4 b0 = deq_int4(wr[slot][0][s]), b1 = deq_int4(wr[slot][1][s]);
+#pragma unroll
+                            for (int mb = 0; mb < 2; ++mb) {
+                                if (s == 0) {
+                                    const f32x16 z = {};
+                                    part[mb][0] = mfma32(a[mb], b0, z);
+                                    part[mb][1] = mfma32(a[mb], b1, z);
+                                } else {
+                                    part[mb][0] = mfma32(a[mb], b0, part[mb][0]);
+                                    part[mb][1] = mfma32(a[mb], b1, part[mb][1]);
+                                }
+                            }
+                        }
+                        const float sc0 = bf16_to_f32(ssc[lrow[0] * G + g]), sc1 = bf16_to_f32(ssc[lrow[1] * G + g]);
+#pragma unroll
+                        for (int mb = 0; mb < 2; ++mb) {
+                            acc[mb][0] += sc0 * part[mb][0];
+                            acc[mb][1] += sc1 * part[mb][1];
+                        }
+                    }
+                    // refill the slot with group g + D (past the end: the last group again)
+                    const int gn = min(g + D, G - 1);
+                    wr[slot][0] = *reinterpret_cast<const u32x4*>(wp0 + 32 * gn);
+                    wr[slot][1] = *reinterpret_cast<const u32x4*>(wp1 + 32 * gn);
+                }
+                // stage c + 1 (loaded during chunk c - 1) into the other buffer, load stage c + 2
+                store_stage((cu + 1) & 1, xr);
+                load_stage(min(c + 2, NC - 1), xr);
+                __syncthreads();
+            }
+        }
+
+        // ---- epilogue
+        if (MODE == 0) {
+            uint16_t* tile = reinterpret_cast<uint16_t*>(xbuf);   // [128 routes][128 columns] bf16, M32 order per group
+            if (nact && mact) {
+#pragma unroll
+                for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) {
+                        const int r = 64 * mh + 32 * mb + 8 * (v >> 2) + 4 * hh + (v & 3);
+                        const int col = 32 * nq + c32;
+                        const float hv = act_fn(P.act, acc[mb][0][v]) * acc[mb][1][v];
+                        tile[r * 128 + 64 * (col >> 6) + m32_pos(col & 63)] = f32_to_bf16(hv);
+                    }
+            }
+            __syncthreads();
+            const int ncol = min(128, P.FF - n0);   // 64 or 128
+            for (int i = tid; i < GM_ROWS * 16; i += 512) {
+                const int r = i >> 4, c8 = i & 15;
+                if (beg + r < end && 8 * c8 < ncol)
+                    *reinterpret_cast<u32x4*>(P.h + static_cast<int64_t>(beg + r) * P.FF + n0 + 8 * c8) =
+                        *reinterpret_cast<const u32x4*>(tile + r * 128 + 8 * c8);
+            }
+            {
+                // group sums of the stored h: 4 threads per route row (2 groups x 2 halves)
+                const int r = tid >> 2, gg = (tid >> 1) & 1, hf = tid & 1;
+                float sum = 0.0f;
+                const uint16_t* src = tile + r * 128 + 64 * gg + 32 * hf;
+#pragma unroll
+                for (int j = 0; j < 32; ++j) sum += bf16_to_f32(src[j]);
+                sum += __shfl_xor(sum, 1, 64);
+                if (hf == 0 && beg + r < end && 64 * gg < ncol) {
+                    const int G2 = P.FF / 64, GP2 = (G2 + 15) & ~15, R = P.T * P.k;
+                    const uint16_t shi = f32_to_bf16(sum);
+                    P.hsum[static_cast<int64_t>(beg + r) * GP2 + 2 * nt + gg] = shi;
+                    P.hsum[(static_cast<int64_t>(R) + beg + r) * GP2 + 2 * nt + gg] = f32_to_bf16(sum - bf16_to_f32(shi));
+                }
+            }
+        } else if (nact && mact) {
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int p = beg + 64 * mh + 32 * mb + 8 * (v >> 2) + 4 * hh + (v & 3);
+                    if (p < end) {
+#pragma unroll
+                        for (int nb = 0; nb < 2; ++nb) {
+                            const int64_t o = static_cast<int64_t>(p) * P.H + n0 + 64 * nq + 32 * nb + c32;
+                            if (P.out_dt == F32)
+                                static_cast<float*>(P.out)[o] = acc[mb][nb][v];
+                            else
+                                static_cast<uint16_t*>(P.out)[o] = f32_to_bf16(acc[mb][nb][v]);
+                        }
+                    }
+                }
+        }
+        __syncthreads();   // LDS is rewritten by the next item
+    }
+}
+
+// true if the int4 GEMM path takes this call
+bool int4_gemm_eligible(const FfnParams& P) {
+    // the tiles handle any H, FF that are multiples of 64 (ragged last N tile,
+    // odd group counts); E bounds the prefix table in LDS
+    return P.fmt == W_INT4 && P.H % 64 == 0 && P.FF % 64 == 0 && P.E <= 4096;
+}
+
+hipError_t launch_int4_gemm(const FfnParams& P0, int phases, hipStream_t s) {
+    FfnParams P = P0;
+    int dev = 0, cus = 0, maxlds = 0;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess) return err;
+    if ((err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return err;
+    if ((err = hipDeviceGetAttribute(&maxlds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev)) != hipSuccess) return err;
+    constexpr int DC = 2;
+    if (phases & 1) {
+        const int64_t nblk = static_cast<int64_t>(P.T) * P.H / 8;
+        P.xq = P.xq_out;
+        P.xsum = P.xsum_out;
+        if (P.x_dt == F32)
+            hipLaunchKernelGGL((prep_x_m32_kernel<F32>), dim3(static_cast<uint32_t>((nblk + 255) / 256)), dim3(256), 0, s,
+                               P.x, P.T, P.H, P.xq_out, reinterpret_cast<uint16_t*>(P.xsum_out));
+        else
+            hipLaunchKernelGGL((prep_x_m32_kernel<BF16>), dim3(static_cast<uint32_t>((nblk + 255) / 256)), dim3(256), 0, s,
+                               P.x, P.T, P.H, P.xq_out, reinterpret_cast<uint16_t*>(P.xsum_out));
+        const size_t lds = gemm_lds_bytes(P.E, P.H / 64);
+        if (static_cast<int>(lds) > maxlds) return hipErrorInvalidConfiguration;
+        static bool attr = false;
+        if (!attr)
+            attr = hipFuncSetAttribute(reinterpret_cast<const void*>(ffn_int4_gemm_kernel<0, DC>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, maxlds) == hipSuccess;
+        hipLaunchKernelGGL((ffn_int4_gemm_kernel<0, DC>), dim3(cus), dim3(512), lds, s, P);
+    }
+    if (phases & 2) {
+        const size_t lds = gemm_lds_bytes(P.E, P.FF / 64);
+        if (static_cast<int>(lds) > maxlds) return hipErrorInvalidConfiguration;
+        static bool attr = false;
+        if (!attr)
+            attr = hipFuncSetAttribute(reinterpret_cast<const void*>(ffn_int4_gemm_kernel<1, DC>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, maxlds) == hipSuccess;
+        hipLaunchKernelGGL((ffn_int4_gemm_kernel<1, DC>), dim3(cus), dim3(512), lds, s, P);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -30,6 +30,7 @@ struct FfnParams {
     float* xsum;              // group sums of xq per (token, 64-group) as bf16 hi [T, H/64] then lo; int4 fast gate/up
     float* xsum_out;          // where the preparation kernel may write them (workspace)
     uint16_t* h;              // [T*k, FF] bf16 in the w2 operand order (workspace)
+    uint16_t* hsum;           // group sums of h per (route, 64-group of FF), bf16 hi then lo (int4 GEMM path)
     void* out;                // [T*k, H] fp32 or bf16 (out_dt)
     int out_dt;
     uint64_t o13, os13, o2, os2;  // blob sub-block offsets
@@ -37,9 +38,13 @@ struct FfnParams {
 
 // Workspace layout of the expert FFN.
 struct FfnWorkspace {
-    size_t xq_off, xsum_off, h_off, bytes;
+    size_t xq_off, xsum_off, h_off, hsum_off, bytes;
 };
 FfnWorkspace ffn_workspace(int T, int k, int H, int FF);
+
+// int4 grouped-GEMM path (large token groups)
+bool int4_gemm_eligible(const FfnParams& p);
+hipError_t launch_int4_gemm(const FfnParams& p, int phases, hipStream_t s);
 
 // 0 = choose by token count, 1 = streaming kernels, 2 = LDS-tiled kernels
 hipError_t launch_ffn(const FfnParams& p, int phases /*1 gate_up, 2 down, 3 both*/, int path,

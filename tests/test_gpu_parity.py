@@ -153,6 +153,29 @@ def test_gemma_int4_prefill(L, zipf):
              T=1024, zipf=zipf, n_sample=12)
 
 
+# The int4 grouped-GEMM path (prefill-sized groups), forced on small shapes:
+# partial and multiple 128-route tiles, odd group counts, ragged N tiles.
+GEMM_CASES = [
+    dict(name="gemm-E8-H256-FF128-T100", E=8, k=2, H=256, FF=128, T=100),
+    dict(name="gemm-E2-H384-FF384-T300-zipf", E=2, k=1, H=384, FF=384, T=300, zipf=1.1),
+    dict(name="gemm-E4-H640-FF640-T150-silu-f32x", E=4, k=2, H=640, FF=640, T=150, act=1, x_kind="f32",
+         out_dtype=torch.bfloat16),
+    dict(name="gemm-E4-H192-FF192-T90", E=4, k=2, H=192, FF=192, T=90),
+    dict(name="gemm-E16-H128-FF256-T40-dropped", E=16, k=4, H=128, FF=256, T=40,
+         slot_of=np.array([0, -1, 2, 3, -1, 5, 6, 7, 8, 9, -1, 11, 12, 13, 14, 15], np.int32)),
+]
+
+
+@pytest.mark.parametrize("case", GEMM_CASES, ids=[c["name"] for c in GEMM_CASES])
+def test_int4_gemm_path(L, case):
+    c = dict(case)
+    run_case(L, c.pop("name"), fmt="int4", path=2, seed=3, **c)
+
+
+def test_gemma_int4_gemm_T256(L):
+    run_case(L, "gemma-int4-T256", E=G["E"], k=G["k"], H=G["H"], FF=G["FF"], fmt="int4", T=256, n_sample=12)
+
+
 # ------------------------------------------------------------ invariants ----
 def test_determinism_and_slot_shuffle(L):
     from expert_ffn_amd.layer import MoeLayer
