@@ -56,10 +56,11 @@ __device__ __forceinline__ u32x2 bload8(rsrc_t r, uint32_t off) {
 
 // Gated activations.  GELU (tanh form) uses 0.5 (1 + tanh(u)) = 1 / (1 + e^(-2u)):
 //   gelu(g) = g / (1 + exp(-2 sqrt(2/pi) (g + 0.044715 g^3)));  silu(g) = g / (1 + exp(-g)).
-// One exponential and one reciprocal; both limits are exact (exp overflow gives 0).
+// One exponential and one hardware reciprocal (v_rcp_f32, 1 ulp); both limits are
+// exact (exp overflow gives 0: the reciprocal of +inf is 0).
 __device__ __forceinline__ float act_fn(int act, float g) {
     const float z = act == ACT_SILU ? -g : -1.5957691216057308f * (g + 0.044715f * g * g * g);
-    return g * __frcp_rn(1.0f + __expf(z));
+    return g * __builtin_amdgcn_rcpf(1.0f + __expf(z));
 }
 
 // slot j of an int4 operand dword holds element perm8(j): 0,4,1,5,2,6,3,7

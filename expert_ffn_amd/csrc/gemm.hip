@@ -128,7 +128,7 @@ __device__ __forceinline__ GemmShape<MODE> gemm_shape(const FfnParams& P) {
 }
 
 __host__ __device__ inline size_t gemm_lds_bytes(int E, int G) {
-    return 2 * GM_XBUF + static_cast<size_t>(256) * G * 2 + 16 + static_cast<size_t>(E + 1) * 4;
+    return 2 * GM_XBUF + static_cast<size_t>(512) * G * 2 + 16 + static_cast<size_t>(E + 1) * 4;
 }
 
 template <int MODE, int DC>
@@ -139,17 +139,22 @@ __global__ __launch_bounds__(512) void ffn_int4_gemm_kernel(FfnParams P) {
     const GemmShape<MODE> S = gemm_shape<MODE>(P);
     const int E = P.E, G = S.G, GP = S.GP, NC = S.NC, NT = S.NT;
     uint8_t* xbuf = lds;                                                   // [2][GM_XBUF]
-    uint16_t* ssc = reinterpret_cast<uint16_t*>(lds + 2 * GM_XBUF);        // [256][G] bf16 scales of the tile
-    int* pre = reinterpret_cast<int*>(lds + 2 * GM_XBUF + ((256 * G * 2 + 15) & ~15));   // [E+1]
+    uint16_t* ssc = reinterpret_cast<uint16_t*>(lds + 2 * GM_XBUF);        // [512][G] bf16 scales of the tile
+    int* pre = reinterpret_cast<int*>(lds + 2 * GM_XBUF + ((512 * G * 2 + 15) & ~15));   // [E+1]
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, c32 = lane & 31, hh = lane >> 5;
     const int mh = wave >> 2, nq = wave & 3;
 
-    // route tiles per expert -> prefix sums (wave 0)
+    // Items per expert -> prefix sums (wave 0).  An expert with at most 64
+    // routes is one "wide" row tile: the two wave halves take different
+    // columns (an N tile twice as wide), so that both waves of each SIMD work.
+    // Larger groups take 128-route tiles, the halves splitting the routes.
+    const int NTW = MODE == 0 ? (P.FF + 255) / 256 : (P.H + 511) / 512;
     if (wave == 0) {
         int run = 0;
         for (int e0 = 0; e0 < E; e0 += 64) {
             const int e = e0 + lane;
-            const int cnt = e < E ? (P.offsets[e + 1] - P.offsets[e] + GM_ROWS - 1) / GM_ROWS : 0;
+            const int me = e < E ? P.offsets[e + 1] - P.offsets[e] : 0;
+            const int cnt = me == 0 ? 0 : (me <= 64 ? NTW : (me + GM_ROWS - 1) / GM_ROWS * NT);
             int incl = cnt;
 #pragma unroll
             for (int d = 1; d < 64; d <<= 1) {
@@ -162,7 +167,7 @@ __global__ __launch_bounds__(512) void ffn_int4_gemm_kernel(FfnParams P) {
         if (lane == 0) pre[0] = 0;
     }
     __syncthreads();
-    const int nitems = pre[E] * NT;
+    const int nitems = pre[E];
 
     const uint64_t o_codes = MODE == 0 ? P.o13 : P.o2, o_scales = MODE == 0 ? P.os13 : P.os2;
     const int arow_stride = MODE == 0 ? P.H : P.FF;                 // elements per A row
@@ -171,22 +176,26 @@ __global__ __launch_bounds__(512) void ffn_int4_gemm_kernel(FfnParams P) {
     const int asum_rows = MODE == 0 ? P.T : P.T * P.k;
 
     for (int item = blockIdx.x; item < nitems; item += gridDim.x) {
-        const int mtg = item / NT, nt = item - mtg * NT;
-        int lo = 0, hi = E;   // largest e with pre[e] <= mtg
+        int lo = 0, hi = E;   // largest e with pre[e] <= item
         while (hi - lo > 1) {
             const int mid = (lo + hi) >> 1;
-            if (pre[mid] <= mtg) lo = mid; else hi = mid;
+            if (pre[mid] <= item) lo = mid; else hi = mid;
         }
-        const int e = lo, mt = mtg - pre[e];
+        const int e = lo, li = item - pre[e];
+        const bool wide = P.offsets[e + 1] - P.offsets[e] <= 64;
+        const int nw = wide ? 2 : 1;                        // N tile width in narrow tiles
+        const int mt = wide ? 0 : li / NT, nt = wide ? li : li - (li / NT) * NT;
         const int beg = P.offsets[e] + GM_ROWS * mt;
         const int end = min(P.offsets[e + 1], beg + GM_ROWS);
         const uint8_t* blob = P.pool + static_cast<uint64_t>(P.slot_of[e]) * P.slot_bytes;
-        const int n0 = MODE == 0 ? 128 * nt : 256 * nt;
+        const int n0 = (MODE == 0 ? 128 : 256) * nw * nt;
+        const int nsub = wide ? wave : nq;                  // this wave's column block of the tile
+        const int mbase = wide ? 0 : 64 * mh;               // this wave's first route row of the tile
 
         // ---- scales of the tile's 256 rows -> LDS (16-byte copies; rows past the matrix read as 0)
         {
             const uint8_t* sblk = blob + o_scales;
-            const int half = MODE == 0 ? 128 * G * 2 : 256 * G * 2;   // bytes of one contiguous row run
+            const int half = (MODE == 0 ? 128 : 256) * nw * G * 2;    // bytes of one contiguous row run
             const int nruns = MODE == 0 ? 2 : 1;
             for (int i = tid; i < nruns * half / 16; i += 512) {
                 const int run = i / (half / 16), o = (i - run * (half / 16)) * 16;
@@ -199,35 +208,39 @@ __global__ __launch_bounds__(512) void ffn_int4_gemm_kernel(FfnParams P) {
         }
 
         // ---- this wave's weight rows and activation rows
-        const bool nact = MODE == 0 ? (n0 + 32 * nq < P.FF) : (n0 + 64 * nq < P.H);
-        const bool mact = beg + 64 * mh < end;
+        const bool nact = MODE == 0 ? (n0 + 32 * nsub < P.FF) : (n0 + 64 * nsub < P.H);
+        const bool mact = beg + mbase < end;
         int wrow[2], lrow[2];
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb) {
             if (MODE == 0) {
-                const int n = min(n0 + 32 * nq + c32, P.FF - 1);
+                const int n = min(n0 + 32 * nsub + c32, P.FF - 1);
                 wrow[nb] = nb * P.FF + n;
-                lrow[nb] = 128 * nb + 32 * nq + c32;
+                lrow[nb] = 128 * nw * nb + 32 * nsub + c32;
             } else {
-                wrow[nb] = min(n0 + 64 * nq + 32 * nb + c32, P.H - 1);
-                lrow[nb] = 64 * nq + 32 * nb + c32;
+                wrow[nb] = min(n0 + 64 * nsub + 32 * nb + c32, P.H - 1);
+                lrow[nb] = 64 * nsub + 32 * nb + c32;
             }
         }
         const uint8_t* wp0 = blob + o_codes + static_cast<int64_t>(wrow[0]) * (S.K / 2) + 16 * hh;
         const uint8_t* wp1 = blob + o_codes + static_cast<int64_t>(wrow[1]) * (S.K / 2) + 16 * hh;
-        // staging: wave w copies (group gi, K step s) = (w >> 2, w & 3) of the 4 route blocks
+        // staging: wave w copies (group gi, K step s) = (w >> 2, w & 3) of the 4
+        // route blocks; rows past the tile (and blocks 2, 3 of a wide tile) read
+        // zeros without a memory access
         const int sgi = wave >> 2, ss = wave & 3;
-        const uint16_t* arow[4];
+        const rsrc_t ares = make_rsrc(abase, static_cast<uint32_t>(asum_rows) * arow_stride * 2);
+        uint32_t aoff[4];
 #pragma unroll
         for (int mb4 = 0; mb4 < 4; ++mb4) {
-            const int p = min(beg + 32 * mb4 + c32, end - 1);
-            const int r = MODE == 0 ? P.sorted_route[p] / P.k : p;
-            arow[mb4] = abase + static_cast<int64_t>(r) * arow_stride + 16 * ss + 8 * hh;
+            const int p = beg + 32 * mb4 + c32;
+            const bool ok = p < end && (!wide || mb4 < 2);
+            const int r = ok ? (MODE == 0 ? P.sorted_route[p] / P.k : p) : 0;
+            aoff[mb4] = ok ? static_cast<uint32_t>((r * arow_stride + 16 * ss + 8 * hh) * 2) : NO_LANE;
         }
         auto load_stage = [&](int c, u32x4* xr) {
-            const int g = min(2 * c + sgi, G - 1);
+            const uint32_t g = static_cast<uint32_t>(min(2 * c + sgi, G - 1)) * 128;
 #pragma unroll
-            for (int mb4 = 0; mb4 < 4; ++mb4) xr[mb4] = *reinterpret_cast<const u32x4*>(arow[mb4] + 64 * g);
+            for (int mb4 = 0; mb4 < 4; ++mb4) xr[mb4] = bload16(ares, aoff[mb4] + g);
         };
         auto store_stage = [&](int buf, const u32x4* xr) {
 #pragma unroll
@@ -235,17 +248,20 @@ __global__ __launch_bounds__(512) void ffn_int4_gemm_kernel(FfnParams P) {
                 *reinterpret_cast<u32x4*>(xbuf + buf * GM_XBUF + ((sgi * 4 + ss) * 4 + mb4) * 1024 + lane * 16) = xr[mb4];
         };
 
+        // Load order = order of need, as in the K loop below (stage c + 1, then
+        // the last two groups of the ring), so that the in-order load counter
+        // gives the same waits on the first pass as on later ones.
         u32x4 xr[4];
         load_stage(0, xr);
         u32x4 wr[D][2];
-#pragma unroll
-        for (int d = 0; d < D; ++d) {
+        auto fill = [&](int d) {
             const int g = min(d, G - 1);
             wr[d][0] = *reinterpret_cast<const u32x4*>(wp0 + 32 * g);
             wr[d][1] = *reinterpret_cast<const u32x4*>(wp1 + 32 * g);
-        }
+        };
+#pragma unroll
+        for (int d = 0; d < D - 2; ++d) fill(d);
         store_stage(0, xr);
-        load_stage(1, xr);
         __syncthreads();   // scales and stage 0 in LDS
 
         // ---- bias of the expanded codes: acc = -136 * sum_g X[m][g] s[n][g]
@@ -267,7 +283,7 @@ __global__ __launch_bounds__(512) void ffn_int4_gemm_kernel(FfnParams P) {
                 }
 #pragma unroll
                 for (int mb = 0; mb < 2; ++mb) {
-                    const int p = min(beg + 64 * mh + 32 * mb + c32, end - 1);
+                    const int p = min(beg + mbase + 32 * mb + c32, end - 1);
                     const int r = MODE == 0 ? P.sorted_route[p] / P.k : p;
                     const uint16_t* sh = asum + static_cast<int64_t>(r) * GP + 16 * t + 8 * hh;
                     const uint16_t* sl = sh + static_cast<int64_t>(asum_rows) * GP;
@@ -291,6 +307,10 @@ __global__ __launch_bounds__(512) void ffn_int4_gemm_kernel(FfnParams P) {
 #pragma unroll
                 for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = corr[mb][nb] * -136.0f;
         }
+        load_stage(1, xr);
+        __builtin_amdgcn_sched_barrier(0);   // keep the issue order
+        fill(D - 2);
+        fill(D - 1);
 
         // ---- K loop: U chunks per unrolled body
         const int ncu = (NC + U - 1) / U * U;
@@ -299,34 +319,56 @@ __global__ __launch_bounds__(512) void ffn_int4_gemm_kernel(FfnParams P) {
             for (int cu = 0; cu < U; ++cu) {
                 const int c = c0 + cu;
                 const uint8_t* xb = xbuf + (cu & 1) * GM_XBUF;
+                // stage c + 1 (loaded one chunk ago) into the other buffer, whose
+                // readers finished at the last barrier; then start stage c + 2,
+                // ahead of this chunk's weight loads so that the in-order load
+                // counter never makes a wait cover weights needed later
+                store_stage((cu + 1) & 1, xr);
+                load_stage(min(c + 2, NC - 1), xr);
+                __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int gi = 0; gi < 2; ++gi) {
                     const int g = 2 * c + gi;
-                    constexpr int dummy = 0;
-                    (void)dummy;
                     const int slot = (2 * cu + gi) % D;
                     if (nact && mact && g < G) {
+                        // K steps software-pipelined: the next step's activation
+                        // fragments are read and its weights expanded while this
+                        // step's MFMAs run
+                        const int mblk = wide ? 0 : 2 * mh;
+                        const uint8_t* xa = xb + (gi * 16 + mblk) * 1024 + lane * 16;
+                        const float sc0 = bf16_to_f32(ssc[lrow[0] * G + g]), sc1 = bf16_to_f32(ssc[lrow[1] * G + g]);
                         f32x16 part[2][2];
+                        u32x4 a0 = *reinterpret_cast<const u32x4*>(xa);
+                        u32x4 a1 = *reinterpret_cast<const u32x4*>(xa + 1024);
+                        u32x4 b0 = deq_int4(wr[slot][0][0]), b1 = deq_int4(wr[slot][1][0]);
 #pragma unroll
                         for (int s = 0; s < 4; ++s) {
-                            u32x4 a[2];
-#pragma unroll
-                            for (int mb = 0; mb < 2; ++mb)
-                                a[mb] = *reinterpret_cast<const u32x4*>(xb + ((gi * 4 + s) * 4 + 2 * mh + mb) * 1024 + lane * 16);
-                            const u32x4 b0 = deq_int4(wr[slot][0][s]), b1 = deq_int4(wr[slot][1][s]);
-#pragma unroll
-                            for (int mb = 0; mb < 2; ++mb) {
-                                if (s == 0) {
-                                    const f32x16 z = {};
-                                    part[mb][0] = mfma32(a[mb], b0, z);
-                                    part[mb][1] = mfma32(a[mb], b1, z);
-                                } else {
-                                    part[mb][0] = mfma32(a[mb], b0, part[mb][0]);
-                                    part[mb][1] = mfma32(a[mb], b1, part[mb][1]);
-                                }
+                            u32x4 na0, na1, nb0, nb1;
+                            if (s < 3) {
+                                na0 = *reinterpret_cast<const u32x4*>(xa + (s + 1) * 4096);
+                                na1 = *reinterpret_cast<const u32x4*>(xa + (s + 1) * 4096 + 1024);
+                            }
+                            if (s == 0) {
+                                const f32x16 z = {};
+                                part[0][0] = mfma32(a0, b0, z);
+                                part[0][1] = mfma32(a0, b1, z);
+                                part[1][0] = mfma32(a1, b0, z);
+                                part[1][1] = mfma32(a1, b1, z);
+                            } else {
+                                part[0][0] = mfma32(a0, b0, part[0][0]);
+                                part[0][1] = mfma32(a0, b1, part[0][1]);
+                                part[1][0] = mfma32(a1, b0, part[1][0]);
+                                part[1][1] = mfma32(a1, b1, part[1][1]);
+                            }
+                            if (s < 3) {
+                                nb0 = deq_int4(wr[slot][0][s + 1]);
+                                nb1 = deq_int4(wr[slot][1][s + 1]);
+                                a0 = na0;
+                                a1 = na1;
+                                b0 = nb0;
+                                b1 = nb1;
                             }
                         }
-                        const float sc0 = bf16_to_f32(ssc[lrow[0] * G + g]), sc1 = bf16_to_f32(ssc[lrow[1] * G + g]);
 #pragma unroll
                         for (int mb = 0; mb < 2; ++mb) {
                             acc[mb][0] += sc0 * part[mb][0];
@@ -338,48 +380,48 @@ __global__ __launch_bounds__(512) void ffn_int4_gemm_kernel(FfnParams P) {
                     wr[slot][0] = *reinterpret_cast<const u32x4*>(wp0 + 32 * gn);
                     wr[slot][1] = *reinterpret_cast<const u32x4*>(wp1 + 32 * gn);
                 }
-                // stage c + 1 (loaded during chunk c - 1) into the other buffer, load stage c + 2
-                store_stage((cu + 1) & 1, xr);
-                load_stage(min(c + 2, NC - 1), xr);
                 __syncthreads();
             }
         }
 
         // ---- epilogue
         if (MODE == 0) {
-            uint16_t* tile = reinterpret_cast<uint16_t*>(xbuf);   // [128 routes][128 columns] bf16, M32 order per group
+            // [128 / nw routes][128 nw columns] bf16, M32 order inside each 64-group
+            uint16_t* tile = reinterpret_cast<uint16_t*>(xbuf);
+            const int tw = 128 * nw;
             if (nact && mact) {
 #pragma unroll
                 for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
                     for (int v = 0; v < 16; ++v) {
-                        const int r = 64 * mh + 32 * mb + 8 * (v >> 2) + 4 * hh + (v & 3);
-                        const int col = 32 * nq + c32;
+                        const int r = mbase + 32 * mb + 8 * (v >> 2) + 4 * hh + (v & 3);
+                        const int col = 32 * nsub + c32;
                         const float hv = act_fn(P.act, acc[mb][0][v]) * acc[mb][1][v];
-                        tile[r * 128 + 64 * (col >> 6) + m32_pos(col & 63)] = f32_to_bf16(hv);
+                        tile[r * tw + 64 * (col >> 6) + m32_pos(col & 63)] = f32_to_bf16(hv);
                     }
             }
             __syncthreads();
-            const int ncol = min(128, P.FF - n0);   // 64 or 128
+            const int ncol = min(tw, P.FF - n0);
             for (int i = tid; i < GM_ROWS * 16; i += 512) {
-                const int r = i >> 4, c8 = i & 15;
+                const int r = i / (16 * nw), c8 = i - r * (16 * nw);
                 if (beg + r < end && 8 * c8 < ncol)
                     *reinterpret_cast<u32x4*>(P.h + static_cast<int64_t>(beg + r) * P.FF + n0 + 8 * c8) =
-                        *reinterpret_cast<const u32x4*>(tile + r * 128 + 8 * c8);
+                        *reinterpret_cast<const u32x4*>(tile + r * tw + 8 * c8);
             }
             {
-                // group sums of the stored h: 4 threads per route row (2 groups x 2 halves)
-                const int r = tid >> 2, gg = (tid >> 1) & 1, hf = tid & 1;
+                // group sums of the stored h: 2 threads per (route row, 64-group)
+                const int pr = tid >> 1, hf = tid & 1, r = pr / (2 * nw), gg = pr - r * (2 * nw);
                 float sum = 0.0f;
-                const uint16_t* src = tile + r * 128 + 64 * gg + 32 * hf;
+                const uint16_t* src = tile + r * tw + 64 * gg + 32 * hf;
 #pragma unroll
                 for (int j = 0; j < 32; ++j) sum += bf16_to_f32(src[j]);
                 sum += __shfl_xor(sum, 1, 64);
                 if (hf == 0 && beg + r < end && 64 * gg < ncol) {
                     const int G2 = P.FF / 64, GP2 = (G2 + 15) & ~15, R = P.T * P.k;
                     const uint16_t shi = f32_to_bf16(sum);
-                    P.hsum[static_cast<int64_t>(beg + r) * GP2 + 2 * nt + gg] = shi;
-                    P.hsum[(static_cast<int64_t>(R) + beg + r) * GP2 + 2 * nt + gg] = f32_to_bf16(sum - bf16_to_f32(shi));
+                    const int gidx = n0 / 64 + gg;
+                    P.hsum[static_cast<int64_t>(beg + r) * GP2 + gidx] = shi;
+                    P.hsum[(static_cast<int64_t>(R) + beg + r) * GP2 + gidx] = f32_to_bf16(sum - bf16_to_f32(shi));
                 }
             }
         } else if (nact && mact) {
@@ -387,11 +429,11 @@ __global__ __launch_bounds__(512) void ffn_int4_gemm_kernel(FfnParams P) {
             for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {
-                    const int p = beg + 64 * mh + 32 * mb + 8 * (v >> 2) + 4 * hh + (v & 3);
+                    const int p = beg + mbase + 32 * mb + 8 * (v >> 2) + 4 * hh + (v & 3);
                     if (p < end) {
 #pragma unroll
                         for (int nb = 0; nb < 2; ++nb) {
-                            const int64_t o = static_cast<int64_t>(p) * P.H + n0 + 64 * nq + 32 * nb + c32;
+                            const int64_t o = static_cast<int64_t>(p) * P.H + n0 + 64 * nsub + 32 * nb + c32;
                             if (P.out_dt == F32)
                                 static_cast<float*>(P.out)[o] = acc[mb][nb][v];
                             else
