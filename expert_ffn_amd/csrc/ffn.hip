@@ -1153,6 +1153,185 @@ __global__ __launch_bounds__(1024) void gate_up_int4_persist_kernel(FfnParams P)
     }
 }
 
+// ------------------------------------------------ int4 gate/up, decode --
+// One workgroup of 4 waves per (expert, 16-row tile u of h): wave (t, part) =
+// (gate or up) x (half of K), so a wave holds the 11 weight fragments of its
+// rows in registers, all requested at once (16 bytes per lane each).  The
+// expert's routes are taken 4 at a time: their activations are converted into
+// LDS in the operand order with their 64-group sums (bf16 hi + lo), then every
+// wave runs its MFMAs against the same weight registers.  Experts without
+// routes leave at once; many small workgroups per CU keep enough loads in
+// flight to stream the weights at close to the HBM rate.
+constexpr int GUD_RT = 4;   // routes per route tile
+
+struct GudLds {             // offsets (bytes) into dynamic LDS
+    int xs, xsum, sc, red, tok, total;
+};
+__host__ __device__ inline GudLds gud_lds(int H) {
+    GudLds L;
+    const int G = H / 64, GS = (G + 39) & ~7, NGW = 2 * ((H / 128 + 1) / 2);
+    L.xs = 0;                                             // bf16 [RT][H + 8]
+    L.xsum = GUD_RT * (H + 8) * 2;                        // bf16 [2][RT][GS] hi, lo (zero past G)
+    L.sc = (L.xsum + 2 * GUD_RT * GS * 2 + 15) & ~15;     // float [4 waves][NGW][16]
+    L.red = L.sc + 4 * NGW * 16 * 4;                      // float [3][4][64]
+    L.tok = L.red + 3 * 4 * 64 * 4;                       // int [RT]
+    L.total = L.tok + GUD_RT * 4;
+    return L;
+}
+
+template <int NDT, int XT>
+__global__ __launch_bounds__(256) void gate_up_int4_dec_kernel(FfnParams P) {
+    constexpr int KS = 2;
+    constexpr int NDW = (NDT + KS - 1) / KS;   // double steps of one wave
+    constexpr int NGW = 2 * NDW;
+    static_assert(NGW <= 32, "the bias MFMA takes 32 groups");
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    const int ntile = P.FF >> 4;
+    const int e = blockIdx.x / ntile, u = blockIdx.x - e * ntile;
+    const int beg = P.offsets[e], end = P.offsets[e + 1];
+    if (beg >= end) return;
+    const int H = P.H, G = H / 64, GS = (G + 39) & ~7;
+    const GudLds L = gud_lds(H);
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r = lane & 15, q = lane >> 4;
+    uint16_t* xs = reinterpret_cast<uint16_t*>(lds + L.xs);
+    uint16_t* xsum = reinterpret_cast<uint16_t*>(lds + L.xsum);
+    float* s_sc = reinterpret_cast<float*>(lds + L.sc) + wave * (NGW * 16);
+    float* s_red = reinterpret_cast<float*>(lds + L.red);
+    int* toks = reinterpret_cast<int*>(lds + L.tok);
+    const int t = wave >> 1, part = wave & 1;
+    const int ds0 = part * NDT / KS, nds = (part + 1) * NDT / KS - ds0;
+    const int ng = 2 * nds, k0 = 128 * ds0;
+
+    // weights first: the scale dwords of this lane's row (groups 8q..8q+7 of the
+    // wave's range) and its 11 fragments
+    const uint8_t* blob = P.pool + static_cast<uint64_t>(P.slot_of[e]) * P.slot_bytes;
+    const int row = t * P.FF + int4_tile_base(u, P.FF) + (r & 8) + perm8(r & 7);
+    const uint32_t* srow = reinterpret_cast<const uint32_t*>(blob + P.os13) + (row * G + k0 / 64) / 2;
+    u32x4 sa = *reinterpret_cast<const u32x4*>(srow + 4 * (8 * q < ng ? q : 0));
+    const uint8_t* a_row = blob + P.o13 + row * (H / 2) + k0 / 2 + 16 * q;
+    u32x4 a[NDW];
+#pragma unroll
+    for (int i = 0; i < NDW; ++i) a[i] = *reinterpret_cast<const u32x4*>(a_row + 64 * min(i, nds - 1));
+
+    for (int i = tid; i < 2 * GUD_RT * GS; i += 256) xsum[i] = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        if (8 * q + 2 * j >= ng) sa[j] = 0u;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int g = 8 * q + 2 * j;
+        if (g < ng) {
+            s_sc[g * 16 + r] = __uint_as_float(sa[j] << 16);
+            s_sc[(g + 1) * 16 + r] = __uint_as_float(sa[j] & 0xFFFF0000u);
+        }
+    }
+
+    const int nb = H / 8;   // blocks of 8 per row, a multiple of 16
+    for (int rt = beg; rt < end; rt += GUD_RT) {
+        const int nr = min(GUD_RT, end - rt);
+        if (tid < GUD_RT) toks[tid] = P.sorted_route[rt + min(tid, nr - 1)] / P.k;
+        __syncthreads();   // toks; the previous tile's readers of xs, xsum and s_red are done
+        // activations of the nr tokens -> LDS (rows past nr keep stale values:
+        // their columns are never stored)
+        for (int i0 = tid; i0 < nr * nb; i0 += 512) {
+            float v[2][8];
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                const int i = min(i0 + 256 * hh, nr * nb - 1);
+                const int j = i / nb, kk = int4_pos_to_k((i - j * nb) * 8, H);
+                if (XT == F32) {
+                    const f32x4* src = reinterpret_cast<const f32x4*>(static_cast<const float*>(P.x) + static_cast<int64_t>(toks[j]) * H + kk);
+                    const f32x4 xa = src[0], xc = src[1];
+#pragma unroll
+                    for (int m = 0; m < 4; ++m) {
+                        v[hh][m] = xa[m];
+                        v[hh][4 + m] = xc[m];
+                    }
+                } else {
+                    const u32x4 xa = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(P.x) + static_cast<int64_t>(toks[j]) * H + kk);
+#pragma unroll
+                    for (int m = 0; m < 4; ++m) {
+                        v[hh][2 * m] = __uint_as_float(xa[m] << 16);
+                        v[hh][2 * m + 1] = __uint_as_float(xa[m] & 0xFFFF0000u);
+                    }
+                }
+            }
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                const int i = i0 + 256 * hh;
+                if (i < nr * nb) {   // nr * nb is a multiple of 16: whole 16-lane groups take this branch
+                    const int j = i / nb, p0 = (i - j * nb) * 8;
+                    u32x4 o;
+                    float sum = 0.0f;
+#pragma unroll
+                    for (int m = 0; m < 4; ++m) {
+                        const uint16_t lo = f32_to_bf16(v[hh][perm8(2 * m)]), hi = f32_to_bf16(v[hh][perm8(2 * m + 1)]);
+                        o[m] = static_cast<uint32_t>(lo) | (static_cast<uint32_t>(hi) << 16);
+                        sum += bf16_to_f32(lo) + bf16_to_f32(hi);
+                    }
+                    *reinterpret_cast<u32x4*>(xs + j * (H + 8) + p0) = o;
+                    // the 8 blocks of a 64-group: block indices differing in bits 0, 2, 3
+                    sum += __shfl_xor(sum, 1, 64);
+                    sum += __shfl_xor(sum, 4, 64);
+                    sum += __shfl_xor(sum, 8, 64);
+                    const int blk = p0 >> 3;
+                    if ((blk & 13) == 0) {
+                        const int gi = j * GS + (blk >> 4) * 2 + ((blk >> 1) & 1);
+                        const uint16_t shi = f32_to_bf16(sum);
+                        xsum[gi] = shi;
+                        xsum[GUD_RT * GS + gi] = f32_to_bf16(sum - bf16_to_f32(shi));
+                    }
+                }
+            }
+        }
+        __syncthreads();
+
+        // column r of the MFMA is token slot r % RT (slots past nr are discarded)
+        const int slot = r & (GUD_RT - 1);
+        const uint16_t* xrow = xs + slot * (H + 8) + k0 + 32 * q;
+        const uint32_t* shi = reinterpret_cast<const uint32_t*>(xsum + slot * GS + k0 / 64 + 8 * q);
+        const uint32_t* slo = reinterpret_cast<const uint32_t*>(xsum + GUD_RT * GS + slot * GS + k0 / 64 + 8 * q);
+        const u32x4 xhi = {shi[0], shi[1], shi[2], shi[3]};
+        const u32x4 xlo = {slo[0], slo[1], slo[2], slo[3]};
+        const f32x4 zero = {0, 0, 0, 0};
+        f32x4 corr = mfma16x16x32(sa, xhi, zero);
+        corr = mfma16x16x32(sa, xlo, corr);
+        f32x4 acc = corr * -136.0f;
+#pragma unroll
+        for (int i = 0; i < NDW; ++i) {
+            if (i < nds) {
+                const u32x4 vv = regroup(a[i]);
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const u32x4 b0 = *reinterpret_cast<const u32x4*>(xrow + 128 * i + 16 * h);
+                    const u32x4 b1 = *reinterpret_cast<const u32x4*>(xrow + 128 * i + 16 * h + 8);
+                    f32x4 tt = mfma16x16x32(deq_int4(vv[2 * h]), b0, zero);
+                    tt = mfma16x16x32(deq_int4(vv[2 * h + 1]), b1, tt);
+                    acc += *reinterpret_cast<const f32x4*>(s_sc + (2 * i + h) * 16 + 4 * q) * tt;
+                }
+            }
+        }
+        if (wave > 0) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) s_red[((wave - 1) * 4 + j) * 64 + lane] = acc[j];
+        }
+        __syncthreads();
+        if (wave == 0 && r < nr) {
+            // gate = this wave + wave 1 (other K half); up = waves 2 + 3
+            f32x4 g = acc, uu;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                g[j] += s_red[(0 * 4 + j) * 64 + lane];
+                uu[j] = s_red[(1 * 4 + j) * 64 + lane] + s_red[(2 * 4 + j) * 64 + lane];
+            }
+            const int p = rt + r;
+            const uint32_t h0 = pack_bf16x2(act_fn(P.act, g[0]) * uu[0], act_fn(P.act, g[1]) * uu[1]);
+            const uint32_t h1 = pack_bf16x2(act_fn(P.act, g[2]) * uu[2], act_fn(P.act, g[3]) * uu[3]);
+            *reinterpret_cast<u32x2*>(P.h + static_cast<int64_t>(p) * P.FF + 16 * u + 4 * q) = u32x2{h0, h1};
+        }
+    }
+}
+
 // x -> xq in the int4 operand order of K = H (one thread per 8 positions)
 template <int XT>
 __global__ __launch_bounds__(256) void prep_x_int4_kernel(const void* __restrict__ x, int T, int H,
@@ -1362,6 +1541,17 @@ hipError_t launch_ffn(const FfnParams& P0, int phases, int path, hipStream_t s) 
     // int4, large token groups: LDS-staged grouped GEMM (both halves, so that
     // split calls with the same T agree on the layout of h)
     if (int4_gemm_eligible(P) && (path == 2 || (path == 0 && P.T >= 256))) return launch_int4_gemm(P, phases, s);
+    if ((phases & 1) && path != 2 && P.fmt == W_INT4 && P.H == 2816 && P.FF % 16 == 0) {
+        const GudLds L = gud_lds(P.H);
+        if (P.x_dt == F32)
+            hipLaunchKernelGGL((gate_up_int4_dec_kernel<22, F32>), dim3(P.E * (P.FF / 16)), dim3(256), L.total, s, P);
+        else
+            hipLaunchKernelGGL((gate_up_int4_dec_kernel<22, BF16>), dim3(P.E * (P.FF / 16)), dim3(256), L.total, s, P);
+        P.xq = nullptr;   // tells launch_int4 the first half is done
+        if (phases == 1) return hipGetLastError();
+        launch_int4(P, 2, s);
+        return hipGetLastError();
+    }
     if ((phases & 1) && path != 2 && try_gate_up_persist(P, s)) {
         P.xq = nullptr;   // tells launch_int4 the first half is done
         if (phases == 1) return hipGetLastError();
