@@ -1154,15 +1154,18 @@ __global__ __launch_bounds__(1024) void gate_up_int4_persist_kernel(FfnParams P)
 }
 
 // ------------------------------------------------ int4 gate/up, decode --
-// One workgroup of 4 waves per (expert, 16-row tile u of h): wave (t, part) =
-// (gate or up) x (half of K), so a wave holds the 11 weight fragments of its
-// rows in registers, all requested at once (16 bytes per lane each).  The
-// expert's routes are taken 4 at a time: their activations are converted into
-// LDS in the operand order with their 64-group sums (bf16 hi + lo), then every
-// wave runs its MFMAs against the same weight registers.  Experts without
+// One workgroup of 4 waves per (expert, GUD_TPW 16-row tiles of h): wave
+// (t, part) = (gate or up) x (half of K), so a wave holds the 11 weight
+// fragments per tile of its rows in registers, all requested at once (16 bytes
+// per lane each).  The
+// expert's routes are taken 4 at a time: their activations, already in the
+// operand order (preparation kernel), and their 64-group sums (bf16 hi + lo)
+// are copied into LDS, then every wave runs its MFMAs against the same weight
+// registers.  Experts without
 // routes leave at once; many small workgroups per CU keep enough loads in
 // flight to stream the weights at close to the HBM rate.
 constexpr int GUD_RT = 4;   // routes per route tile
+constexpr int GUD_TPW = 1;  // 16-row tiles per workgroup
 
 struct GudLds {             // offsets (bytes) into dynamic LDS
     int xs, xsum, sc, red, tok, total;
@@ -1170,15 +1173,17 @@ struct GudLds {             // offsets (bytes) into dynamic LDS
 __host__ __device__ inline GudLds gud_lds(int H) {
     GudLds L;
     const int G = H / 64, GS = (G + 39) & ~7, NGW = 2 * ((H / 128 + 1) / 2);
-    L.xs = 0;                                             // bf16 [RT][H + 8]
-    L.xsum = GUD_RT * (H + 8) * 2;                        // bf16 [2][RT][GS] hi, lo (zero past G)
-    L.sc = (L.xsum + 2 * GUD_RT * GS * 2 + 15) & ~15;     // float [4 waves][NGW][16]
-    L.red = L.sc + 4 * NGW * 16 * 4;                      // float [3][4][64]
-    L.tok = L.red + 3 * 4 * 64 * 4;                       // int [RT]
+    L.xs = 0;                                             // bf16 [RT][H]
+    L.xsum = GUD_RT * H * 2;                              // bf16 [2][RT][GS] hi, lo (zero past G)
+    L.sc = (L.xsum + 2 * GUD_RT * GS * 2 + 15) & ~15;     // float [4 waves][TPW][NGW][16]
+    L.red = L.sc + 4 * GUD_TPW * NGW * 16 * 4;            // float [TPW][3][4][64]
+    L.tok = L.red + GUD_TPW * 3 * 4 * 64 * 4;             // int [RT]
     L.total = L.tok + GUD_RT * 4;
     return L;
 }
 
+// XT = BF16: x rows are copied as they are and put into the operand order in
+// LDS; XT = F32: the preparation kernel has converted them (P.xq, P.xsum).
 template <int NDT, int XT>
 __global__ __launch_bounds__(256) void gate_up_int4_dec_kernel(FfnParams P) {
     constexpr int KS = 2;
@@ -1186,8 +1191,8 @@ __global__ __launch_bounds__(256) void gate_up_int4_dec_kernel(FfnParams P) {
     constexpr int NGW = 2 * NDW;
     static_assert(NGW <= 32, "the bias MFMA takes 32 groups");
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-    const int ntile = P.FF >> 4;
-    const int e = blockIdx.x / ntile, u = blockIdx.x - e * ntile;
+    const int nwt = (P.FF >> 4) / GUD_TPW;   // workgroups per expert
+    const int e = blockIdx.x / nwt, u0 = (blockIdx.x - e * nwt) * GUD_TPW;
     const int beg = P.offsets[e], end = P.offsets[e + 1];
     if (beg >= end) return;
     const int H = P.H, G = H / 64, GS = (G + 39) & ~7;
@@ -1195,86 +1200,67 @@ __global__ __launch_bounds__(256) void gate_up_int4_dec_kernel(FfnParams P) {
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r = lane & 15, q = lane >> 4;
     uint16_t* xs = reinterpret_cast<uint16_t*>(lds + L.xs);
     uint16_t* xsum = reinterpret_cast<uint16_t*>(lds + L.xsum);
-    float* s_sc = reinterpret_cast<float*>(lds + L.sc) + wave * (NGW * 16);
+    float* s_sc = reinterpret_cast<float*>(lds + L.sc) + wave * (GUD_TPW * NGW * 16);
     float* s_red = reinterpret_cast<float*>(lds + L.red);
     int* toks = reinterpret_cast<int*>(lds + L.tok);
     const int t = wave >> 1, part = wave & 1;
     const int ds0 = part * NDT / KS, nds = (part + 1) * NDT / KS - ds0;
     const int ng = 2 * nds, k0 = 128 * ds0;
 
-    // weights first: the scale dwords of this lane's row (groups 8q..8q+7 of the
-    // wave's range) and its 11 fragments
+    // The activations of a route tile come from L2 and arrive long before the
+    // weights, so they are requested first (tokens by uniform scalar loads,
+    // read before any global store): waiting for them in the in-order vector
+    // load counter does not wait for the weights.  A thread takes up to NSB of
+    // the tile's 4 x H/8 blocks of 8 elements; bf16 x is read as it is and put
+    // into the operand order in registers, fp32 x was converted by the
+    // preparation kernel (xq and its group sums).
+    constexpr int NSB = (GUD_RT * NDT * 16 + 255) / 256;
+    static_assert(GUD_RT == 4, "four route tokens");
     const uint8_t* blob = P.pool + static_cast<uint64_t>(P.slot_of[e]) * P.slot_bytes;
-    const int row = t * P.FF + int4_tile_base(u, P.FF) + (r & 8) + perm8(r & 7);
-    const uint32_t* srow = reinterpret_cast<const uint32_t*>(blob + P.os13) + (row * G + k0 / 64) / 2;
-    u32x4 sa = *reinterpret_cast<const u32x4*>(srow + 4 * (8 * q < ng ? q : 0));
-    const uint8_t* a_row = blob + P.o13 + row * (H / 2) + k0 / 2 + 16 * q;
-    u32x4 a[NDW];
+    const int nb = H / 8;   // blocks per row, a multiple of 16
+    int tk0 = P.sorted_route[beg] / P.k, tk1 = P.sorted_route[beg + min(1, end - beg - 1)] / P.k;
+    int tk2 = P.sorted_route[beg + min(2, end - beg - 1)] / P.k, tk3 = P.sorted_route[beg + min(3, end - beg - 1)] / P.k;
+    u32x4 xr[NSB];
+    auto load_x = [&](int nr) {
 #pragma unroll
-    for (int i = 0; i < NDW; ++i) a[i] = *reinterpret_cast<const u32x4*>(a_row + 64 * min(i, nds - 1));
-
-    for (int i = tid; i < 2 * GUD_RT * GS; i += 256) xsum[i] = 0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-        if (8 * q + 2 * j >= ng) sa[j] = 0u;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int g = 8 * q + 2 * j;
-        if (g < ng) {
-            s_sc[g * 16 + r] = __uint_as_float(sa[j] << 16);
-            s_sc[(g + 1) * 16 + r] = __uint_as_float(sa[j] & 0xFFFF0000u);
+        for (int sb = 0; sb < NSB; ++sb) {
+            const int i = min(tid + 256 * sb, nr * nb - 1);
+            const int j = i / nb, blk = i - j * nb;
+            const int tj = j >= 3 ? tk3 : (j == 2 ? tk2 : (j == 1 ? tk1 : tk0));
+            if (XT == BF16)
+                xr[sb] = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(P.x) + static_cast<int64_t>(tj) * H +
+                                                         int4_pos_to_k(8 * blk, H));
+            else
+                xr[sb] = *reinterpret_cast<const u32x4*>(P.xq + static_cast<int64_t>(tj) * H + 8 * blk);
         }
-    }
-
-    const int nb = H / 8;   // blocks of 8 per row, a multiple of 16
-    for (int rt = beg; rt < end; rt += GUD_RT) {
-        const int nr = min(GUD_RT, end - rt);
-        if (tid < GUD_RT) toks[tid] = P.sorted_route[rt + min(tid, nr - 1)] / P.k;
-        __syncthreads();   // toks; the previous tile's readers of xs, xsum and s_red are done
-        // activations of the nr tokens -> LDS (rows past nr keep stale values:
-        // their columns are never stored)
-        for (int i0 = tid; i0 < nr * nb; i0 += 512) {
-            float v[2][8];
+    };
+    auto store_x = [&](int nr) {
 #pragma unroll
-            for (int hh = 0; hh < 2; ++hh) {
-                const int i = min(i0 + 256 * hh, nr * nb - 1);
-                const int j = i / nb, kk = int4_pos_to_k((i - j * nb) * 8, H);
-                if (XT == F32) {
-                    const f32x4* src = reinterpret_cast<const f32x4*>(static_cast<const float*>(P.x) + static_cast<int64_t>(toks[j]) * H + kk);
-                    const f32x4 xa = src[0], xc = src[1];
+        for (int sb = 0; sb < NSB; ++sb) {
+            const int i = tid + 256 * sb;
+            const bool ok = i < nr * nb;   // nr * nb is a multiple of 16: whole 16-lane groups agree
+            const int ic = min(i, nr * nb - 1), j = ic / nb, blk = ic - j * nb;
+            if (XT == BF16) {
+                float v[8];
 #pragma unroll
-                    for (int m = 0; m < 4; ++m) {
-                        v[hh][m] = xa[m];
-                        v[hh][4 + m] = xc[m];
-                    }
-                } else {
-                    const u32x4 xa = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(P.x) + static_cast<int64_t>(toks[j]) * H + kk);
-#pragma unroll
-                    for (int m = 0; m < 4; ++m) {
-                        v[hh][2 * m] = __uint_as_float(xa[m] << 16);
-                        v[hh][2 * m + 1] = __uint_as_float(xa[m] & 0xFFFF0000u);
-                    }
+                for (int m = 0; m < 4; ++m) {
+                    v[2 * m] = __uint_as_float(xr[sb][m] << 16);
+                    v[2 * m + 1] = __uint_as_float(xr[sb][m] & 0xFFFF0000u);
                 }
-            }
+                u32x4 o;
+                float sum = 0.0f;
 #pragma unroll
-            for (int hh = 0; hh < 2; ++hh) {
-                const int i = i0 + 256 * hh;
-                if (i < nr * nb) {   // nr * nb is a multiple of 16: whole 16-lane groups take this branch
-                    const int j = i / nb, p0 = (i - j * nb) * 8;
-                    u32x4 o;
-                    float sum = 0.0f;
-#pragma unroll
-                    for (int m = 0; m < 4; ++m) {
-                        const uint16_t lo = f32_to_bf16(v[hh][perm8(2 * m)]), hi = f32_to_bf16(v[hh][perm8(2 * m + 1)]);
-                        o[m] = static_cast<uint32_t>(lo) | (static_cast<uint32_t>(hi) << 16);
-                        sum += bf16_to_f32(lo) + bf16_to_f32(hi);
-                    }
-                    *reinterpret_cast<u32x4*>(xs + j * (H + 8) + p0) = o;
-                    // the 8 blocks of a 64-group: block indices differing in bits 0, 2, 3
-                    sum += __shfl_xor(sum, 1, 64);
-                    sum += __shfl_xor(sum, 4, 64);
-                    sum += __shfl_xor(sum, 8, 64);
-                    const int blk = p0 >> 3;
+                for (int m = 0; m < 4; ++m) {
+                    const uint16_t lo = f32_to_bf16(v[perm8(2 * m)]), hi = f32_to_bf16(v[perm8(2 * m + 1)]);
+                    o[m] = static_cast<uint32_t>(lo) | (static_cast<uint32_t>(hi) << 16);
+                    sum += bf16_to_f32(lo) + bf16_to_f32(hi);
+                }
+                // the 8 blocks of a 64-group: block indices differing in bits 0, 2, 3
+                sum += __shfl_xor(sum, 1, 64);
+                sum += __shfl_xor(sum, 4, 64);
+                sum += __shfl_xor(sum, 8, 64);
+                if (ok) {
+                    *reinterpret_cast<u32x4*>(xs + j * H + 8 * blk) = o;
                     if ((blk & 13) == 0) {
                         const int gi = j * GS + (blk >> 4) * 2 + ((blk >> 1) & 1);
                         const uint16_t shi = f32_to_bf16(sum);
@@ -1282,53 +1268,242 @@ __global__ __launch_bounds__(256) void gate_up_int4_dec_kernel(FfnParams P) {
                         xsum[GUD_RT * GS + gi] = f32_to_bf16(sum - bf16_to_f32(shi));
                     }
                 }
+            } else if (ok) {
+                *reinterpret_cast<u32x4*>(xs + j * H + 8 * blk) = xr[sb];
             }
         }
-        __syncthreads();
+        if (XT != BF16) {
+            const uint16_t* xsg = reinterpret_cast<const uint16_t*>(P.xsum);
+            for (int i = tid; i < 2 * nr * G; i += 256) {
+                const int hl = i / (nr * G), rem = i - hl * (nr * G), j = rem / G, g = rem - j * G;
+                const int tj = j >= 3 ? tk3 : (j == 2 ? tk2 : (j == 1 ? tk1 : tk0));
+                xsum[(hl * GUD_RT + j) * GS + g] = xsg[(static_cast<int64_t>(hl) * P.T + tj) * G + g];
+            }
+        }
+    };
+    load_x(min(GUD_RT, end - beg));
 
+    // then the weights: the scale dwords of this lane's row (groups 8q..8q+7 of
+    // the wave's range) and its 11 fragments
+    u32x4 sa[GUD_TPW];
+    u32x4 a[GUD_TPW][NDW];
+#pragma unroll
+    for (int tt = 0; tt < GUD_TPW; ++tt) {
+        const int row = t * P.FF + int4_tile_base(u0 + tt, P.FF) + (r & 8) + perm8(r & 7);
+        const uint32_t* srow = reinterpret_cast<const uint32_t*>(blob + P.os13) + (row * G + k0 / 64) / 2;
+        sa[tt] = *reinterpret_cast<const u32x4*>(srow + 4 * (8 * q < ng ? q : 0));
+        const uint8_t* a_row = blob + P.o13 + row * (H / 2) + k0 / 2 + 16 * q;
+#pragma unroll
+        for (int i = 0; i < NDW; ++i) a[tt][i] = *reinterpret_cast<const u32x4*>(a_row + 64 * min(i, nds - 1));
+    }
+
+    for (int i = tid; i < 2 * GUD_RT * GS; i += 256) xsum[i] = 0;
+    __syncthreads();   // padding zero before any group sum lands
+    auto compute_tile = [&](int rt, int nr) {
         // column r of the MFMA is token slot r % RT (slots past nr are discarded)
         const int slot = r & (GUD_RT - 1);
-        const uint16_t* xrow = xs + slot * (H + 8) + k0 + 32 * q;
+        const uint16_t* xrow = xs + slot * H + k0 + 32 * q;
         const uint32_t* shi = reinterpret_cast<const uint32_t*>(xsum + slot * GS + k0 / 64 + 8 * q);
         const uint32_t* slo = reinterpret_cast<const uint32_t*>(xsum + GUD_RT * GS + slot * GS + k0 / 64 + 8 * q);
         const u32x4 xhi = {shi[0], shi[1], shi[2], shi[3]};
         const u32x4 xlo = {slo[0], slo[1], slo[2], slo[3]};
         const f32x4 zero = {0, 0, 0, 0};
-        f32x4 corr = mfma16x16x32(sa, xhi, zero);
-        corr = mfma16x16x32(sa, xlo, corr);
-        f32x4 acc = corr * -136.0f;
+        f32x4 acc[GUD_TPW];
+#pragma unroll
+        for (int tt = 0; tt < GUD_TPW; ++tt) {
+            f32x4 corr = mfma16x16x32(sa[tt], xhi, zero);
+            corr = mfma16x16x32(sa[tt], xlo, corr);
+            acc[tt] = corr * -136.0f;
+        }
 #pragma unroll
         for (int i = 0; i < NDW; ++i) {
             if (i < nds) {
-                const u32x4 vv = regroup(a[i]);
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
                     const u32x4 b0 = *reinterpret_cast<const u32x4*>(xrow + 128 * i + 16 * h);
                     const u32x4 b1 = *reinterpret_cast<const u32x4*>(xrow + 128 * i + 16 * h + 8);
-                    f32x4 tt = mfma16x16x32(deq_int4(vv[2 * h]), b0, zero);
-                    tt = mfma16x16x32(deq_int4(vv[2 * h + 1]), b1, tt);
-                    acc += *reinterpret_cast<const f32x4*>(s_sc + (2 * i + h) * 16 + 4 * q) * tt;
+#pragma unroll
+                    for (int tt = 0; tt < GUD_TPW; ++tt) {
+                        const u32x4 vv = regroup(a[tt][i]);
+                        f32x4 d = mfma16x16x32(deq_int4(vv[2 * h]), b0, zero);
+                        d = mfma16x16x32(deq_int4(vv[2 * h + 1]), b1, d);
+                        acc[tt] += *reinterpret_cast<const f32x4*>(s_sc + (tt * NGW + 2 * i + h) * 16 + 4 * q) * d;
+                    }
                 }
             }
         }
         if (wave > 0) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) s_red[((wave - 1) * 4 + j) * 64 + lane] = acc[j];
+            for (int tt = 0; tt < GUD_TPW; ++tt)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) s_red[((tt * 3 + wave - 1) * 4 + j) * 64 + lane] = acc[tt][j];
         }
         __syncthreads();
         if (wave == 0 && r < nr) {
             // gate = this wave + wave 1 (other K half); up = waves 2 + 3
-            f32x4 g = acc, uu;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                g[j] += s_red[(0 * 4 + j) * 64 + lane];
-                uu[j] = s_red[(1 * 4 + j) * 64 + lane] + s_red[(2 * 4 + j) * 64 + lane];
-            }
             const int p = rt + r;
-            const uint32_t h0 = pack_bf16x2(act_fn(P.act, g[0]) * uu[0], act_fn(P.act, g[1]) * uu[1]);
-            const uint32_t h1 = pack_bf16x2(act_fn(P.act, g[2]) * uu[2], act_fn(P.act, g[3]) * uu[3]);
-            *reinterpret_cast<u32x2*>(P.h + static_cast<int64_t>(p) * P.FF + 16 * u + 4 * q) = u32x2{h0, h1};
+#pragma unroll
+            for (int tt = 0; tt < GUD_TPW; ++tt) {
+                f32x4 g = acc[tt], uu;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    g[j] += s_red[((tt * 3 + 0) * 4 + j) * 64 + lane];
+                    uu[j] = s_red[((tt * 3 + 1) * 4 + j) * 64 + lane] + s_red[((tt * 3 + 2) * 4 + j) * 64 + lane];
+                }
+                const uint32_t h0 = pack_bf16x2(act_fn(P.act, g[0]) * uu[0], act_fn(P.act, g[1]) * uu[1]);
+                const uint32_t h1 = pack_bf16x2(act_fn(P.act, g[2]) * uu[2], act_fn(P.act, g[3]) * uu[3]);
+                *reinterpret_cast<u32x2*>(P.h + static_cast<int64_t>(p) * P.FF + 16 * (u0 + tt) + 4 * q) = u32x2{h0, h1};
+            }
         }
+    };
+
+    // first route tile: its activations were requested before the weights
+    const int nr0 = min(GUD_RT, end - beg);
+    store_x(nr0);
+#pragma unroll
+    for (int tt = 0; tt < GUD_TPW; ++tt) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            if (8 * q + 2 * j >= ng) sa[tt][j] = 0u;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int g = 8 * q + 2 * j;
+            if (g < ng) {
+                s_sc[(tt * NGW + g) * 16 + r] = __uint_as_float(sa[tt][j] << 16);
+                s_sc[(tt * NGW + g + 1) * 16 + r] = __uint_as_float(sa[tt][j] & 0xFFFF0000u);
+            }
+        }
+    }
+    __syncthreads();
+    compute_tile(beg, nr0);
+    // further route tiles (groups of more than 4 routes)
+    for (int rt = beg + GUD_RT; rt < end; rt += GUD_RT) {
+        const int nr = min(GUD_RT, end - rt);
+        tk0 = P.sorted_route[rt] / P.k;
+        tk1 = P.sorted_route[rt + min(1, nr - 1)] / P.k;
+        tk2 = P.sorted_route[rt + min(2, nr - 1)] / P.k;
+        tk3 = P.sorted_route[rt + min(3, nr - 1)] / P.k;
+        __syncthreads();   // the previous tile's readers of xs, xsum and s_red are done
+        load_x(nr);
+        store_x(nr);
+        __syncthreads();
+        compute_tile(rt, nr);
+    }
+}
+
+// ------------------------------------------------------ int4 down, decode --
+// One workgroup of 4 waves per (expert, 64 rows of H); a wave owns 16 rows and
+// the whole K = FF (NDS double steps and, when FF % 128 == 64, a tail group).
+// The expert's routes are taken 4 at a time.  The first tile's h rows are
+// requested before the weights (h sits in L2), so waiting for them in the
+// in-order vector load counter does not wait for the weights; all weight
+// fragments and row scales of the wave are then requested at once.
+template <int NDS, bool TAIL>
+__global__ __launch_bounds__(256) void down_int4_dec_kernel(FfnParams P) {
+    constexpr int NG = 2 * NDS + (TAIL ? 1 : 0);   // groups per row
+    constexpr int SPL = (16 * NG + 63) / 64;       // scale values per lane
+    constexpr int RT = GUD_RT;
+    __shared__ __attribute__((aligned(16))) uint16_t hs[RT * 128 * (NDS + 1)];   // [RT][FF] bf16
+    __shared__ float s_scs[4][NG * 16];
+    const int FF = P.FF;
+    const int nblk = P.H >> 6;
+    const int e = blockIdx.x / nblk, blk = blockIdx.x - e * nblk;
+    const int beg = P.offsets[e], end = P.offsets[e + 1];
+    if (beg >= end) return;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r = lane & 15, q = lane >> 4;
+    const uint8_t* blob = P.pool + static_cast<uint64_t>(P.slot_of[e]) * P.slot_bytes;   // scalar, first
+    const int m0 = blk * 64 + wave * 16;
+    float* s_sc = s_scs[wave];
+    constexpr int NHB = (RT * 128 * (NDS + 1) / 8 + 255) / 256;   // blocks of 8 per thread (upper bound)
+    const int nbr = FF / 8;                                         // blocks per h row
+
+    u32x4 hr[NHB];
+    auto load_h = [&](int rt, int nr) {
+#pragma unroll
+        for (int sb = 0; sb < NHB; ++sb) {
+            const int i = min(tid + 256 * sb, nr * nbr - 1);
+            const int j = i / nbr, c = i - j * nbr;
+            hr[sb] = *reinterpret_cast<const u32x4*>(P.h + static_cast<int64_t>(rt + j) * FF + 8 * c);
+        }
+    };
+    auto store_h = [&](int nr) {
+#pragma unroll
+        for (int sb = 0; sb < NHB; ++sb) {
+            const int i = tid + 256 * sb;
+            if (i < nr * nbr) {
+                const int j = i / nbr, c = i - j * nbr;
+                *reinterpret_cast<u32x4*>(hs + j * FF + 8 * c) = hr[sb];
+            }
+        }
+    };
+    const int nr0 = min(RT, end - beg);
+    load_h(beg, nr0);
+
+    // weights of the wave's 16 rows, and their scales
+    const uint8_t* a_row = blob + P.o2 + static_cast<int64_t>(m0 + r) * (FF / 2);
+    u32x4 a[NDS];
+#pragma unroll
+    for (int i = 0; i < NDS; ++i) a[i] = *reinterpret_cast<const u32x4*>(a_row + 64 * i + 16 * q);
+    u32x2 at = {0u, 0u};
+    if (TAIL) at = *reinterpret_cast<const u32x2*>(a_row + 64 * NDS + 8 * q);
+    float sv[SPL];
+    {
+        const uint16_t* sc = reinterpret_cast<const uint16_t*>(blob + P.os2);
+#pragma unroll
+        for (int m = 0; m < SPL; ++m) {
+            const int idx = min(lane + 64 * m, 16 * NG - 1);
+            const int i = idx / NG, g = idx - i * NG;
+            sv[m] = bf16_to_f32(sc[static_cast<int64_t>(m0 + i) * NG + g]);
+        }
+    }
+
+    auto compute_tile = [&](int rt, int nr) {
+        const int slot = r & (RT - 1);
+        const uint16_t* hrow = hs + slot * FF + 32 * q;
+        f32x4 acc = {0, 0, 0, 0};
+#pragma unroll
+        for (int i = 0; i < NDS; ++i) {
+            u32x4 b[4];
+#pragma unroll
+            for (int m = 0; m < 4; ++m) b[m] = *reinterpret_cast<const u32x4*>(hrow + 128 * i + 8 * m);
+            const u32x4 v = regroup(a[i]);
+            int4_group(v[0], v[1], b[0], b[1], *reinterpret_cast<const f32x4*>(s_sc + (2 * i) * 16 + 4 * q), acc);
+            int4_group(v[2], v[3], b[2], b[3], *reinterpret_cast<const f32x4*>(s_sc + (2 * i + 1) * 16 + 4 * q), acc);
+        }
+        if (TAIL) {
+            const uint16_t* tr = hs + slot * FF + 128 * NDS + 16 * q;
+            const u32x4 b0 = *reinterpret_cast<const u32x4*>(tr), b1 = *reinterpret_cast<const u32x4*>(tr + 8);
+            int4_group(at[0], at[1], b0, b1, *reinterpret_cast<const f32x4*>(s_sc + 2 * NDS * 16 + 4 * q), acc);
+        }
+        if (r < nr) {
+            const int64_t o = static_cast<int64_t>(rt + r) * P.H + m0 + 4 * q;
+            if (P.out_dt == F32) {
+                *reinterpret_cast<f32x4*>(static_cast<float*>(P.out) + o) = acc;
+            } else {
+                *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(P.out) + o) =
+                    u32x2{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
+            }
+        }
+    };
+
+    store_h(nr0);
+#pragma unroll
+    for (int m = 0; m < SPL; ++m) {
+        const int idx = lane + 64 * m;
+        if (idx < 16 * NG) {
+            const int i = idx / NG, g = idx - i * NG;
+            s_sc[g * 16 + i] = sv[m];
+        }
+    }
+    __syncthreads();
+    compute_tile(beg, nr0);
+    for (int rt = beg + RT; rt < end; rt += RT) {
+        const int nr = min(RT, end - rt);
+        __syncthreads();   // readers of the previous tile's h are done
+        load_h(rt, nr);
+        store_h(nr);
+        __syncthreads();
+        compute_tile(rt, nr);
     }
 }
 
@@ -1450,6 +1625,10 @@ static void launch_int4(const FfnParams& P, int phases, hipStream_t s) {
     }
     if (phases & 2) {
         const size_t smem = 4 * 16 * (P.FF / 64) * sizeof(float);
+        if (P.FF == 704) {   // decode: 5 double steps and a tail group
+            hipLaunchKernelGGL((down_int4_dec_kernel<5, true>), dim3(P.E * (P.H / 64)), dim3(256), 0, s, P);
+            return;
+        }
         if (P.FF <= 704)   // <= 5 double steps and a tail, <= 11 groups
             hipLaunchKernelGGL((down_int4_kernel<5, 3>), dim3(P.E * (P.H / 64), tiles_y), dim3(256), smem, s, P);
         else
@@ -1541,12 +1720,19 @@ hipError_t launch_ffn(const FfnParams& P0, int phases, int path, hipStream_t s) 
     // int4, large token groups: LDS-staged grouped GEMM (both halves, so that
     // split calls with the same T agree on the layout of h)
     if (int4_gemm_eligible(P) && (path == 2 || (path == 0 && P.T >= 256))) return launch_int4_gemm(P, phases, s);
-    if ((phases & 1) && path != 2 && P.fmt == W_INT4 && P.H == 2816 && P.FF % 16 == 0) {
+    if ((phases & 1) && path != 2 && P.fmt == W_INT4 && P.H == 2816 && P.FF % (16 * GUD_TPW) == 0) {
         const GudLds L = gud_lds(P.H);
-        if (P.x_dt == F32)
-            hipLaunchKernelGGL((gate_up_int4_dec_kernel<22, F32>), dim3(P.E * (P.FF / 16)), dim3(256), L.total, s, P);
-        else
-            hipLaunchKernelGGL((gate_up_int4_dec_kernel<22, BF16>), dim3(P.E * (P.FF / 16)), dim3(256), L.total, s, P);
+        const dim3 grid(P.E * (P.FF / 16 / GUD_TPW));
+        if (P.x_dt == F32) {
+            const int64_t nblk = static_cast<int64_t>(P.T) * P.H / 8;
+            P.xq = P.xq_out;
+            P.xsum = P.xsum_out;
+            hipLaunchKernelGGL((prep_x_int4_kernel<F32>), dim3(static_cast<uint32_t>((nblk + 255) / 256)), dim3(256), 0, s,
+                               P.x, P.T, P.H, P.xq_out, P.xsum);
+            hipLaunchKernelGGL((gate_up_int4_dec_kernel<22, F32>), grid, dim3(256), L.total, s, P);
+        } else {
+            hipLaunchKernelGGL((gate_up_int4_dec_kernel<22, BF16>), grid, dim3(256), L.total, s, P);
+        }
         P.xq = nullptr;   // tells launch_int4 the first half is done
         if (phases == 1) return hipGetLastError();
         launch_int4(P, 2, s);
