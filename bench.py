@@ -32,7 +32,7 @@ import synth  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
 # the kernel moe_ffn_gate_up launches for int4 at H = 2816, T <= 16 (the whole call)
-GATE_UP_KERNEL = "gate_up_int4_persist_kernel"
+GATE_UP_KERNEL = "gate_up_int4_dec_kernel"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gate_up_int4_T16.json")
 CALIB_BYTES = 512 << 20
 MFMA_BF16_PEAK_TFLOPS = 2500.0
