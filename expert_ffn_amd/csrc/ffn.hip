@@ -794,365 +794,6 @@ __global__ __launch_bounds__(256) void down_int4_kernel(FfnParams P) {
     }
 }
 
-// gate/up, int4, decode fast path (H = 256 * NDS): workgroup = 4 waves =
-// (tile t: gate or up) x (K half hp), each 16 rows x NDS double steps.
-// Issue order keeps the in-order load counter from serialising the wave:
-// route indices (uniform, scalar loads), then this lane's row scales, the
-// first two weight fragments, the first activations, then the remaining
-// weights.  The -136 bias of the expanded codes is folded into each group's
-// MFMA accumulator as -136 * (sum of the group's bf16 activations), which the
-// preparation kernel stores per token and group (xsum).
-template <int NDT, int KS>
-__global__ __launch_bounds__(128 * KS) void gate_up_int4_fast_kernel(FfnParams P) {
-    // NDT double steps per row (H = 128 NDT) split over KS waves per tile:
-    // wave (t, part) covers double steps [part*NDT/KS, (part+1)*NDT/KS).
-    constexpr int NDW = (NDT + KS - 1) / KS;    // most double steps of one wave
-    constexpr int NGW = 2 * NDW;                // most groups of one wave (<= 32)
-    static_assert(NGW <= 32, "the bias MFMA takes 32 groups");
-    extern __shared__ float smem[];             // s_sc [2KS][NGW][16], s_red [2KS-1][4][64]
-    const int ntile = P.FF >> 4;
-    const int e = blockIdx.x / ntile, u = blockIdx.x - e * ntile;
-    const int beg = P.offsets[e] + 16 * static_cast<int>(blockIdx.y), end = P.offsets[e + 1];
-    if (beg >= end) return;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, r = lane & 15, q = lane >> 4;
-    const int t = wave / KS, part = wave - t * KS;
-    const int ds0 = part * NDT / KS, nds = (part + 1) * NDT / KS - ds0;
-    const int ng = 2 * nds;
-    const uint8_t* blob = P.pool + static_cast<uint64_t>(P.slot_of[e]) * P.slot_bytes;
-    const int n0 = int4_tile_base(u, P.FF);
-    const int row = t * P.FF + n0 + (r & 8) + perm8(r & 7);
-    const int k0 = 128 * ds0;
-    const int G = P.H / 64;
-
-    int routes[16];
-#pragma unroll
-    for (int c = 0; c < 16; ++c) routes[c] = P.sorted_route[min(beg + c, end - 1)];
-    // scales of this lane's row, groups 8q..8q+7 of the wave's range (bf16
-    // pairs, natural order): the A operand of the bias MFMA and the source of
-    // the per-group scale staging.  Groups past the wave's range are zeroed.
-    const uint32_t* srow = reinterpret_cast<const uint32_t*>(blob + P.os13) + (static_cast<int64_t>(row) * G + k0 / 64) / 2;
-    u32x4 sa = *reinterpret_cast<const u32x4*>(srow + 4 * (8 * q < ng ? q : 0));
-    const uint8_t* a_row = blob + P.o13 + static_cast<int64_t>(row) * (P.H / 2) + k0 / 2 + 16 * q;
-    u32x4 a[NDW];
-    a[0] = *reinterpret_cast<const u32x4*>(a_row);
-    if (NDW > 1 && nds > 1) a[1] = *reinterpret_cast<const u32x4*>(a_row + 64);
-    int route = routes[0];
-#pragma unroll
-    for (int c = 1; c < 16; ++c) route = (r == c) ? routes[c] : route;
-    const int p = beg + r;
-    const bool valid = p < end;
-    const int tok = route / P.k;
-    // only lanes holding a route load activations (the others read zeros
-    // without a memory access; their D columns are never stored)
-    const rsrc_t xres = make_rsrc(P.xq, static_cast<uint32_t>(P.T) * P.H * 2);
-    const uint32_t xoff = valid ? static_cast<uint32_t>((tok * P.H + k0 + 32 * q) * 2) : NO_LANE;
-    u32x4 b[2][4];
-#pragma unroll
-    for (int m = 0; m < 4; ++m) b[0][m] = bload16(xres, xoff + 16 * m);
-    const rsrc_t sres = make_rsrc(P.xsum, static_cast<uint32_t>(P.T) * G * 4);
-    const uint32_t soff = valid ? static_cast<uint32_t>((tok * G + k0 / 64 + 8 * q) * 2) : NO_LANE;
-    const u32x4 xhi = bload16(sres, soff), xlo = bload16(sres, soff + static_cast<uint32_t>(P.T) * G * 2);
-#pragma unroll
-    for (int i = 2; i < NDW; ++i)
-        if (i < nds) a[i] = *reinterpret_cast<const u32x4*>(a_row + 64 * i);
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-        if (8 * q + 2 * j >= ng) sa[j] = 0u;
-    // scales -> wave-private LDS in the D-row layout (row r of this lane is D row r)
-    float* s_sc = smem + wave * (16 * NGW);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int g = 8 * q + 2 * j;
-        if (g < ng) {
-            s_sc[g * 16 + r] = __uint_as_float(sa[j] << 16);
-            s_sc[(g + 1) * 16 + r] = __uint_as_float(sa[j] & 0xFFFF0000u);
-        }
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-
-    // bias of the expanded codes: -136 * sum_g s[row][g] * X[col][g]
-    const f32x4 zero = {0, 0, 0, 0};
-    f32x4 corr = mfma16x16x32(sa, xhi, zero);
-    corr = mfma16x16x32(sa, xlo, corr);
-    f32x4 acc = corr * -136.0f;
-#pragma unroll
-    for (int i = 0; i < NDW; ++i) {
-        if (i < nds) {
-            if (i + 1 < nds) {
-#pragma unroll
-                for (int m = 0; m < 4; ++m) b[(i + 1) & 1][m] = bload16(xres, xoff + 256 * (i + 1) + 16 * m);
-            }
-            const u32x4 v = regroup(a[i]);
-            const u32x4* bb = b[i & 1];
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                f32x4 tt = mfma16x16x32(deq_int4(v[2 * h]), bb[2 * h], zero);
-                tt = mfma16x16x32(deq_int4(v[2 * h + 1]), bb[2 * h + 1], tt);
-                acc += *reinterpret_cast<const f32x4*>(s_sc + (2 * i + h) * 16 + 4 * q) * tt;
-            }
-        }
-    }
-    float* s_red = smem + 2 * KS * 16 * NGW;
-    if (wave > 0) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) s_red[((wave - 1) * 4 + j) * 64 + lane] = acc[j];
-    }
-    __syncthreads();
-    if (wave != 0) return;
-    f32x4 g = acc, uu = zero;
-#pragma unroll
-    for (int w = 1; w < 2 * KS; ++w)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const float v = s_red[((w - 1) * 4 + j) * 64 + lane];
-            if (w < KS) g[j] += v; else uu[j] += v;
-        }
-    if (valid) {
-        const uint32_t h0 = pack_bf16x2(act_fn(P.act, g[0]) * uu[0], act_fn(P.act, g[1]) * uu[1]);
-        const uint32_t h1 = pack_bf16x2(act_fn(P.act, g[2]) * uu[2], act_fn(P.act, g[3]) * uu[3]);
-        *reinterpret_cast<u32x2*>(P.h + static_cast<int64_t>(p) * P.FF + 16 * u + 4 * q) = u32x2{h0, h1};
-    }
-}
-
-// ------------------------------------------- int4 gate/up, decode, persistent --
-// One workgroup of 16 waves per CU.  Everything an item needs besides its
-// weights lives in LDS: the activations of all T tokens in the int4 operand
-// order (with their bf16 hi/lo group sums), the tokens of the sorted routes and
-// the table of experts that have routes.  An item is (active expert, 16
-// positions of h); the workgroup runs two at a time, each on 8 waves = (gate or
-// up) x 4 parts of K.  A wave loads the weights of its next item while it
-// computes the current one: activations come from LDS, so waiting on them never
-// waits on the weight loads in flight.
-constexpr int GUP_KS = 4;          // waves per tile splitting K
-constexpr int GUP_MAX_T = 16;      // tokens whose activations fit in LDS
-
-struct GupLds {                    // offsets (bytes) into dynamic LDS
-    int xs, xsum, tok, act, sc, red, total;
-};
-__host__ __device__ inline GupLds gup_lds(int T, int H, int E, int R) {
-    GupLds L;
-    const int G = H / 64;
-    L.xs = 0;                                         // bf16 [T][H + 8]
-    L.xsum = L.xs + T * (H + 8) * 2;                  // bf16 [2][T][GS] (hi, lo; zero pad), GS = G + 32 rounded to 8
-    L.tok = L.xsum + 2 * T * ((G + 39) & ~7) * 2;     // int [R]
-    L.act = L.tok + R * 4;                            // int [4][E] expert, beg, end, slot; [4E] = count
-    L.sc = (L.act + 16 * E + 4 + 15) & ~15;           // float [16 waves][NGW][16]
-    L.red = L.sc + 16 * 12 * 16 * 4;                  // float [2 parities][2 groups][7][4][64]
-    L.total = L.red + 4 * 7 * 4 * 64 * 4;
-    return L;
-}
-
-template <int NDT, int XT>
-__global__ __launch_bounds__(1024) void gate_up_int4_persist_kernel(FfnParams P) {
-    constexpr int KS = GUP_KS;
-    constexpr int NDW = (NDT + KS - 1) / KS;   // most double steps of one wave
-    constexpr int NGW = 2 * NDW;
-    static_assert(NGW <= 12, "scale staging holds 12 groups per wave");
-    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-    const int T = P.T, H = P.H, G = H / 64, E = P.E, R = P.T * P.k;
-    const int GS = (G + 39) & ~7;   // row stride of the group sums: the bias MFMA may read 32 groups past k0
-    const GupLds L = gup_lds(T, H, E, R);
-    uint16_t* xs = reinterpret_cast<uint16_t*>(lds + L.xs);
-    uint16_t* xsum = reinterpret_cast<uint16_t*>(lds + L.xsum);
-    int* toks = reinterpret_cast<int*>(lds + L.tok);
-    int* act = reinterpret_cast<int*>(lds + L.act);
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r = lane & 15, q = lane >> 4;
-
-    // ---- prologue: activations, group sums, route tokens, active experts
-    for (int i = tid; i < 2 * T * GS; i += 1024) xsum[i] = 0;
-    __syncthreads();
-    for (int b = tid; b < T * (H / 8); b += 1024) {   // T*H/8 is a multiple of 16
-        const int t = b / (H / 8), p0 = (b - t * (H / 8)) * 8;
-        const int k0 = int4_pos_to_k(p0, H);
-        float v[8];
-        if (XT == F32) {
-            const f32x4* src = reinterpret_cast<const f32x4*>(static_cast<const float*>(P.x) + static_cast<int64_t>(t) * H + k0);
-            const f32x4 a = src[0], c = src[1];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                v[j] = a[j];
-                v[4 + j] = c[j];
-            }
-        } else {
-            const u32x4 a = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(P.x) + static_cast<int64_t>(t) * H + k0);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                v[2 * j] = __uint_as_float(a[j] << 16);
-                v[2 * j + 1] = __uint_as_float(a[j] & 0xFFFF0000u);
-            }
-        }
-        u32x4 o;
-        float sum = 0.0f;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const uint16_t lo = f32_to_bf16(v[perm8(2 * j)]), hi = f32_to_bf16(v[perm8(2 * j + 1)]);
-            o[j] = static_cast<uint32_t>(lo) | (static_cast<uint32_t>(hi) << 16);
-            sum += bf16_to_f32(lo) + bf16_to_f32(hi);
-        }
-        *reinterpret_cast<u32x4*>(xs + t * (H + 8) + p0) = o;
-        sum += __shfl_xor(sum, 1, 64);
-        sum += __shfl_xor(sum, 4, 64);
-        sum += __shfl_xor(sum, 8, 64);
-        const int blk = p0 >> 3;
-        if ((blk & 13) == 0) {
-            const int gi = t * GS + (blk >> 4) * 2 + ((blk >> 1) & 1);
-            const uint16_t hi = f32_to_bf16(sum);
-            xsum[gi] = hi;
-            xsum[T * GS + gi] = f32_to_bf16(sum - bf16_to_f32(hi));
-        }
-    }
-    const int nkept = P.offsets[E];
-    for (int i = tid; i < nkept; i += 1024) toks[i] = P.sorted_route[i] / P.k;
-    if (wave == 0) {
-        int na = 0;
-        for (int e0 = 0; e0 < E; e0 += 64) {
-            const int e = e0 + lane;
-            const int b0 = e < E ? P.offsets[e] : 0, b1 = e < E ? P.offsets[e + 1] : 0;
-            const bool has = b1 > b0;
-            const uint64_t m = __ballot(has);
-            const int pos = na + __popcll(m & ((lane == 0) ? 0ull : (~0ull >> (64 - lane))));
-            if (has) {
-                act[pos] = e;
-                act[E + pos] = b0;
-                act[2 * E + pos] = b1;
-                act[3 * E + pos] = P.slot_of[e];
-            }
-            na += __popcll(m);
-        }
-        if (lane == 0) act[4 * E] = na;
-    }
-    __syncthreads();
-    const int nact = act[4 * E];
-
-    // ---- items: (active expert, 16-row tile u of gate and up); one per group
-    // of 8 waves at a time, round robin over the groups of the grid.  Item
-    // indices are wave-uniform (scalar registers); the weight loads of the next
-    // item are unconditional (past the end they re-read the last item, a cache
-    // hit) so that the wait before a compute only covers the older item.
-    const int ntile = P.FF >> 4;
-    const int nitems = nact * ntile;
-    if (nitems == 0) return;
-    const int grp = wave >> 3, wg = wave & 7, t = wg / KS, part = wg - t * KS;
-    const int ds0 = part * NDT / KS, nds = (part + 1) * NDT / KS - ds0;
-    const int ng = 2 * nds, k0 = 128 * ds0;
-    const int gid = __builtin_amdgcn_readfirstlane(2 * static_cast<int>(blockIdx.x) + grp), ngr = 2 * gridDim.x;
-    // the same trip count for both groups of the workgroup (they share barriers)
-    const int niter = (nitems - 2 * static_cast<int>(blockIdx.x) + ngr - 1) / ngr;
-    float* s_sc = reinterpret_cast<float*>(lds + L.sc) + wave * (NGW * 16);
-    float* s_red0 = reinterpret_cast<float*>(lds + L.red) + grp * (7 * 4 * 64);   // [parity][group][7][4][64]
-    const int lrow = (r & 8) + perm8(r & 7);
-
-    // weight fragments and scale dwords of an item, this wave's part
-    auto fetch = [&](int it, u32x4* a, u32x4& sa) {
-        it = min(it, nitems - 1);
-        const int ai = it / ntile, u = it - ai * ntile;
-        const int slot = __builtin_amdgcn_readfirstlane(act[3 * E + ai]);
-        const uint8_t* blob = P.pool + static_cast<uint64_t>(slot) * P.slot_bytes;
-        const int row = t * P.FF + int4_tile_base(u, P.FF) + lrow;
-        const uint32_t* srow = reinterpret_cast<const uint32_t*>(blob + P.os13) + (row * G + k0 / 64) / 2;
-        sa = *reinterpret_cast<const u32x4*>(srow + 4 * (8 * q < ng ? q : 0));
-        const uint8_t* a_row = blob + P.o13 + row * (H / 2) + k0 / 2 + 16 * q;
-#pragma unroll
-        for (int i = 0; i < NDW; ++i) a[i] = *reinterpret_cast<const u32x4*>(a_row + 64 * min(i, nds - 1));
-    };
-    auto compute = [&](int it, const u32x4* a, u32x4 sa, float* s_red) {
-        const int ai = it / ntile;
-        const int beg = act[E + ai], end = act[2 * E + ai];
-        // one 16-route tile: an expert has at most T <= 16 routes
-        const int p = beg + r;
-        const int tok = toks[p < end ? p : beg];
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            if (8 * q + 2 * j >= ng) sa[j] = 0u;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int g = 8 * q + 2 * j;
-            if (g < ng) {
-                s_sc[g * 16 + r] = __uint_as_float(sa[j] << 16);
-                s_sc[(g + 1) * 16 + r] = __uint_as_float(sa[j] & 0xFFFF0000u);
-            }
-        }
-        const uint16_t* xrow = xs + tok * (H + 8) + k0 + 32 * q;
-        // dword-aligned only (k0 / 64 may be odd in dwords): four dword reads
-        const uint32_t* shi = reinterpret_cast<const uint32_t*>(xsum + tok * GS + k0 / 64 + 8 * q);
-        const uint32_t* slo = reinterpret_cast<const uint32_t*>(xsum + T * GS + tok * GS + k0 / 64 + 8 * q);
-        const u32x4 xhi = {shi[0], shi[1], shi[2], shi[3]};
-        const u32x4 xlo = {slo[0], slo[1], slo[2], slo[3]};
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        const f32x4 zero = {0, 0, 0, 0};
-        f32x4 corr = mfma16x16x32(sa, xhi, zero);
-        corr = mfma16x16x32(sa, xlo, corr);
-        f32x4 acc = corr * -136.0f;
-#pragma unroll
-        for (int i = 0; i < NDW; ++i) {
-            if (i < nds) {
-                u32x4 bb[4];
-#pragma unroll
-                for (int m = 0; m < 4; ++m) bb[m] = *reinterpret_cast<const u32x4*>(xrow + 128 * i + 8 * m);
-                const u32x4 v = regroup(a[i]);
-#pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    f32x4 tt = mfma16x16x32(deq_int4(v[2 * h]), bb[2 * h], zero);
-                    tt = mfma16x16x32(deq_int4(v[2 * h + 1]), bb[2 * h + 1], tt);
-                    acc += *reinterpret_cast<const f32x4*>(s_sc + (2 * i + h) * 16 + 4 * q) * tt;
-                }
-            }
-        }
-        if (wg > 0) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) s_red[((wg - 1) * 4 + j) * 64 + lane] = acc[j];
-        }
-        return acc;
-    };
-    auto finish = [&](int it, f32x4 acc, const float* s_red) {
-        // leader wave of the group: gate parts 1.., up parts 0.. from LDS
-        const int ai = it / ntile, u = it - ai * ntile;
-        const int beg = act[E + ai], end = act[2 * E + ai];
-        const int p = beg + r;
-        f32x4 g = acc, uu = {0, 0, 0, 0};
-#pragma unroll
-        for (int w = 1; w < 2 * KS; ++w)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const float v = s_red[((w - 1) * 4 + j) * 64 + lane];
-                if (w < KS) g[j] += v; else uu[j] += v;
-            }
-        if (p < end) {
-            const uint32_t h0 = pack_bf16x2(act_fn(P.act, g[0]) * uu[0], act_fn(P.act, g[1]) * uu[1]);
-            const uint32_t h1 = pack_bf16x2(act_fn(P.act, g[2]) * uu[2], act_fn(P.act, g[3]) * uu[3]);
-            *reinterpret_cast<u32x2*>(P.h + static_cast<int64_t>(p) * P.FF + 16 * u + 4 * q) = u32x2{h0, h1};
-        }
-    };
-    // one barrier per item: the partial sums alternate between two buffers,
-    // and a buffer is rewritten only after the next item's barrier, which the
-    // leader passes after reading it
-    float* const s_redp[2] = {s_red0, s_red0 + 2 * 7 * 4 * 64};
-    u32x4 a0[NDW], a1[NDW], sa0, sa1;
-    fetch(gid, a0, sa0);
-    for (int n = 0; n < niter; n += 2) {
-        {
-            const int it = gid + n * ngr;
-            fetch(it + ngr, a1, sa1);
-            f32x4 acc = {0, 0, 0, 0};
-            if (it < nitems) acc = compute(it, a0, sa0, s_redp[0]);
-            __syncthreads();
-            if (it < nitems && wg == 0) finish(it, acc, s_redp[0]);
-        }
-        if (n + 1 < niter) {
-            const int it = gid + (n + 1) * ngr;
-            fetch(it + ngr, a0, sa0);
-            f32x4 acc = {0, 0, 0, 0};
-            if (it < nitems) acc = compute(it, a1, sa1, s_redp[1]);
-            __syncthreads();
-            if (it < nitems && wg == 0) finish(it, acc, s_redp[1]);
-        }
-    }
-}
-
 // ------------------------------------------------ int4 gate/up, decode --
 // One workgroup of 4 waves per (expert, GUD_TPW 16-row tiles of h): wave
 // (t, part) = (gate or up) x (half of K), so a wave holds the 11 weight
@@ -1562,57 +1203,11 @@ __global__ __launch_bounds__(256) void prep_x_int4_kernel(const void* __restrict
     }
 }
 
-#ifndef GU_KS
-#define GU_KS 2
-#endif
-// Persistent decode gate/up: needs the device's CU count and LDS limit.
-struct DevInfo {
-    int cus = 0, max_lds = 0;
-};
-static DevInfo dev_info() {
-    static DevInfo cache[64];
-    int d = 0;
-    if (hipGetDevice(&d) != hipSuccess || d < 0 || d >= 64) return DevInfo{};
-    if (cache[d].cus == 0) {
-        int cus = 0, lds = 0;
-        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, d) != hipSuccess) return DevInfo{};
-        if (hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerBlock, d) != hipSuccess) return DevInfo{};
-        cache[d].max_lds = lds;
-        cache[d].cus = cus;
-    }
-    return cache[d];
-}
-
-// true if the persistent kernel ran (it prepares the activations itself)
-static bool try_gate_up_persist(const FfnParams& P, hipStream_t s) {
-    if (P.fmt != W_INT4 || P.T > GUP_MAX_T || P.H != 2816 || P.FF % 16) return false;
-    const DevInfo di = dev_info();
-    const GupLds L = gup_lds(P.T, P.H, P.E, P.T * P.k);
-    if (di.cus == 0 || L.total > di.max_lds) return false;
-    if (P.x_dt == F32) {
-        static bool attr = false;
-        if (!attr) attr = hipFuncSetAttribute(reinterpret_cast<const void*>(gate_up_int4_persist_kernel<22, F32>),
-                                              hipFuncAttributeMaxDynamicSharedMemorySize, di.max_lds) == hipSuccess;
-        hipLaunchKernelGGL((gate_up_int4_persist_kernel<22, F32>), dim3(di.cus), dim3(1024), L.total, s, P);
-    } else {
-        static bool attr = false;
-        if (!attr) attr = hipFuncSetAttribute(reinterpret_cast<const void*>(gate_up_int4_persist_kernel<22, BF16>),
-                                              hipFuncAttributeMaxDynamicSharedMemorySize, di.max_lds) == hipSuccess;
-        hipLaunchKernelGGL((gate_up_int4_persist_kernel<22, BF16>), dim3(di.cus), dim3(1024), L.total, s, P);
-    }
-    return true;
-}
-
 static void launch_int4(const FfnParams& P, int phases, hipStream_t s) {
     const unsigned tiles_y = (P.T + 15) / 16;
     if (phases & 1) {
         if (P.xq == nullptr) {
-            // activations prepared inside the persistent kernel
-        } else if (P.xsum != nullptr && P.H == 2816) {   // 22 double steps per row, split over GU_KS waves per tile
-            constexpr int KS = GU_KS, NGW = 2 * ((22 + KS - 1) / KS);
-            const size_t smem = (2 * KS * 16 * NGW + (2 * KS - 1) * 4 * 64) * sizeof(float);
-            hipLaunchKernelGGL((gate_up_int4_fast_kernel<22, KS>), dim3(P.E * (P.FF / 16), tiles_y), dim3(128 * KS),
-                               smem, s, P);
+            // the decode kernel has run the first half
         } else if (P.H % 256 == 0 && P.H <= 2816) {   // two K halves of <= 11 double steps, <= 22 groups each
             const int ngw = P.H / 128;
             const size_t smem = (4 * 16 * ngw + 3 * 4 * 64) * sizeof(float);
@@ -1738,18 +1333,11 @@ hipError_t launch_ffn(const FfnParams& P0, int phases, int path, hipStream_t s) 
         launch_int4(P, 2, s);
         return hipGetLastError();
     }
-    if ((phases & 1) && path != 2 && try_gate_up_persist(P, s)) {
-        P.xq = nullptr;   // tells launch_int4 the first half is done
-        if (phases == 1) return hipGetLastError();
-        launch_int4(P, 2, s);
-        return hipGetLastError();
-    }
     if (phases & 1) {
         const bool perm = (P.fmt == W_INT4);
         if (perm || P.x_dt == F32) {
             const int64_t nblk = static_cast<int64_t>(P.T) * P.H / 8;
             const dim3 grid(static_cast<uint32_t>((nblk + 255) / 256)), block(256);
-            if (perm && P.H == 2816) P.xsum = P.xsum_out;   // the int4 fast gate/up path reads group sums
             if (P.x_dt == F32 && perm)
                 hipLaunchKernelGGL((prep_x_int4_kernel<F32>), grid, block, 0, s, P.x, P.T, P.H, P.xq_out, P.xsum);
             else if (P.x_dt == F32)
