@@ -858,59 +858,58 @@ __global__ __launch_bounds__(256) void gate_up_int4_dec_kernel(FfnParams P) {
     constexpr int NSB = (GUD_RT * NDT * 16 + 255) / 256;
     static_assert(GUD_RT == 4, "four route tokens");
     const uint8_t* blob = P.pool + static_cast<uint64_t>(P.slot_of[e]) * P.slot_bytes;
-    const int nb = H / 8;   // blocks per row, a multiple of 16
+    constexpr int HC = 128 * NDT;   // H of this instantiation
+    constexpr int nb = HC / 8;      // blocks per row, a multiple of 16
     int tk0 = P.sorted_route[beg] / P.k, tk1 = P.sorted_route[beg + min(1, end - beg - 1)] / P.k;
     int tk2 = P.sorted_route[beg + min(2, end - beg - 1)] / P.k, tk3 = P.sorted_route[beg + min(3, end - beg - 1)] / P.k;
     u32x4 xr[NSB];
+    // Blocks past the tile's rows are neither read nor converted (nr * nb is
+    // uniform, so the skips are scalar branches).
     auto load_x = [&](int nr) {
 #pragma unroll
         for (int sb = 0; sb < NSB; ++sb) {
+            if (256 * sb >= nr * nb) continue;
             const int i = min(tid + 256 * sb, nr * nb - 1);
             const int j = i / nb, blk = i - j * nb;
             const int tj = j >= 3 ? tk3 : (j == 2 ? tk2 : (j == 1 ? tk1 : tk0));
             if (XT == BF16)
-                xr[sb] = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(P.x) + static_cast<int64_t>(tj) * H +
-                                                         int4_pos_to_k(8 * blk, H));
+                xr[sb] = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(P.x) + static_cast<int64_t>(tj) * HC +
+                                                         int4_pos_to_k(8 * blk, HC));
             else
-                xr[sb] = *reinterpret_cast<const u32x4*>(P.xq + static_cast<int64_t>(tj) * H + 8 * blk);
+                xr[sb] = *reinterpret_cast<const u32x4*>(P.xq + static_cast<int64_t>(tj) * HC + 8 * blk);
         }
     };
     auto store_x = [&](int nr) {
 #pragma unroll
         for (int sb = 0; sb < NSB; ++sb) {
+            if (256 * sb >= nr * nb) continue;
             const int i = tid + 256 * sb;
             const bool ok = i < nr * nb;   // nr * nb is a multiple of 16: whole 16-lane groups agree
             const int ic = min(i, nr * nb - 1), j = ic / nb, blk = ic - j * nb;
             if (XT == BF16) {
-                float v[8];
-#pragma unroll
-                for (int m = 0; m < 4; ++m) {
-                    v[2 * m] = __uint_as_float(xr[sb][m] << 16);
-                    v[2 * m + 1] = __uint_as_float(xr[sb][m] & 0xFFFF0000u);
-                }
-                u32x4 o;
+                // operand dword m = (element m, element m + 4) of the 8 read: a byte permute
+                const u32x4 v = xr[sb];
+                const u32x4 o = {__builtin_amdgcn_perm(v[2], v[0], 0x05040100u), __builtin_amdgcn_perm(v[2], v[0], 0x07060302u),
+                                 __builtin_amdgcn_perm(v[3], v[1], 0x05040100u), __builtin_amdgcn_perm(v[3], v[1], 0x07060302u)};
+                // sum of the 8 bf16 values in fp32
                 float sum = 0.0f;
 #pragma unroll
-                for (int m = 0; m < 4; ++m) {
-                    const uint16_t lo = f32_to_bf16(v[perm8(2 * m)]), hi = f32_to_bf16(v[perm8(2 * m + 1)]);
-                    o[m] = static_cast<uint32_t>(lo) | (static_cast<uint32_t>(hi) << 16);
-                    sum += bf16_to_f32(lo) + bf16_to_f32(hi);
-                }
+                for (int m = 0; m < 4; ++m) sum += __uint_as_float(v[m] << 16) + __uint_as_float(v[m] & 0xFFFF0000u);
                 // the 8 blocks of a 64-group: block indices differing in bits 0, 2, 3
                 sum += __shfl_xor(sum, 1, 64);
                 sum += __shfl_xor(sum, 4, 64);
                 sum += __shfl_xor(sum, 8, 64);
                 if (ok) {
-                    *reinterpret_cast<u32x4*>(xs + j * H + 8 * blk) = o;
+                    *reinterpret_cast<u32x4*>(xs + j * HC + 8 * blk) = o;
                     if ((blk & 13) == 0) {
                         const int gi = j * GS + (blk >> 4) * 2 + ((blk >> 1) & 1);
-                        const uint16_t shi = f32_to_bf16(sum);
-                        xsum[gi] = shi;
-                        xsum[GUD_RT * GS + gi] = f32_to_bf16(sum - bf16_to_f32(shi));
+                        const uint32_t shi = pack_bf16x2(sum, 0.0f) & 0xFFFFu;
+                        xsum[gi] = static_cast<uint16_t>(shi);
+                        xsum[GUD_RT * GS + gi] = static_cast<uint16_t>(pack_bf16x2(sum - __uint_as_float(shi << 16), 0.0f));
                     }
                 }
             } else if (ok) {
-                *reinterpret_cast<u32x4*>(xs + j * H + 8 * blk) = xr[sb];
+                *reinterpret_cast<u32x4*>(xs + j * HC + 8 * blk) = xr[sb];
             }
         }
         if (XT != BF16) {
