@@ -69,6 +69,10 @@ def layer_inputs(seed, L, T, E, H, device, zipf=None):
     return logits, xs
 
 
+def _no_call():
+    return 0
+
+
 class StackRunner:
     """Raw C calls with every argument prepared once (no per-call marshalling)."""
 
@@ -89,9 +93,11 @@ class StackRunner:
         self.calls = []
         for l in range(self.L):
             slot = P(self.slot_d[l])
-            route = (c.moe_route_topk, (P(logits[l]), T, E, k, 1, P(ml.topk_ids), P(ml.topk_w), s))
-            perm = (c.moe_permute, (P(ml.topk_ids), T, k, E, slot, P(ml.offsets), P(ml.sorted_route),
-                                    P(ml.route_pos), P(ml.n_dropped), s))
+            # router top-k and grouping in one call (one launch for T k <= 1024)
+            route = (c.moe_route_permute, (P(logits[l]), T, E, k, 1, slot, P(ml.topk_ids), P(ml.topk_w),
+                                           P(ml.offsets), P(ml.sorted_route), P(ml.route_pos),
+                                           P(ml.n_dropped), s))
+            perm = (_no_call, ())
             ffn_args = (P(pool), sb, slot, E, H, FF, fmt, 0, P(xs[l]), 1, T, k, P(ml.offsets),
                         P(ml.sorted_route), P(ml.out_routes), 0, P(ml.ws), ws, s)
             gu = (c.moe_ffn_gate_up, ffn_args)

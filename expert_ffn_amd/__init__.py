@@ -44,6 +44,7 @@ def lib():
         L.moe_workspace_bytes.restype = sz
         L.moe_route_topk.argtypes = [P, i32, i32, i32, i32, P, P, P]
         L.moe_permute.argtypes = [P, i32, i32, i32, P, P, P, P, P, P]
+        L.moe_route_permute.argtypes = [P, i32, i32, i32, i32, P, P, P, P, P, P, P, P]
         ffn = [P, u64, P, i32, i32, i32, i32, i32, P, i32, i32, i32, P, P, P, i32, P, sz, P]
         for name in ("moe_expert_ffn", "moe_ffn_gate_up", "moe_ffn_down"):
             getattr(L, name).argtypes = ffn
@@ -51,7 +52,7 @@ def lib():
         L.moe_quantize.argtypes = [i32, P, i32, i32, P, P, P]
         L.moe_pack_expert.argtypes = [i32, P, P, i32, i32, P, P]
         L.moe_set_ffn_path.argtypes = [i32]
-        for name in ("moe_blob_layout", "moe_route_topk", "moe_permute", "moe_expert_ffn",
+        for name in ("moe_blob_layout", "moe_route_topk", "moe_permute", "moe_route_permute", "moe_expert_ffn",
                      "moe_ffn_gate_up", "moe_ffn_down", "moe_combine", "moe_quantize",
                      "moe_pack_expert", "moe_set_ffn_path"):
             getattr(L, name).restype = ctypes.c_int
@@ -114,6 +115,14 @@ def permute(topk_ids, E: int, slot_of, expert_offsets, sorted_route, route_pos, 
     T, k = topk_ids.shape
     _check(lib().moe_permute(_ptr(topk_ids), T, k, E, _ptr(slot_of), _ptr(expert_offsets),
                              _ptr(sorted_route), _ptr(route_pos), _ptr(n_dropped), _stream(stream)))
+
+
+def route_permute(logits, k: int, slot_of, topk_ids, topk_w, expert_offsets, sorted_route, route_pos,
+                  n_dropped, renorm: int = 1, stream=None):
+    T, E = logits.shape
+    _check(lib().moe_route_permute(_ptr(logits), T, E, k, renorm, _ptr(slot_of), _ptr(topk_ids), _ptr(topk_w),
+                                   _ptr(expert_offsets), _ptr(sorted_route), _ptr(route_pos), _ptr(n_dropped),
+                                   _stream(stream)))
 
 
 def _ffn(name, pool, slot_bytes, slot_of, E, H, FF, fmt, act, x, T, k, expert_offsets,

@@ -135,6 +135,25 @@ moe_status moe_permute(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E,
                                               route_pos, n_dropped, static_cast<hipStream_t>(stream)));
 }
 
+moe_status moe_route_permute(const float* logits, int32_t T, int32_t E, int32_t k, int32_t renorm,
+                             const int32_t* slot_of, int32_t* topk_ids, float* topk_w, int32_t* expert_offsets,
+                             int32_t* sorted_route, int32_t* route_pos, int32_t* n_dropped, void* stream) {
+    const char* fn = "moe_route_permute";
+    if (!slot_of || !expert_offsets || !n_dropped) return fail(MOE_E_ARG, fn, "null pointer argument");
+    if (T < 0) return fail(MOE_E_SHAPE, fn, "T=%d < 0", T);
+    if (T > 0 && (!logits || !topk_ids || !topk_w || !sorted_route || !route_pos))
+        return fail(MOE_E_ARG, fn, "null pointer argument");
+    if (E < 1 || E > 512) return fail(MOE_E_SHAPE, fn, "E=%d outside [1, 512]", E);
+    if (k < 1 || k > 32 || k > E) return fail(MOE_E_SHAPE, fn, "k=%d outside [1, min(E=%d, 32)]", k, E);
+    if (static_cast<int64_t>(T) * k > (1ll << 30)) return fail(MOE_E_SHAPE, fn, "T*k too large");
+    if (T == 0)   // offsets and the dropped count are still written
+        return hip_status(fn, moe::launch_permute(topk_ids, 0, E, slot_of, expert_offsets, sorted_route, route_pos,
+                                                  n_dropped, static_cast<hipStream_t>(stream)));
+    return hip_status(fn, moe::launch_route_permute(logits, T, E, k, renorm, slot_of, topk_ids, topk_w,
+                                                    expert_offsets, sorted_route, route_pos, n_dropped,
+                                                    static_cast<hipStream_t>(stream)));
+}
+
 static moe_status ffn_entry(const char* fn, int phases, const void* pool, uint64_t slot_bytes,
                             const int32_t* slot_of, int32_t E, int32_t H, int32_t FF, int32_t wfmt,
                             int32_t act, const void* x, int32_t x_dtype, int32_t T, int32_t k,

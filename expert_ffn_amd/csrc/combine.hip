@@ -1,40 +1,67 @@
 // Weighted scatter-combine back to token order (Winery-Strata
 // RemoteExperts::finish; prain README, "Trading quality for speed").
 // One thread per 8 consecutive outputs of a token; the k routes are summed in
-// ascending j in fp32, dropped routes (position -1) skipped.
+// ascending j in fp32, dropped routes (position -1) skipped.  Routes are taken
+// CMB_CH at a time: their positions (uniform, scalar loads) and rows are all
+// requested before the first is added, so a thread waits for one round trip
+// per chunk instead of one per route.
 #include "common.h"
 #include "kernels.h"
 
 namespace moe {
 
+constexpr int CMB_THREADS = 64;
+constexpr int CMB_CH = 8;
+
+template <int OT>
+__device__ __forceinline__ void load_row8(const void* __restrict__ out_routes, int64_t base, u32x4 (&r)[2]) {
+    if (OT == F32) {
+        const u32x4* src = reinterpret_cast<const u32x4*>(static_cast<const float*>(out_routes) + base);
+        r[0] = src[0];
+        r[1] = src[1];
+    } else {
+        r[0] = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(out_routes) + base);
+        r[1] = r[0];
+    }
+}
+
 template <int OT, int YT>
-__global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ out_routes,
-                                                      const float* __restrict__ w,
-                                                      const int* __restrict__ route_pos, int k,
-                                                      int H, void* __restrict__ y) {
+__global__ __launch_bounds__(CMB_THREADS) void combine_kernel(const void* __restrict__ out_routes,
+                                                              const float* __restrict__ w,
+                                                              const int* __restrict__ route_pos, int k,
+                                                              int H, void* __restrict__ y) {
     const int t = blockIdx.x;
-    const int n0 = (blockIdx.y * 256 + threadIdx.x) * 8;
+    const int n0 = (blockIdx.y * CMB_THREADS + threadIdx.x) * 8;
     if (n0 >= H) return;
     float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    for (int j = 0; j < k; ++j) {
-        const int p = route_pos[static_cast<int64_t>(t) * k + j];
-        if (p < 0) continue;
-        const float wj = w[static_cast<int64_t>(t) * k + j];
-        const int64_t base = static_cast<int64_t>(p) * H + n0;
-        if (OT == F32) {
-            const f32x4* src = reinterpret_cast<const f32x4*>(static_cast<const float*>(out_routes) + base);
-            const f32x4 a = src[0], b = src[1];
+    for (int j0 = 0; j0 < k; j0 += CMB_CH) {
+        int pj[CMB_CH];
+        float wj[CMB_CH];
+        u32x4 rows[CMB_CH][2];
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                acc[v] += wj * a[v];
-                acc[4 + v] += wj * b[v];
-            }
-        } else {
-            const u32x4 a = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(out_routes) + base);
+        for (int c = 0; c < CMB_CH; ++c) {
+            const int j = min(j0 + c, k - 1);
+            pj[c] = route_pos[static_cast<int64_t>(t) * k + j];
+            wj[c] = w[static_cast<int64_t>(t) * k + j];
+        }
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                acc[2 * v] += wj * __uint_as_float(a[v] << 16);
-                acc[2 * v + 1] += wj * __uint_as_float(a[v] & 0xFFFF0000u);
+        for (int c = 0; c < CMB_CH; ++c)
+            load_row8<OT>(out_routes, static_cast<int64_t>(max(pj[c], 0)) * H + n0, rows[c]);
+#pragma unroll
+        for (int c = 0; c < CMB_CH; ++c) {
+            if (j0 + c >= k || pj[c] < 0) continue;
+            if (OT == F32) {
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    acc[v] += wj[c] * __uint_as_float(rows[c][0][v]);
+                    acc[4 + v] += wj[c] * __uint_as_float(rows[c][1][v]);
+                }
+            } else {
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    acc[2 * v] += wj[c] * __uint_as_float(rows[c][0][v] << 16);
+                    acc[2 * v + 1] += wj[c] * __uint_as_float(rows[c][0][v] & 0xFFFF0000u);
+                }
             }
         }
     }
@@ -55,7 +82,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ o
 
 hipError_t launch_combine(const void* out_routes, int out_dt, const float* w, const int* route_pos,
                           int T, int k, int H, void* y, int y_dt, hipStream_t s) {
-    const dim3 grid(T, (H / 8 + 255) / 256), block(256);
+    const dim3 grid(T, (H / 8 + CMB_THREADS - 1) / CMB_THREADS), block(CMB_THREADS);
     if (out_dt == F32 && y_dt == F32)
         hipLaunchKernelGGL((combine_kernel<F32, F32>), grid, block, 0, s, out_routes, w, route_pos, k, H, y);
     else if (out_dt == F32)

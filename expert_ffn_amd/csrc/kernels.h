@@ -10,6 +10,10 @@ hipError_t launch_route_topk(const float* logits, int T, int E, int k, int renor
                              float* w, hipStream_t s);
 hipError_t launch_permute(const int* ids, int R, int E, const int* slot_of, int* offsets,
                           int* sorted_route, int* route_pos, int* n_dropped, hipStream_t s);
+// route + permute: one fused launch for T k <= 1024 (and T <= 64), else the two
+hipError_t launch_route_permute(const float* logits, int T, int E, int k, int renorm, const int* slot_of,
+                                int* ids, float* w, int* offsets, int* sorted_route, int* route_pos,
+                                int* n_dropped, hipStream_t s);
 hipError_t launch_combine(const void* out_routes, int out_dt, const float* w, const int* route_pos,
                           int T, int k, int H, void* y, int y_dt, hipStream_t s);
 hipError_t launch_quantize(int fmt, const uint16_t* w, int N, int K, void* q, void* scales,

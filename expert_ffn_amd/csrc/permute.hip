@@ -4,51 +4,69 @@
 // route order; rlx_runtime/expert_pool.rs count_hits is the per-expert
 // histogram.  Here: an LDS histogram (integer atomics; counts do not depend on
 // their order), a wave scan into group offsets, then blocks of 1024 routes in
-// order: each wave finds the lanes sharing its expert with ballots, writes one
-// per-(wave, expert) count, and every route's position is
+// order: each wave finds the lanes sharing its expert with one ballot per bit
+// of the expert id, writes one per-(wave, expert) count, and every route's
+// position is
 //   base[e] + counts of earlier waves in the block + rank among equal lanes.
-// No position depends on thread timing, so the result is deterministic.
+// No position depends on thread timing, so the result is deterministic.  The
+// cross-lane steps use ballots, DPP and lane reads only (no LDS round trips),
+// since the kernel is a chain of short dependent steps.
 #include "common.h"
 #include "kernels.h"
+#include "route.h"
 
 namespace moe {
 
 constexpr int PERM_THREADS = 1024;
 constexpr int PERM_WAVES = PERM_THREADS / 64;
 constexpr int PERM_MAX_E = 512;
+static_assert(PERM_MAX_E <= PERM_THREADS, "one expert per thread at set-up");
 
-__global__ __launch_bounds__(PERM_THREADS) void permute_kernel(
-    const int* __restrict__ ids, int R, int E, const int* __restrict__ slot_of,
-    int* __restrict__ offsets, int* __restrict__ sorted_route, int* __restrict__ route_pos,
-    int* __restrict__ n_dropped) {
-    __shared__ int s_count[PERM_MAX_E];
-    __shared__ int s_base[PERM_MAX_E];
-    __shared__ int s_res[PERM_MAX_E];
-    __shared__ int s_wcnt[PERM_WAVES][PERM_MAX_E];
-    __shared__ int s_drop;
-    __shared__ int s_total;
+// inclusive prefix sum over the 64 lanes of a wave: DPP shifts inside rows of
+// 16, then the totals of the lower rows (lane reads)
+__device__ __forceinline__ int wave_incl_scan(int v) {
+    v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false);   // row_shr:1
+    v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false);   // row_shr:2
+    v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);   // row_shr:4
+    v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false);   // row_shr:8
+    const int r0 = __builtin_amdgcn_readlane(v, 15), r1 = __builtin_amdgcn_readlane(v, 31);
+    const int r2 = __builtin_amdgcn_readlane(v, 47);
+    const int row = (threadIdx.x & 63) >> 4;
+    return v + (row > 0 ? r0 : 0) + (row > 1 ? r1 : 0) + (row > 2 ? r2 : 0);
+}
+
+struct PermLds {
+    int count[PERM_MAX_E];
+    int base[PERM_MAX_E];
+    int res[PERM_MAX_E];
+    int wcnt[PERM_WAVES][PERM_MAX_E];
+    int drop;
+    int total;
+};
+
+// Steps of the grouping for one workgroup of PERM_THREADS threads.  res: is
+// expert tid resident (tid < E); id0: the expert of route tid (tid < R, else
+// -1); routes of later blocks of 1024 are read from ids.
+__device__ __forceinline__ void permute_steps(PermLds& S, const int* __restrict__ ids, int id0, int res, int R,
+                                              int E, int* __restrict__ offsets, int* __restrict__ sorted_route,
+                                              int* __restrict__ route_pos, int* __restrict__ n_dropped) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-
-    for (int e = tid; e < E; e += PERM_THREADS) {
-        s_count[e] = 0;
-        s_res[e] = slot_of[e] >= 0;
-        for (int v = 0; v < PERM_WAVES; ++v) s_wcnt[v][e] = 0;
+    if (tid < E) {
+        S.count[tid] = 0;
+        S.res[tid] = res;
+        for (int v = 0; v < PERM_WAVES; ++v) S.wcnt[v][tid] = 0;
     }
-    if (tid == 0) s_drop = 0;
+    if (tid == 0) S.drop = 0;
     __syncthreads();
 
     // 1. histogram of kept routes, count of dropped ones
-    int mydrop = 0;
-    for (int i = tid; i < R; i += PERM_THREADS) {
-        const int e = ids[i];
-        if (e >= 0 && e < E && s_res[e])
-            atomicAdd(&s_count[e], 1);
-        else
-            ++mydrop;
+    for (int i = tid; i - tid < R; i += PERM_THREADS) {
+        const int e = i == tid ? id0 : (i < R ? ids[i] : -1);
+        const bool keep = e >= 0 && e < E && S.res[e];
+        if (keep) atomicAdd(&S.count[e], 1);
+        const int nd = __popcll(__ballot(i < R && !keep));
+        if (lane == 0 && nd) atomicAdd(&S.drop, nd);
     }
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) mydrop += __shfl_xor(mydrop, m, 64);
-    if (lane == 0 && mydrop) atomicAdd(&s_drop, mydrop);
     __syncthreads();
 
     // 2. exclusive scan of the counts (wave 0, 64 experts per step)
@@ -56,69 +74,120 @@ __global__ __launch_bounds__(PERM_THREADS) void permute_kernel(
         int carry = 0;
         for (int e0 = 0; e0 < E; e0 += 64) {
             const int e = e0 + lane;
-            const int c = e < E ? s_count[e] : 0;
-            int incl = c;
-#pragma unroll
-            for (int d = 1; d < 64; d <<= 1) {
-                const int o = __shfl_up(incl, d, 64);
-                if (lane >= d) incl += o;
-            }
+            const int c = e < E ? S.count[e] : 0;
+            const int incl = wave_incl_scan(c);
             if (e < E) {
-                s_base[e] = carry + incl - c;
+                S.base[e] = carry + incl - c;
                 offsets[e] = carry + incl - c;
             }
-            carry += __shfl(incl, 63, 64);
+            carry += __builtin_amdgcn_readlane(incl, 63);
         }
         if (lane == 0) {
             offsets[E] = carry;
-            s_total = carry;
-            *n_dropped = s_drop;
+            S.total = carry;
+            *n_dropped = S.drop;
         }
     }
     __syncthreads();
 
     // 3. stable positions, one block of 1024 routes at a time
-    const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    const int nbits = E > 1 ? 32 - __clz(E - 1) : 0;   // bits of an expert id
     for (int blk = 0; blk < R; blk += PERM_THREADS) {
         const int i = blk + tid;
         int e = -1;
         if (i < R) {
-            const int v = ids[i];
-            if (v >= 0 && v < E && s_res[v]) e = v;
+            const int v = blk == 0 ? id0 : ids[i];
+            if (v >= 0 && v < E && S.res[v]) e = v;
         }
-        uint64_t peers = 0ull;
-        uint64_t rem = __ballot(e >= 0);
-        while (rem) {
-            const int leader = __ffsll(static_cast<unsigned long long>(rem)) - 1;
-            const int le = __shfl(e, leader, 64);
-            const uint64_t m = __ballot(e == le);
-            if (e == le) peers = m;
-            rem &= ~m;
+        // peers: the lanes of this wave with the same kept expert
+        uint64_t peers = __ballot(e >= 0);
+        for (int bit = 0; bit < nbits; ++bit) {
+            const bool mine = (e >> bit) & 1;
+            const uint64_t bb = __ballot(mine);
+            peers &= mine ? bb : ~bb;
         }
-        const int rank = __popcll(peers & lt_mask);
-        if (e >= 0 && rank == 0) s_wcnt[wave][e] = __popcll(peers);
+        const int rank = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(peers >> 32),
+                                                   __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(peers), 0));
+        if (e >= 0 && rank == 0) S.wcnt[wave][e] = __popcll(peers);
         __syncthreads();
         if (e >= 0) {
-            int pos = s_base[e] + rank;
-            for (int v = 0; v < wave; ++v) pos += s_wcnt[v][e];
+            int pos = S.base[e] + rank;
+            for (int v = 0; v < wave; ++v) pos += S.wcnt[v][e];
             sorted_route[pos] = i;
             route_pos[i] = pos;
         } else if (i < R) {
             route_pos[i] = -1;
         }
-        __syncthreads();
-        for (int ee = tid; ee < E; ee += PERM_THREADS) {
-            int sum = 0;
-            for (int v = 0; v < PERM_WAVES; ++v) {
-                sum += s_wcnt[v][ee];
-                s_wcnt[v][ee] = 0;
+        if (blk + PERM_THREADS < R) {   // set up the next block
+            __syncthreads();
+            for (int ee = tid; ee < E; ee += PERM_THREADS) {
+                int sum = 0;
+                for (int v = 0; v < PERM_WAVES; ++v) {
+                    sum += S.wcnt[v][ee];
+                    S.wcnt[v][ee] = 0;
+                }
+                S.base[ee] += sum;
             }
-            s_base[ee] += sum;
+            __syncthreads();
         }
-        __syncthreads();
     }
     // 4. positions past the kept routes
-    for (int p = s_total + tid; p < R; p += PERM_THREADS) sorted_route[p] = -1;
+    for (int p = S.total + tid; p < R; p += PERM_THREADS) sorted_route[p] = -1;
+}
+
+__global__ __launch_bounds__(PERM_THREADS) void permute_kernel(
+    const int* __restrict__ ids, int R, int E, const int* __restrict__ slot_of,
+    int* __restrict__ offsets, int* __restrict__ sorted_route, int* __restrict__ route_pos,
+    int* __restrict__ n_dropped) {
+    __shared__ PermLds S;
+    const int tid = threadIdx.x;
+    // both inputs requested at once: the residency of expert tid and route tid
+    const int res = tid < E ? (slot_of[tid] >= 0) : 0;
+    const int id0 = tid < R ? ids[tid] : -1;
+    permute_steps(S, ids, id0, res, R, E, offsets, sorted_route, route_pos, n_dropped);
+}
+
+// Router top-k and grouping in one workgroup, for R = T k <= 1024: wave w
+// routes tokens w, w + 16, ...; the ids also go to LDS, and the grouping reads
+// them there, so the two steps cost one launch and no round trip through
+// memory between them.
+template <int NPL>
+__global__ __launch_bounds__(PERM_THREADS) void route_permute_kernel(
+    const float* __restrict__ logits, int T, int E, int k, int renorm, const int* __restrict__ slot_of,
+    int* __restrict__ ids, float* __restrict__ w, int* __restrict__ offsets, int* __restrict__ sorted_route,
+    int* __restrict__ route_pos, int* __restrict__ n_dropped) {
+    __shared__ PermLds S;
+    __shared__ int s_ids[PERM_THREADS];
+    const int tid = threadIdx.x, R = T * k;
+    const int res = tid < E ? (slot_of[tid] >= 0) : 0;
+    for (int t = tid >> 6; t < T; t += PERM_WAVES) route_token<NPL>(logits, t, E, k, renorm, ids, w, s_ids);
+    __syncthreads();
+    const int id0 = tid < R ? s_ids[tid] : -1;
+    permute_steps(S, ids, id0, res, R, E, offsets, sorted_route, route_pos, n_dropped);
+}
+
+hipError_t launch_route_permute(const float* logits, int T, int E, int k, int renorm, const int* slot_of,
+                                int* ids, float* w, int* offsets, int* sorted_route, int* route_pos,
+                                int* n_dropped, hipStream_t s) {
+    if (T * k > PERM_THREADS || T > 4 * PERM_WAVES) {
+        const hipError_t e = launch_route_topk(logits, T, E, k, renorm, ids, w, s);
+        if (e != hipSuccess) return e;
+        return launch_permute(ids, T * k, E, slot_of, offsets, sorted_route, route_pos, n_dropped, s);
+    }
+    const dim3 grid(1), block(PERM_THREADS);
+    if (E <= 64)
+        hipLaunchKernelGGL(route_permute_kernel<1>, grid, block, 0, s, logits, T, E, k, renorm, slot_of, ids, w,
+                           offsets, sorted_route, route_pos, n_dropped);
+    else if (E <= 128)
+        hipLaunchKernelGGL(route_permute_kernel<2>, grid, block, 0, s, logits, T, E, k, renorm, slot_of, ids, w,
+                           offsets, sorted_route, route_pos, n_dropped);
+    else if (E <= 256)
+        hipLaunchKernelGGL(route_permute_kernel<4>, grid, block, 0, s, logits, T, E, k, renorm, slot_of, ids, w,
+                           offsets, sorted_route, route_pos, n_dropped);
+    else
+        hipLaunchKernelGGL(route_permute_kernel<8>, grid, block, 0, s, logits, T, E, k, renorm, slot_of, ids, w,
+                           offsets, sorted_route, route_pos, n_dropped);
+    return hipGetLastError();
 }
 
 hipError_t launch_permute(const int* ids, int R, int E, const int* slot_of, int* offsets,

@@ -1,11 +1,11 @@
 // Router top-k with softmax weights: one wavefront per token.
 //
-// Each lane holds NPL = ceil(E / 64) logits in registers as 64-bit keys
-// (order-preserving image of the logit << 32 | ~expert), so one wave-wide max
-// picks the best remaining expert with the lower id winning ties (the tie rule
-// of rlx_runtime/expert_pool.rs, target_gpu_from_counts).  k rounds of a
-// 6-step butterfly max give the ids in rank order; lanes j < k then compute the
-// softmax weights (prain README, "Trading quality for speed").
+// Each lane holds NPL = ceil(E / 64) logits in registers with their
+// order-preserving 32-bit images.  A round takes the wave maximum of the
+// images (DPP and lane swaps, no LDS) and then the lowest expert id holding it
+// (ballots), which is the tie rule of rlx_runtime/expert_pool.rs
+// (target_gpu_from_counts).  k rounds give the ids in rank order; lanes j < k
+// then compute the softmax weights (prain README, "Trading quality for speed").
 #include "common.h"
 #include "kernels.h"
 #include "route.h"

@@ -130,6 +130,17 @@ moe_status moe_permute(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E,
                        int32_t* route_pos, int32_t* n_dropped, void* stream);
 
 /*
+ * moe_route_topk followed by moe_permute on the same routes, with the same
+ * arguments and results as those two calls (the definitions above).  For
+ * T*k <= 1024 and T <= 64 both run in one workgroup of one launch and the ids
+ * never make a round trip through memory between them; larger T falls back
+ * to the two launches.  topk_ids and topk_w are written as by moe_route_topk.
+ */
+moe_status moe_route_permute(const float* logits, int32_t T, int32_t E, int32_t k, int32_t renorm,
+                             const int32_t* slot_of, int32_t* topk_ids, float* topk_w, int32_t* expert_offsets,
+                             int32_t* sorted_route, int32_t* route_pos, int32_t* n_dropped, void* stream);
+
+/*
  * The expert FFN of every kept route (prain README, "Expert formats": an
  * expert is its w13 and w2; weights are dequantised inside the kernels):
  *   for the route at position p (route i = sorted_route[p], token t = i / k,

@@ -266,6 +266,52 @@ def test_permute_large_and_empty(L):
         assert int(to_np(nd)[0]) == rn
 
 
+@pytest.mark.parametrize("T,E,k,zipf,case", [
+    (16, 128, 8, None, "decode"),          # one launch
+    (1, 128, 8, None, "one-token"),
+    (64, 128, 16, 1.2, "full-block"),     # T k = 1024: still one launch
+    (65, 128, 8, None, "fallback"),       # T > 64: two launches
+    (200, 512, 8, None, "fallback-large"),
+    (37, 7, 3, None, "ragged"),
+    (40, 300, 25, None, "ties-nan"),
+    (0, 16, 4, None, "empty"),
+])
+def test_route_permute_fused(L, T, E, k, zipf, case):
+    """moe_route_permute against the oracle's route_topk + permute (ids, order,
+    offsets bit-exact; weights within 1e-5), with experts not resident."""
+    import expert_ffn_amd as lib
+    import oracle as ora
+    log(f"[case] route_permute {case}: T={T} E={E} k={k} zipf={zipf}")
+    r = np.random.default_rng(T * 1000 + E)
+    logits = synth.logits(5, 0, T, E, zipf) if T else np.zeros((0, E), np.float32)
+    if case == "ties-nan":
+        logits = r.integers(-3, 3, size=(T, E)).astype(np.float32)
+        logits[3, :] = 0.0
+        logits[4, ::2] = -0.0
+        logits[5, 1] = np.nan
+        logits[6, :] = -np.inf
+    so = r.permutation(E).astype(np.int32)
+    so[r.choice(E, max(E // 10, 1), replace=False)] = -1
+    d = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    R = max(T * k, 1)
+    ids = torch.full((max(T, 1), k), -5, dtype=torch.int32, device="cuda")
+    w = torch.empty((max(T, 1), k), dtype=torch.float32, device="cuda")
+    off = torch.full((E + 1,), 7, dtype=torch.int32, device="cuda")
+    sr = torch.empty(R, dtype=torch.int32, device="cuda")
+    rp = torch.empty(R, dtype=torch.int32, device="cuda")
+    nd = torch.full((1,), 9, dtype=torch.int32, device="cuda")
+    lib.route_permute(d(logits).reshape(T, E), k, d(so), ids[:T], w[:T], off, sr[:T * k], rp[:T * k], nd)
+    torch.cuda.synchronize()
+    rid, rw = ora.route_topk(logits, k)
+    ro, rs, rr, rn = ora.permute(rid, E, so)
+    assert np.array_equal(to_np(ids[:T]), rid), "topk ids differ"
+    if T:
+        assert np.nanmax(np.abs(to_np(w[:T]) - rw)) <= 1e-5, "router weights differ"
+    assert np.array_equal(to_np(off), ro), "expert offsets differ"
+    assert np.array_equal(to_np(sr[:T * k]), rs) and np.array_equal(to_np(rp[:T * k]), rr), "order differs"
+    assert int(to_np(nd)[0]) == rn
+
+
 def test_quantize_bit_exact_specials(L):
     import expert_ffn_amd as lib
     import oracle as ora
