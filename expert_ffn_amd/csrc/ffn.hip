@@ -1032,35 +1032,42 @@ __global__ __launch_bounds__(256) void gate_up_int4_dec_kernel(FfnParams P) {
 }
 
 // ------------------------------------------------------ int4 down, decode --
-// One workgroup of 4 waves per (expert, 64 rows of H); a wave owns 16 rows and
-// the whole K = FF (NDS double steps and, when FF % 128 == 64, a tail group).
-// The expert's routes are taken 4 at a time.  The first tile's h rows are
-// requested before the weights (h sits in L2), so waiting for them in the
-// in-order vector load counter does not wait for the weights; all weight
-// fragments and row scales of the wave are then requested at once.
-template <int NDS, bool TAIL>
+// One workgroup of 4 waves per (expert, 64 TPW rows of H); a wave owns TPW
+// tiles of 16 rows and the whole K = FF (NDS double steps and, when
+// FF % 128 == 64, a tail group).  The expert's routes are taken 4 at a time.
+// The first tile's h rows are requested before the weights (h sits in L2), so
+// waiting for them in the in-order vector load counter does not wait for the
+// weights; all weight fragments and row scales of the wave are then requested
+// at once.  More rows per wave keep more bytes in flight per workgroup; the
+// h fragments read from LDS serve every tile of the wave.
+#ifndef DND_TPW
+#define DND_TPW 1
+#endif
+template <int NDS, bool TAIL, int TPW>
 __global__ __launch_bounds__(256) void down_int4_dec_kernel(FfnParams P) {
     constexpr int NG = 2 * NDS + (TAIL ? 1 : 0);   // groups per row
-    constexpr int SPL = (16 * NG + 63) / 64;       // scale values per lane
+    constexpr int SPL = (16 * NG + 63) / 64;       // scale values per lane and tile
     constexpr int RT = GUD_RT;
     __shared__ __attribute__((aligned(16))) uint16_t hs[RT * 128 * (NDS + 1)];   // [RT][FF] bf16
-    __shared__ float s_scs[4][NG * 16];
+    __shared__ float s_scs[4][TPW][NG * 16];
     const int FF = P.FF;
-    const int nblk = P.H >> 6;
+    const int nblk = P.H / (64 * TPW);
     const int e = blockIdx.x / nblk, blk = blockIdx.x - e * nblk;
     const int beg = P.offsets[e], end = P.offsets[e + 1];
     if (beg >= end) return;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r = lane & 15, q = lane >> 4;
     const uint8_t* blob = P.pool + static_cast<uint64_t>(P.slot_of[e]) * P.slot_bytes;   // scalar, first
-    const int m0 = blk * 64 + wave * 16;
-    float* s_sc = s_scs[wave];
+    const int m0 = (blk * 4 + wave) * 16 * TPW;   // first row of the wave; tile tt is rows m0 + 16 tt
     constexpr int NHB = (RT * 128 * (NDS + 1) / 8 + 255) / 256;   // blocks of 8 per thread (upper bound)
     const int nbr = FF / 8;                                         // blocks per h row
 
+    // blocks past the tile's rows are neither read nor stored (nr * nbr is
+    // uniform, so the skips are scalar branches)
     u32x4 hr[NHB];
     auto load_h = [&](int rt, int nr) {
 #pragma unroll
         for (int sb = 0; sb < NHB; ++sb) {
+            if (256 * sb >= nr * nbr) continue;
             const int i = min(tid + 256 * sb, nr * nbr - 1);
             const int j = i / nbr, c = i - j * nbr;
             hr[sb] = *reinterpret_cast<const u32x4*>(P.h + static_cast<int64_t>(rt + j) * FF + 8 * c);
@@ -1069,6 +1076,7 @@ __global__ __launch_bounds__(256) void down_int4_dec_kernel(FfnParams P) {
     auto store_h = [&](int nr) {
 #pragma unroll
         for (int sb = 0; sb < NHB; ++sb) {
+            if (256 * sb >= nr * nbr) continue;
             const int i = tid + 256 * sb;
             if (i < nr * nbr) {
                 const int j = i / nbr, c = i - j * nbr;
@@ -1079,62 +1087,82 @@ __global__ __launch_bounds__(256) void down_int4_dec_kernel(FfnParams P) {
     const int nr0 = min(RT, end - beg);
     load_h(beg, nr0);
 
-    // weights of the wave's 16 rows, and their scales
-    const uint8_t* a_row = blob + P.o2 + static_cast<int64_t>(m0 + r) * (FF / 2);
-    u32x4 a[NDS];
+    // weights of the wave's TPW tiles of 16 rows, and their scales
+    u32x4 a[TPW][NDS];
+    u32x2 at[TPW];
+    float sv[TPW][SPL];
 #pragma unroll
-    for (int i = 0; i < NDS; ++i) a[i] = *reinterpret_cast<const u32x4*>(a_row + 64 * i + 16 * q);
-    u32x2 at = {0u, 0u};
-    if (TAIL) at = *reinterpret_cast<const u32x2*>(a_row + 64 * NDS + 8 * q);
-    float sv[SPL];
+    for (int tt = 0; tt < TPW; ++tt) {
+        const uint8_t* a_row = blob + P.o2 + static_cast<int64_t>(m0 + 16 * tt + r) * (FF / 2);
+#pragma unroll
+        for (int i = 0; i < NDS; ++i) a[tt][i] = *reinterpret_cast<const u32x4*>(a_row + 64 * i + 16 * q);
+        at[tt] = u32x2{0u, 0u};
+        if (TAIL) at[tt] = *reinterpret_cast<const u32x2*>(a_row + 64 * NDS + 8 * q);
+    }
     {
         const uint16_t* sc = reinterpret_cast<const uint16_t*>(blob + P.os2);
 #pragma unroll
-        for (int m = 0; m < SPL; ++m) {
-            const int idx = min(lane + 64 * m, 16 * NG - 1);
-            const int i = idx / NG, g = idx - i * NG;
-            sv[m] = bf16_to_f32(sc[static_cast<int64_t>(m0 + i) * NG + g]);
-        }
+        for (int tt = 0; tt < TPW; ++tt)
+#pragma unroll
+            for (int m = 0; m < SPL; ++m) {
+                const int idx = min(lane + 64 * m, 16 * NG - 1);
+                const int i = idx / NG, g = idx - i * NG;
+                sv[tt][m] = bf16_to_f32(sc[static_cast<int64_t>(m0 + 16 * tt + i) * NG + g]);
+            }
     }
 
     auto compute_tile = [&](int rt, int nr) {
         const int slot = r & (RT - 1);
         const uint16_t* hrow = hs + slot * FF + 32 * q;
-        f32x4 acc = {0, 0, 0, 0};
+        f32x4 acc[TPW];
+#pragma unroll
+        for (int tt = 0; tt < TPW; ++tt) acc[tt] = f32x4{0, 0, 0, 0};
 #pragma unroll
         for (int i = 0; i < NDS; ++i) {
             u32x4 b[4];
 #pragma unroll
             for (int m = 0; m < 4; ++m) b[m] = *reinterpret_cast<const u32x4*>(hrow + 128 * i + 8 * m);
-            const u32x4 v = regroup(a[i]);
-            int4_group(v[0], v[1], b[0], b[1], *reinterpret_cast<const f32x4*>(s_sc + (2 * i) * 16 + 4 * q), acc);
-            int4_group(v[2], v[3], b[2], b[3], *reinterpret_cast<const f32x4*>(s_sc + (2 * i + 1) * 16 + 4 * q), acc);
+#pragma unroll
+            for (int tt = 0; tt < TPW; ++tt) {
+                const float* s_sc = &s_scs[wave][tt][0];
+                const u32x4 v = regroup(a[tt][i]);
+                int4_group(v[0], v[1], b[0], b[1], *reinterpret_cast<const f32x4*>(s_sc + (2 * i) * 16 + 4 * q), acc[tt]);
+                int4_group(v[2], v[3], b[2], b[3], *reinterpret_cast<const f32x4*>(s_sc + (2 * i + 1) * 16 + 4 * q), acc[tt]);
+            }
         }
         if (TAIL) {
             const uint16_t* tr = hs + slot * FF + 128 * NDS + 16 * q;
             const u32x4 b0 = *reinterpret_cast<const u32x4*>(tr), b1 = *reinterpret_cast<const u32x4*>(tr + 8);
-            int4_group(at[0], at[1], b0, b1, *reinterpret_cast<const f32x4*>(s_sc + 2 * NDS * 16 + 4 * q), acc);
+#pragma unroll
+            for (int tt = 0; tt < TPW; ++tt)
+                int4_group(at[tt][0], at[tt][1], b0, b1, *reinterpret_cast<const f32x4*>(&s_scs[wave][tt][0] + 2 * NDS * 16 + 4 * q),
+                           acc[tt]);
         }
         if (r < nr) {
-            const int64_t o = static_cast<int64_t>(rt + r) * P.H + m0 + 4 * q;
-            if (P.out_dt == F32) {
-                *reinterpret_cast<f32x4*>(static_cast<float*>(P.out) + o) = acc;
-            } else {
-                *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(P.out) + o) =
-                    u32x2{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
+#pragma unroll
+            for (int tt = 0; tt < TPW; ++tt) {
+                const int64_t o = static_cast<int64_t>(rt + r) * P.H + m0 + 16 * tt + 4 * q;
+                if (P.out_dt == F32) {
+                    *reinterpret_cast<f32x4*>(static_cast<float*>(P.out) + o) = acc[tt];
+                } else {
+                    *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(P.out) + o) =
+                        u32x2{pack_bf16x2(acc[tt][0], acc[tt][1]), pack_bf16x2(acc[tt][2], acc[tt][3])};
+                }
             }
         }
     };
 
     store_h(nr0);
 #pragma unroll
-    for (int m = 0; m < SPL; ++m) {
-        const int idx = lane + 64 * m;
-        if (idx < 16 * NG) {
-            const int i = idx / NG, g = idx - i * NG;
-            s_sc[g * 16 + i] = sv[m];
+    for (int tt = 0; tt < TPW; ++tt)
+#pragma unroll
+        for (int m = 0; m < SPL; ++m) {
+            const int idx = lane + 64 * m;
+            if (idx < 16 * NG) {
+                const int i = idx / NG, g = idx - i * NG;
+                s_scs[wave][tt][g * 16 + i] = sv[tt][m];
+            }
         }
-    }
     __syncthreads();
     compute_tile(beg, nr0);
     for (int rt = beg + RT; rt < end; rt += RT) {
@@ -1220,7 +1248,10 @@ static void launch_int4(const FfnParams& P, int phases, hipStream_t s) {
     if (phases & 2) {
         const size_t smem = 4 * 16 * (P.FF / 64) * sizeof(float);
         if (P.FF == 704) {   // decode: 5 double steps and a tail group
-            hipLaunchKernelGGL((down_int4_dec_kernel<5, true>), dim3(P.E * (P.H / 64)), dim3(256), 0, s, P);
+            if (P.H % (64 * DND_TPW) == 0)
+                hipLaunchKernelGGL((down_int4_dec_kernel<5, true, DND_TPW>), dim3(P.E * (P.H / (64 * DND_TPW))), dim3(256), 0, s, P);
+            else
+                hipLaunchKernelGGL((down_int4_dec_kernel<5, true, 1>), dim3(P.E * (P.H / 64)), dim3(256), 0, s, P);
             return;
         }
         if (P.FF <= 704)   // <= 5 double steps and a tail, <= 11 groups
