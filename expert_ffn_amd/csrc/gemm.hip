@@ -47,7 +47,9 @@ __host__ __device__ __forceinline__ int m32_pos(int f) {
 }
 
 constexpr int GM_ROWS = 128;   // routes per tile
-constexpr int GM_XBUF = 32768; // one LDS stage: [2 groups][4 K steps][4 route blocks] x 1 KB
+constexpr int GM_GBUF = 16384; // one group of a stage: [4 K steps][4 route blocks] x 1 KB
+// A workgroup of NW waves (4 or 8): wave (mh, nq), NQ = NW / 2 column blocks
+// per narrow tile; a stage holds NW / 4 groups.
 
 // ---------------------------------------------------------------- prep ----
 // x [T, H] (fp32 or bf16) -> xq [T, H] bf16 in M32 operand order, and the
@@ -110,45 +112,51 @@ __global__ __launch_bounds__(256) void prep_x_m32_kernel(const void* __restrict_
 //         and the group sums of h (bf16 hi + lo) for the second half.
 // MODE 1: down.  K = FF.  N tile = 256 rows of w2; wave nq owns rows
 //         n0 + 64 nq + 32 nb + c.  Epilogue: the route rows of out (fp32/bf16).
-template <int MODE>
+template <int MODE, int NW>
 struct GemmShape {
     int K, G, GP, NC, NT, nrows, gp_a;
 };
 
-template <int MODE>
-__device__ __forceinline__ GemmShape<MODE> gemm_shape(const FfnParams& P) {
-    GemmShape<MODE> S;
+template <int MODE, int NW>
+__device__ __forceinline__ GemmShape<MODE, NW> gemm_shape(const FfnParams& P) {
+    constexpr int NQ = NW / 2, SG = NW / 4;
+    GemmShape<MODE, NW> S;
     S.K = MODE == 0 ? P.H : P.FF;
     S.G = S.K / 64;
     S.GP = (S.G + 15) & ~15;
-    S.NC = (S.G + 1) / 2;
-    S.NT = MODE == 0 ? (P.FF + 127) / 128 : (P.H + 255) / 256;
+    S.NC = (S.G + SG - 1) / SG;
+    S.NT = MODE == 0 ? (P.FF + 32 * NQ - 1) / (32 * NQ) : (P.H + 64 * NQ - 1) / (64 * NQ);
     S.nrows = MODE == 0 ? 2 * P.FF : P.H;   // rows of the weight matrix
     return S;
 }
 
-__host__ __device__ inline size_t gemm_lds_bytes(int E, int G) {
-    return 2 * GM_XBUF + static_cast<size_t>(512) * G * 2 + 16 + static_cast<size_t>(E + 1) * 4;
+__host__ __device__ inline size_t gemm_lds_bytes(int E, int G, int NW) {
+    return 2 * static_cast<size_t>(NW / 4) * GM_GBUF + static_cast<size_t>(64 * NW) * G * 2 + 16 +
+           static_cast<size_t>(E + 1) * 4;
 }
 
-template <int MODE, int DC>
-__global__ __launch_bounds__(512) void ffn_int4_gemm_kernel(FfnParams P) {
+template <int MODE, int DC, int NW>
+__global__ __launch_bounds__(64 * NW, 8 / NW) void ffn_int4_gemm_kernel(FfnParams P) {
+    constexpr int NQ = NW / 2;                      // column blocks of a narrow tile
+    constexpr int SG = NW / 4;                      // groups per stage
+    constexpr int XBUF = SG * GM_GBUF;              // bytes of one stage
+    constexpr int NTH = 64 * NW;                    // threads
     constexpr int D = 2 * DC;                       // weight groups in flight per wave
-    constexpr int U = (DC % 2 == 0) ? DC : 2 * DC;  // chunks per unrolled body: multiple of DC and of 2
+    constexpr int U = (D / SG) > 2 ? (D / SG) : 2;  // chunks per unrolled body: static slots and stage parity
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-    const GemmShape<MODE> S = gemm_shape<MODE>(P);
+    const GemmShape<MODE, NW> S = gemm_shape<MODE, NW>(P);
     const int E = P.E, G = S.G, GP = S.GP, NC = S.NC, NT = S.NT;
-    uint8_t* xbuf = lds;                                                   // [2][GM_XBUF]
-    uint16_t* ssc = reinterpret_cast<uint16_t*>(lds + 2 * GM_XBUF);        // [512][G] bf16 scales of the tile
-    int* pre = reinterpret_cast<int*>(lds + 2 * GM_XBUF + ((512 * G * 2 + 15) & ~15));   // [E+1]
+    uint8_t* xbuf = lds;                                                   // [2][XBUF]
+    uint16_t* ssc = reinterpret_cast<uint16_t*>(lds + 2 * XBUF);           // [NTH][G] bf16 scales of the tile
+    int* pre = reinterpret_cast<int*>(lds + 2 * XBUF + ((NTH * G * 2 + 15) & ~15));   // [E+1]
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, c32 = lane & 31, hh = lane >> 5;
-    const int mh = wave >> 2, nq = wave & 3;
+    const int mh = wave / NQ, nq = wave % NQ;
 
     // Items per expert -> prefix sums (wave 0).  An expert with at most 64
     // routes is one "wide" row tile: the two wave halves take different
     // columns (an N tile twice as wide), so that both waves of each SIMD work.
     // Larger groups take 128-route tiles, the halves splitting the routes.
-    const int NTW = MODE == 0 ? (P.FF + 255) / 256 : (P.H + 511) / 512;
+    const int NTW = MODE == 0 ? (P.FF + 32 * NW - 1) / (32 * NW) : (P.H + 64 * NW - 1) / (64 * NW);
     if (wave == 0) {
         int run = 0;
         for (int e0 = 0; e0 < E; e0 += 64) {
@@ -188,16 +196,16 @@ __global__ __launch_bounds__(512) void ffn_int4_gemm_kernel(FfnParams P) {
         const int beg = P.offsets[e] + GM_ROWS * mt;
         const int end = min(P.offsets[e + 1], beg + GM_ROWS);
         const uint8_t* blob = P.pool + static_cast<uint64_t>(P.slot_of[e]) * P.slot_bytes;
-        const int n0 = (MODE == 0 ? 128 : 256) * nw * nt;
+        const int n0 = (MODE == 0 ? 32 * NQ : 64 * NQ) * nw * nt;
         const int nsub = wide ? wave : nq;                  // this wave's column block of the tile
         const int mbase = wide ? 0 : 64 * mh;               // this wave's first route row of the tile
 
         // ---- scales of the tile's 256 rows -> LDS (16-byte copies; rows past the matrix read as 0)
         {
             const uint8_t* sblk = blob + o_scales;
-            const int half = (MODE == 0 ? 128 : 256) * nw * G * 2;    // bytes of one contiguous row run
+            const int half = (MODE == 0 ? 32 * NQ : 64 * NQ) * nw * G * 2;    // bytes of one contiguous row run
             const int nruns = MODE == 0 ? 2 : 1;
-            for (int i = tid; i < nruns * half / 16; i += 512) {
+            for (int i = tid; i < nruns * half / 16; i += NTH) {
                 const int run = i / (half / 16), o = (i - run * (half / 16)) * 16;
                 const int r0 = MODE == 0 ? run * P.FF + n0 : n0;            // first matrix row of the run
                 const int64_t src = static_cast<int64_t>(r0) * G * 2 + o;
@@ -216,7 +224,7 @@ __global__ __launch_bounds__(512) void ffn_int4_gemm_kernel(FfnParams P) {
             if (MODE == 0) {
                 const int n = min(n0 + 32 * nsub + c32, P.FF - 1);
                 wrow[nb] = nb * P.FF + n;
-                lrow[nb] = 128 * nw * nb + 32 * nsub + c32;
+                lrow[nb] = 32 * NQ * nw * nb + 32 * nsub + c32;
             } else {
                 wrow[nb] = min(n0 + 64 * nsub + 32 * nb + c32, P.H - 1);
                 lrow[nb] = 64 * nsub + 32 * nb + c32;
@@ -238,14 +246,14 @@ __global__ __launch_bounds__(512) void ffn_int4_gemm_kernel(FfnParams P) {
             aoff[mb4] = ok ? static_cast<uint32_t>((r * arow_stride + 16 * ss + 8 * hh) * 2) : NO_LANE;
         }
         auto load_stage = [&](int c, u32x4* xr) {
-            const uint32_t g = static_cast<uint32_t>(min(2 * c + sgi, G - 1)) * 128;
+            const uint32_t g = static_cast<uint32_t>(min(SG * c + sgi, G - 1)) * 128;
 #pragma unroll
             for (int mb4 = 0; mb4 < 4; ++mb4) xr[mb4] = bload16(ares, aoff[mb4] + g);
         };
         auto store_stage = [&](int buf, const u32x4* xr) {
 #pragma unroll
             for (int mb4 = 0; mb4 < 4; ++mb4)
-                *reinterpret_cast<u32x4*>(xbuf + buf * GM_XBUF + ((sgi * 4 + ss) * 4 + mb4) * 1024 + lane * 16) = xr[mb4];
+                *reinterpret_cast<u32x4*>(xbuf + buf * XBUF + ((sgi * 4 + ss) * 4 + mb4) * 1024 + lane * 16) = xr[mb4];
         };
 
         // Load order = order of need, as in the K loop below (stage c + 1, then
@@ -318,7 +326,7 @@ __global__ __launch_bounds__(512) void ffn_int4_gemm_kernel(FfnParams P) {
 #pragma unroll
             for (int cu = 0; cu < U; ++cu) {
                 const int c = c0 + cu;
-                const uint8_t* xb = xbuf + (cu & 1) * GM_XBUF;
+                const uint8_t* xb = xbuf + (cu & 1) * XBUF;
                 // stage c + 1 (loaded one chunk ago) into the other buffer, whose
                 // readers finished at the last barrier; then start stage c + 2,
                 // ahead of this chunk's weight loads so that the in-order load
@@ -327,9 +335,9 @@ __global__ __launch_bounds__(512) void ffn_int4_gemm_kernel(FfnParams P) {
                 load_stage(min(c + 2, NC - 1), xr);
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                for (int gi = 0; gi < 2; ++gi) {
-                    const int g = 2 * c + gi;
-                    const int slot = (2 * cu + gi) % D;
+                for (int gi = 0; gi < SG; ++gi) {
+                    const int g = SG * c + gi;
+                    const int slot = (SG * cu + gi) % D;
                     if (nact && mact && g < G) {
                         // K steps software-pipelined: the next step's activation
                         // fragments are read and its weights expanded while this
@@ -388,7 +396,7 @@ __global__ __launch_bounds__(512) void ffn_int4_gemm_kernel(FfnParams P) {
         if (MODE == 0) {
             // [128 / nw routes][128 nw columns] bf16, M32 order inside each 64-group
             uint16_t* tile = reinterpret_cast<uint16_t*>(xbuf);
-            const int tw = 128 * nw;
+            const int tw = 32 * NQ * nw;
             if (nact && mact) {
 #pragma unroll
                 for (int mb = 0; mb < 2; ++mb)
@@ -402,15 +410,15 @@ __global__ __launch_bounds__(512) void ffn_int4_gemm_kernel(FfnParams P) {
             }
             __syncthreads();
             const int ncol = min(tw, P.FF - n0);
-            for (int i = tid; i < GM_ROWS * 16; i += 512) {
-                const int r = i / (16 * nw), c8 = i - r * (16 * nw);
+            for (int i = tid; i < 512 * NQ; i += NTH) {   // (128 / nw rows) x (tw / 8 blocks)
+                const int r = i / (4 * NQ * nw), c8 = i - r * (4 * NQ * nw);
                 if (beg + r < end && 8 * c8 < ncol)
                     *reinterpret_cast<u32x4*>(P.h + static_cast<int64_t>(beg + r) * P.FF + n0 + 8 * c8) =
                         *reinterpret_cast<const u32x4*>(tile + r * tw + 8 * c8);
             }
             {
                 // group sums of the stored h: 2 threads per (route row, 64-group)
-                const int pr = tid >> 1, hf = tid & 1, r = pr / (2 * nw), gg = pr - r * (2 * nw);
+                const int pr = tid >> 1, hf = tid & 1, r = pr / (NQ * nw / 2), gg = pr - r * (NQ * nw / 2);
                 float sum = 0.0f;
                 const uint16_t* src = tile + r * tw + 64 * gg + 32 * hf;
 #pragma unroll
@@ -453,6 +461,9 @@ bool int4_gemm_eligible(const FfnParams& P) {
     return P.fmt == W_INT4 && P.H % 64 == 0 && P.FF % 64 == 0 && P.E <= 4096;
 }
 
+#ifndef GEMM_NW
+#define GEMM_NW 4
+#endif
 hipError_t launch_int4_gemm(const FfnParams& P0, int phases, hipStream_t s) {
     FfnParams P = P0;
     int dev = 0, cus = 0, maxlds = 0;
@@ -460,7 +471,10 @@ hipError_t launch_int4_gemm(const FfnParams& P0, int phases, hipStream_t s) {
     if (err != hipSuccess) return err;
     if ((err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return err;
     if ((err = hipDeviceGetAttribute(&maxlds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev)) != hipSuccess) return err;
-    constexpr int DC = 2;
+    constexpr int DC = 2, NW = GEMM_NW;
+    // persistent: 8 waves per CU, as one workgroup of 8 or two of 4 (which then
+    // run out of step with each other)
+    const dim3 grid(static_cast<uint32_t>(cus * (8 / NW))), block(64 * NW);
     if (phases & 1) {
         const int64_t nblk = static_cast<int64_t>(P.T) * P.H / 8;
         P.xq = P.xq_out;
@@ -471,22 +485,22 @@ hipError_t launch_int4_gemm(const FfnParams& P0, int phases, hipStream_t s) {
         else
             hipLaunchKernelGGL((prep_x_m32_kernel<BF16>), dim3(static_cast<uint32_t>((nblk + 255) / 256)), dim3(256), 0, s,
                                P.x, P.T, P.H, P.xq_out, reinterpret_cast<uint16_t*>(P.xsum_out));
-        const size_t lds = gemm_lds_bytes(P.E, P.H / 64);
+        const size_t lds = gemm_lds_bytes(P.E, P.H / 64, NW);
         if (static_cast<int>(lds) > maxlds) return hipErrorInvalidConfiguration;
         static bool attr = false;
         if (!attr)
-            attr = hipFuncSetAttribute(reinterpret_cast<const void*>(ffn_int4_gemm_kernel<0, DC>),
+            attr = hipFuncSetAttribute(reinterpret_cast<const void*>(ffn_int4_gemm_kernel<0, DC, NW>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, maxlds) == hipSuccess;
-        hipLaunchKernelGGL((ffn_int4_gemm_kernel<0, DC>), dim3(cus), dim3(512), lds, s, P);
+        hipLaunchKernelGGL((ffn_int4_gemm_kernel<0, DC, NW>), grid, block, lds, s, P);
     }
     if (phases & 2) {
-        const size_t lds = gemm_lds_bytes(P.E, P.FF / 64);
+        const size_t lds = gemm_lds_bytes(P.E, P.FF / 64, NW);
         if (static_cast<int>(lds) > maxlds) return hipErrorInvalidConfiguration;
         static bool attr = false;
         if (!attr)
-            attr = hipFuncSetAttribute(reinterpret_cast<const void*>(ffn_int4_gemm_kernel<1, DC>),
+            attr = hipFuncSetAttribute(reinterpret_cast<const void*>(ffn_int4_gemm_kernel<1, DC, NW>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, maxlds) == hipSuccess;
-        hipLaunchKernelGGL((ffn_int4_gemm_kernel<1, DC>), dim3(cus), dim3(512), lds, s, P);
+        hipLaunchKernelGGL((ffn_int4_gemm_kernel<1, DC, NW>), grid, block, lds, s, P);
     }
     return hipGetLastError();
 }
