@@ -183,7 +183,16 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void ffn_int4_gemm_kernel(FfnParam
     const uint16_t* asum = MODE == 0 ? reinterpret_cast<const uint16_t*>(P.xsum) : P.hsum;
     const int asum_rows = MODE == 0 ? P.T : P.T * P.k;
 
-    for (int item = blockIdx.x; item < nitems; item += gridDim.x) {
+    // XCD-aware order: workgroups are dealt to the 8 XCDs round robin, so the
+    // workgroups of one XCD (blockIdx % 8) take one contiguous eighth of the
+    // item list.  An expert's N tiles then run on one XCD and its activation
+    // rows are fetched into that XCD's L2 once.  (A mapping that differs only
+    // costs locality, not correctness: every item is still taken once.)
+    const int nxcd = gridDim.x % 8 == 0 ? 8 : 1;
+    const int xcd = blockIdx.x % nxcd, wpx = gridDim.x / nxcd, wj = blockIdx.x / nxcd;
+    const int ibeg = static_cast<int>(static_cast<int64_t>(nitems) * xcd / nxcd);
+    const int iend = static_cast<int>(static_cast<int64_t>(nitems) * (xcd + 1) / nxcd);
+    for (int item = ibeg + wj; item < iend; item += wpx) {
         int lo = 0, hi = E;   // largest e with pre[e] <= item
         while (hi - lo > 1) {
             const int mid = (lo + hi) >> 1;
