@@ -280,6 +280,58 @@ def cpu_baseline(seed, T, budget_s=20.0):
                        f"scaled x30 to the stack step")
 
 
+def measure_configs(lib, dev, seed, copies=4, reps=20):
+    """Single-layer timings of the other Gemma-shaped workloads (bf16 decode
+    T = 1, 4, 16, 64; int8 decode T = 16 with Zipf routing; int4 prefill
+    T = 1024, uniform and Zipf).  Each runs over `copies` independently packed
+    copies of the layer, in turn, so that the weights come from HBM and not
+    from the 256 MB last-level cache; a replay of one graph per copy round."""
+    import torch
+    E, k, H, FF = G["E"], G["k"], G["H"], G["FF"]
+    cases = [("bf16_decode", lib.W_BF16, T, None) for T in (1, 4, 16, 64)]
+    cases += [("int8_decode_zipf", lib.W_INT8_ROW, 16, 1.1),
+              ("int4_prefill", lib.W_INT4_G64, 1024, None), ("int4_prefill_zipf", lib.W_INT4_G64, 1024, 1.1)]
+    out, built = [], {}
+    stream = torch.cuda.Stream()
+    for name, fmt, T, zipf in cases:
+        if fmt not in built:
+            built.clear()
+            torch.cuda.empty_cache()
+            log(f"packing {copies} copies of the layer as format {fmt} ...")
+            built[fmt] = build_stack(lib, seed + 11, copies, E, H, FF, fmt, dev)
+        pool, sb, slots = built[fmt]
+        logits, xs = layer_inputs(seed + 13, copies, T, E, H, dev, zipf)
+        with torch.cuda.stream(stream):
+            run = StackRunner(lib, pool, sb, slots, T, E, k, H, FF, fmt, logits, xs, stream)
+            routing = realised_routing(lib, run, logits)
+            for _ in range(3):
+                run.step()
+            torch.cuda.synchronize()
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph, stream=stream):
+                run.step()
+            graph.replay()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(reps):
+                graph.replay()
+            torch.cuda.synchronize()
+            us = (time.perf_counter() - t0) / (reps * copies) * 1e6
+            del graph, run
+        distinct = float(np.mean([d for d, _ in routing]))
+        kept = float(np.mean([r for _, r in routing]))
+        byts = distinct * sb + 2 * T * H * 2 + T * E * 4 + T * k * 16
+        flops = kept * 6.0 * H * FF
+        out.append(dict(config=name, weights=["bf16", "int8_row", "int4_g64"][fmt], T=T, zipf=zipf,
+                        us_per_layer=round(us, 2), tokens_per_s=round(T / (us * 1e-6), 1),
+                        distinct_experts=round(distinct, 1), hbm_gbs=round(byts / (us * 1e-6) / 1e9, 1),
+                        hbm_frac=round(byts / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                        mfma_tflops=round(flops / (us * 1e-6) / 1e12, 1),
+                        mfma_frac=round(flops / (us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)))
+        log(json.dumps(out[-1]))
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -297,6 +349,9 @@ def main():
     ap.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_DIR", "DEST"),
                     help="write a kernel-trace summary from a rocprofv3 run (no GPU)")
     ap.add_argument("--command", default="", help="the profiled command, recorded in summaries")
+    ap.add_argument("--configs", action="store_true",
+                    help="instead of the stack step: single-layer timings of the other workloads "
+                         "(one JSON object per line)")
     args = ap.parse_args()
     if args.summarize_pmc:
         summarize_pmc(*args.summarize_pmc, commands=args.command)
@@ -314,6 +369,10 @@ def main():
     import expert_ffn_amd as lib
     lib.lib()
     dev = torch.device("cuda:0")
+    if args.configs:
+        for r in measure_configs(lib, dev, args.seed):
+            print(json.dumps(r), flush=True)
+        return
     E, k, H, FF = G["E"], G["k"], G["H"], G["FF"]
     fmt = lib.W_INT4_G64
     T = args.tokens
