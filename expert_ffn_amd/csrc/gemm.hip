@@ -46,7 +46,13 @@ __host__ __device__ __forceinline__ int m32_pos(int f) {
     return 16 * s + 8 * h + (((e & 3) << 1) | (e >> 2));   // slot j with perm8(j) = e
 }
 
-constexpr int GM_ROWS = 128;   // routes per tile
+constexpr int GM_ROWS = 128;   // routes per narrow tile
+// Groups of at most GEMM_WIDE_MAX routes take wide tiles (64 routes, an N
+// tile twice as wide: half the activation traffic per weight byte); larger
+// ones take 128-route narrow tiles.
+#ifndef GEMM_WIDE_MAX
+#define GEMM_WIDE_MAX 64
+#endif
 constexpr int GM_GBUF = 16384; // one group of a stage: [4 K steps][4 route blocks] x 1 KB
 // A workgroup of NW waves (4 or 8): wave (mh, nq), NQ = NW / 2 column blocks
 // per narrow tile; a stage holds NW / 4 groups.
@@ -162,7 +168,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void ffn_int4_gemm_kernel(FfnParam
         for (int e0 = 0; e0 < E; e0 += 64) {
             const int e = e0 + lane;
             const int me = e < E ? P.offsets[e + 1] - P.offsets[e] : 0;
-            const int cnt = me == 0 ? 0 : (me <= 64 ? NTW : (me + GM_ROWS - 1) / GM_ROWS * NT);
+            const int cnt = me == 0 ? 0 : (me <= GEMM_WIDE_MAX ? (me + 63) / 64 * NTW : (me + GM_ROWS - 1) / GM_ROWS * NT);
             int incl = cnt;
 #pragma unroll
             for (int d = 1; d < 64; d <<= 1) {
@@ -199,11 +205,12 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void ffn_int4_gemm_kernel(FfnParam
             if (pre[mid] <= item) lo = mid; else hi = mid;
         }
         const int e = lo, li = item - pre[e];
-        const bool wide = P.offsets[e + 1] - P.offsets[e] <= 64;
+        const bool wide = P.offsets[e + 1] - P.offsets[e] <= GEMM_WIDE_MAX;
         const int nw = wide ? 2 : 1;                        // N tile width in narrow tiles
-        const int mt = wide ? 0 : li / NT, nt = wide ? li : li - (li / NT) * NT;
-        const int beg = P.offsets[e] + GM_ROWS * mt;
-        const int end = min(P.offsets[e + 1], beg + GM_ROWS);
+        const int ntl = wide ? NTW : NT, rows = wide ? 64 : GM_ROWS;
+        const int mt = li / ntl, nt = li - mt * ntl;
+        const int beg = P.offsets[e] + rows * mt;
+        const int end = min(P.offsets[e + 1], beg + rows);
         const uint8_t* blob = P.pool + static_cast<uint64_t>(P.slot_of[e]) * P.slot_bytes;
         const int n0 = (MODE == 0 ? 32 * NQ : 64 * NQ) * nw * nt;
         const int nsub = wide ? wave : nq;                  // this wave's column block of the tile
@@ -480,7 +487,7 @@ hipError_t launch_int4_gemm(const FfnParams& P0, int phases, hipStream_t s) {
     if (err != hipSuccess) return err;
     if ((err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return err;
     if ((err = hipDeviceGetAttribute(&maxlds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev)) != hipSuccess) return err;
-    constexpr int DC = 2, NW = GEMM_NW;
+    constexpr int DC0 = 2, DC1 = 3, NW = GEMM_NW;   // weight prefetch depth (2 DC groups) per half
     // persistent: 8 waves per CU, as one workgroup of 8 or two of 4 (which then
     // run out of step with each other)
     const dim3 grid(static_cast<uint32_t>(cus * (8 / NW))), block(64 * NW);
@@ -498,18 +505,18 @@ hipError_t launch_int4_gemm(const FfnParams& P0, int phases, hipStream_t s) {
         if (static_cast<int>(lds) > maxlds) return hipErrorInvalidConfiguration;
         static bool attr = false;
         if (!attr)
-            attr = hipFuncSetAttribute(reinterpret_cast<const void*>(ffn_int4_gemm_kernel<0, DC, NW>),
+            attr = hipFuncSetAttribute(reinterpret_cast<const void*>(ffn_int4_gemm_kernel<0, DC0, NW>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, maxlds) == hipSuccess;
-        hipLaunchKernelGGL((ffn_int4_gemm_kernel<0, DC, NW>), grid, block, lds, s, P);
+        hipLaunchKernelGGL((ffn_int4_gemm_kernel<0, DC0, NW>), grid, block, lds, s, P);
     }
     if (phases & 2) {
         const size_t lds = gemm_lds_bytes(P.E, P.FF / 64, NW);
         if (static_cast<int>(lds) > maxlds) return hipErrorInvalidConfiguration;
         static bool attr = false;
         if (!attr)
-            attr = hipFuncSetAttribute(reinterpret_cast<const void*>(ffn_int4_gemm_kernel<1, DC, NW>),
+            attr = hipFuncSetAttribute(reinterpret_cast<const void*>(ffn_int4_gemm_kernel<1, DC1, NW>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, maxlds) == hipSuccess;
-        hipLaunchKernelGGL((ffn_int4_gemm_kernel<1, DC, NW>), grid, block, lds, s, P);
+        hipLaunchKernelGGL((ffn_int4_gemm_kernel<1, DC1, NW>), grid, block, lds, s, P);
     }
     return hipGetLastError();
 }
