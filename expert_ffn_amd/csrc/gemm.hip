@@ -136,8 +136,13 @@ __device__ __forceinline__ GemmShape<MODE, NW> gemm_shape(const FfnParams& P) {
     return S;
 }
 
+// stages of activations in LDS: 4-wave workgroups copy them with LDS DMA
+// into a ring of 3 (two groups of prefetch), 8-wave ones through registers
+// into 2
+__host__ __device__ constexpr int gemm_nstage(int NW) { return NW == 4 ? 3 : 2; }
+
 __host__ __device__ inline size_t gemm_lds_bytes(int E, int G, int NW) {
-    return 2 * static_cast<size_t>(NW / 4) * GM_GBUF + static_cast<size_t>(64 * NW) * G * 2 + 16 +
+    return gemm_nstage(NW) * static_cast<size_t>(NW / 4) * GM_GBUF + static_cast<size_t>(64 * NW) * G * 2 + 16 +
            static_cast<size_t>(E + 1) * 4;
 }
 
@@ -149,12 +154,14 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void ffn_int4_gemm_kernel(FfnParam
     constexpr int NTH = 64 * NW;                    // threads
     constexpr int D = 2 * DC;                       // weight groups in flight per wave
     constexpr int U = (D / SG) > 2 ? (D / SG) : 2;  // chunks per unrolled body: static slots and stage parity
+    constexpr bool XD = NW == 4;                    // activations by LDS DMA (3-stage ring)
+    constexpr int NSTG = gemm_nstage(NW);
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     const GemmShape<MODE, NW> S = gemm_shape<MODE, NW>(P);
     const int E = P.E, G = S.G, GP = S.GP, NC = S.NC, NT = S.NT;
-    uint8_t* xbuf = lds;                                                   // [2][XBUF]
-    uint16_t* ssc = reinterpret_cast<uint16_t*>(lds + 2 * XBUF);           // [NTH][G] bf16 scales of the tile
-    int* pre = reinterpret_cast<int*>(lds + 2 * XBUF + ((NTH * G * 2 + 15) & ~15));   // [E+1]
+    uint8_t* xbuf = lds;                                                   // [NSTG][XBUF]
+    uint16_t* ssc = reinterpret_cast<uint16_t*>(lds + NSTG * XBUF);        // [NTH][G] bf16 scales of the tile
+    int* pre = reinterpret_cast<int*>(lds + NSTG * XBUF + ((NTH * G * 2 + 15) & ~15));   // [E+1]
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, c32 = lane & 31, hh = lane >> 5;
     const int mh = wave / NQ, nq = wave % NQ;
 
@@ -271,12 +278,24 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void ffn_int4_gemm_kernel(FfnParam
             for (int mb4 = 0; mb4 < 4; ++mb4)
                 *reinterpret_cast<u32x4*>(xbuf + buf * XBUF + ((sgi * 4 + ss) * 4 + mb4) * 1024 + lane * 16) = xr[mb4];
         };
+        // the same copy by LDS DMA: 4 loads per wave straight into the stage
+        // buffer (each writes 64 lanes x 16 bytes, the block layout above);
+        // lanes past the tile write zeros
+        auto dma_stage = [&](int c, int buf) {
+            const uint32_t g = static_cast<uint32_t>(min(SG * c + sgi, G - 1)) * 128;
+#pragma unroll
+            for (int mb4 = 0; mb4 < 4; ++mb4)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    ares, reinterpret_cast<__attribute__((address_space(3))) void*>(
+                              reinterpret_cast<uintptr_t>(xbuf + buf * XBUF + ((sgi * 4 + ss) * 4 + mb4) * 1024)),
+                    16, aoff[mb4] + g, 0, 0, 0);
+        };
 
         // Load order = order of need, as in the K loop below (stage c + 1, then
         // the last two groups of the ring), so that the in-order load counter
         // gives the same waits on the first pass as on later ones.
         u32x4 xr[4];
-        load_stage(0, xr);
+        if (!XD) load_stage(0, xr);
         u32x4 wr[D][2];
         auto fill = [&](int d) {
             const int g = min(d, G - 1);
@@ -285,8 +304,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void ffn_int4_gemm_kernel(FfnParam
         };
 #pragma unroll
         for (int d = 0; d < D - 2; ++d) fill(d);
-        store_stage(0, xr);
-        __syncthreads();   // scales and stage 0 in LDS
+        if (!XD) store_stage(0, xr);
+        __syncthreads();   // scales (and stage 0) in LDS
 
         // ---- bias of the expanded codes: acc = -136 * sum_g X[m][g] s[n][g]
         f32x16 acc[2][2];
@@ -331,24 +350,49 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void ffn_int4_gemm_kernel(FfnParam
 #pragma unroll
                 for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = corr[mb][nb] * -136.0f;
         }
-        load_stage(1, xr);
-        __builtin_amdgcn_sched_barrier(0);   // keep the issue order
-        fill(D - 2);
-        fill(D - 1);
+        if (XD) {
+            // stage 0, the last two weight groups of the ring, stage 1: the
+            // same order as in the loop, so each chunk's wait below is exact
+            dma_stage(0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+            fill(D - 2);
+            fill(D - 1);
+            __builtin_amdgcn_sched_barrier(0);
+            dma_stage(1, 1);
+        } else {
+            load_stage(1, xr);
+            __builtin_amdgcn_sched_barrier(0);   // keep the issue order
+            fill(D - 2);
+            fill(D - 1);
+        }
 
         // ---- K loop: U chunks per unrolled body
         const int ncu = (NC + U - 1) / U * U;
+        int bcur = 0;   // LDS DMA ring: the buffer of stage c is c % 3
         for (int c0 = 0; c0 < ncu; c0 += U) {
 #pragma unroll
             for (int cu = 0; cu < U; ++cu) {
                 const int c = c0 + cu;
-                const uint8_t* xb = xbuf + (cu & 1) * XBUF;
-                // stage c + 1 (loaded one chunk ago) into the other buffer, whose
-                // readers finished at the last barrier; then start stage c + 2,
-                // ahead of this chunk's weight loads so that the in-order load
-                // counter never makes a wait cover weights needed later
-                store_stage((cu + 1) & 1, xr);
-                load_stage(min(c + 2, NC - 1), xr);
+                const uint8_t* xb = xbuf + (XD ? bcur : (cu & 1)) * XBUF;
+                if (XD) {
+                    // Stage c was requested two chunks ago; after it this wave
+                    // issued at most 6 vector-memory operations (one chunk's 2
+                    // weight loads, stage c + 1's 4 copies, the next 2 weight
+                    // loads), so vmcnt <= 6 means its copies have landed.  The
+                    // barrier makes that true for every wave, and also ends the
+                    // reads of stage c - 1, whose buffer stage c + 2 now takes.
+                    // (The compiler does not track LDS DMA completion itself.)
+                    __builtin_amdgcn_s_waitcnt(0x0F76);   // vmcnt(6), lgkm/exp not waited
+                    __builtin_amdgcn_s_barrier();
+                    dma_stage(min(c + 2, NC - 1), bcur == 0 ? 2 : bcur - 1);
+                } else {
+                    // stage c + 1 (loaded one chunk ago) into the other buffer, whose
+                    // readers finished at the last barrier; then start stage c + 2,
+                    // ahead of this chunk's weight loads so that the in-order load
+                    // counter never makes a wait cover weights needed later
+                    store_stage((cu + 1) & 1, xr);
+                    load_stage(min(c + 2, NC - 1), xr);
+                }
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int gi = 0; gi < SG; ++gi) {
@@ -404,8 +448,16 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void ffn_int4_gemm_kernel(FfnParam
                     wr[slot][0] = *reinterpret_cast<const u32x4*>(wp0 + 32 * gn);
                     wr[slot][1] = *reinterpret_cast<const u32x4*>(wp1 + 32 * gn);
                 }
-                __syncthreads();
+                if (XD)
+                    bcur = bcur == 2 ? 0 : bcur + 1;
+                else
+                    __syncthreads();
             }
+        }
+        if (XD) {
+            // every copy into the ring has landed before the epilogue reuses it
+            __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+            __syncthreads();
         }
 
         // ---- epilogue
