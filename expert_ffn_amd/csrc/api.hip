@@ -238,7 +238,7 @@ moe_status moe_quantize(int32_t wfmt, const uint16_t* w_bf16, int32_t N, int32_t
         return fail(MOE_E_ARG, fn, "format %d is not a quantised format", wfmt);
     if (N < 0 || K < 1) return fail(MOE_E_SHAPE, fn, "N=%d K=%d", N, K);
     if (wfmt == MOE_W_INT4_G64 && K % 64) return fail(MOE_E_SHAPE, fn, "K=%d is not a multiple of 64", K);
-    return hip_status(fn, moe::launch_quantize(wfmt, w_bf16, N, K, q, scales,
+    return hip_status(fn, moe::launch_quantize(wfmt, w_bf16, N, K, q, scales, false,
                                                static_cast<hipStream_t>(stream)));
 }
 
@@ -259,8 +259,8 @@ moe_status moe_pack_expert(int32_t wfmt, const uint16_t* w13_bf16, const uint16_
             e = hipMemcpyAsync(b + off[2], w2_bf16, static_cast<uint64_t>(H) * FF * 2, hipMemcpyDeviceToDevice, s);
         return hip_status(fn, e);
     }
-    e = moe::launch_quantize(wfmt, w13_bf16, 2 * FF, H, b + off[0], b + off[1], s);
-    if (e == hipSuccess) e = moe::launch_quantize(wfmt, w2_bf16, H, FF, b + off[2], b + off[3], s);
+    e = moe::launch_quantize(wfmt, w13_bf16, 2 * FF, H, b + off[0], b + off[1], true, s);
+    if (e == hipSuccess) e = moe::launch_quantize(wfmt, w2_bf16, H, FF, b + off[2], b + off[3], true, s);
     return hip_status(fn, e);
 }
 

@@ -50,6 +50,13 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
 __device__ __forceinline__ u32x4 bload16(rsrc_t r, uint32_t off) {
     return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
+// with a wave-uniform byte offset in an SGPR (soff) added to the lane's
+__device__ __forceinline__ u32x4 bload16s(rsrc_t r, uint32_t off, uint32_t soff) {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, soff, 0));
+}
+__device__ __forceinline__ uint32_t bload_u16(rsrc_t r, uint32_t off, uint32_t soff) {
+    return static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b16(r, off, soff, 0));
+}
 __device__ __forceinline__ u32x2 bload8(rsrc_t r, uint32_t off) {
     return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
 }
@@ -61,6 +68,15 @@ __device__ __forceinline__ u32x2 bload8(rsrc_t r, uint32_t off) {
 __device__ __forceinline__ float act_fn(int act, float g) {
     const float z = act == ACT_SILU ? -g : -1.5957691216057308f * (g + 0.044715f * g * g * g);
     return g * __builtin_amdgcn_rcpf(1.0f + __expf(z));
+}
+
+// int4 codes of a matrix [N rows][K] inside an expert blob: 32-row blocks,
+// and inside a block one [32 rows][32 bytes] piece per 64-element group, so
+// that one group of 32 consecutive rows is 1 KB of contiguous memory.  Offset
+// of byte kb (of the row's K/2 bytes, element 2 kb in the low nibble) of row n,
+// G = K / 64; N is a multiple of 32.
+__host__ __device__ __forceinline__ int64_t int4_code_off(int n, int G, int kb) {
+    return ((static_cast<int64_t>(n >> 5) * G + (kb >> 5)) << 10) + ((n & 31) << 5) + (kb & 31);
 }
 
 // slot j of an int4 operand dword holds element perm8(j): 0,4,1,5,2,6,3,7

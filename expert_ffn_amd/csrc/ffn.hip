@@ -630,18 +630,20 @@ __device__ __forceinline__ void int4_group(uint32_t d0, uint32_t d1, const u32x4
 }
 
 // One wave: 16 rows of a w13 or w2 tile over the K range [k0, k0 + Kw) of a
-// row of K elements; rows a_row (this lane's row, already offset to k0/2),
-// activations brow (this lane's column, at position k0), scales s_sc [group][16].
+// row of K elements; codes a_lane (this lane's 16 bytes of double step 0: row,
+// byte k0 / 2 + 16 q, in the blob's tiled layout, so double step i is 2 KB
+// further), a_tail (its 8 bytes of the tail group), activations brow (this
+// lane's column, at position k0), scales s_sc [group][16].
 template <int CH>
-__device__ __forceinline__ f32x4 int4_tile(const uint8_t* a_row, rsrc_t bres, uint32_t boff, const float* s_sc,
-                                           int nds, bool tail, int q) {
+__device__ __forceinline__ f32x4 int4_tile(const uint8_t* a_lane, const uint8_t* a_tail, rsrc_t bres, uint32_t boff,
+                                           const float* s_sc, int nds, bool tail, int q) {
     // boff: byte offset of this lane's activation row at the K range start, or NO_LANE
     f32x4 acc = {0, 0, 0, 0};
     for (int c = 0; c < nds; c += CH) {
         u32x4 a[CH];
 #pragma unroll
         for (int i = 0; i < CH; ++i)
-            if (c + i < nds) a[i] = *reinterpret_cast<const u32x4*>(a_row + 64 * (c + i) + 16 * q);
+            if (c + i < nds) a[i] = *reinterpret_cast<const u32x4*>(a_lane + 2048 * (c + i));
         u32x4 b[2][4];
 #pragma unroll
         for (int m = 0; m < 4; ++m) b[0][m] = bload16(bres, boff + 2 * (128 * c + 32 * q + 8 * m));
@@ -662,7 +664,7 @@ __device__ __forceinline__ f32x4 int4_tile(const uint8_t* a_row, rsrc_t bres, ui
         }
     }
     if (tail) {
-        const u32x2 a = *reinterpret_cast<const u32x2*>(a_row + 64 * nds + 8 * q);
+        const u32x2 a = *reinterpret_cast<const u32x2*>(a_tail);
         const u32x4 b0 = bload16(bres, boff + 2 * (128 * nds + 16 * q));
         const u32x4 b1 = bload16(bres, boff + 2 * (128 * nds + 16 * q + 8));
         int4_group(a[0], a[1], b0, b1, *reinterpret_cast<const f32x4*>(s_sc + 2 * nds * 16 + 4 * q), acc);
@@ -718,7 +720,9 @@ __global__ __launch_bounds__(128 * KH) void gate_up_int4_kernel(FfnParams P) {
     const int n0 = int4_tile_base(u, P.FF);
     const int Kw = P.H / KH, k0 = hp * Kw;
     const int rowbase = t * P.FF + n0;
-    const uint8_t* a_row = blob + P.o13 + static_cast<int64_t>(rowbase + (r & 8) + perm8(r & 7)) * (P.H / 2) + k0 / 2;
+    const int arow = rowbase + (r & 8) + perm8(r & 7);
+    const uint8_t* a_lane = blob + P.o13 + int4_code_off(arow, P.H / 64, k0 / 2 + 16 * q);
+    const uint8_t* a_tail = blob + P.o13 + int4_code_off(arow, P.H / 64, k0 / 2 + 64 * (Kw >> 7) + 8 * q);
     const int p = beg + r;
     const bool valid = p < end;
     const int route = P.sorted_route[valid ? p : beg];
@@ -735,7 +739,7 @@ __global__ __launch_bounds__(128 * KH) void gate_up_int4_kernel(FfnParams P) {
     __syncthreads();
     const rsrc_t xres = make_rsrc(P.xq, static_cast<uint32_t>(P.T) * P.H * 2);
     const uint32_t xoff = valid ? static_cast<uint32_t>(((route / P.k) * P.H + k0) * 2) : NO_LANE;
-    const f32x4 acc = int4_tile<CH>(a_row, xres, xoff, s_sc, Kw >> 7, (Kw & 127) != 0, q);
+    const f32x4 acc = int4_tile<CH>(a_lane, a_tail, xres, xoff, s_sc, Kw >> 7, (Kw & 127) != 0, q);
     if (wave > 0) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) s_red[((wave - 1) * 4 + j) * 64 + lane] = acc[j];
@@ -768,7 +772,8 @@ __global__ __launch_bounds__(256) void down_int4_kernel(FfnParams P) {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, r = lane & 15, q = lane >> 4;
     const uint8_t* blob = P.pool + static_cast<uint64_t>(P.slot_of[e]) * P.slot_bytes;
     const int m0 = blk * 64 + wave * 16;
-    const uint8_t* a_row = blob + P.o2 + static_cast<int64_t>(m0 + r) * (P.FF / 2);
+    const uint8_t* a_lane = blob + P.o2 + int4_code_off(m0 + r, P.FF / 64, 16 * q);
+    const uint8_t* a_tail = blob + P.o2 + int4_code_off(m0 + r, P.FF / 64, 64 * (P.FF >> 7) + 8 * q);
     const int p = beg + r;
     const bool valid = p < end;
     float* s_sc = smem + wave * (16 * (P.FF / 64));
@@ -782,7 +787,7 @@ __global__ __launch_bounds__(256) void down_int4_kernel(FfnParams P) {
     __syncthreads();
     const rsrc_t hres = make_rsrc(P.h, static_cast<uint32_t>(P.T) * P.k * P.FF * 2);
     const uint32_t hoff = valid ? static_cast<uint32_t>(p) * P.FF * 2 : NO_LANE;
-    const f32x4 acc = int4_tile<CH>(a_row, hres, hoff, s_sc, P.FF >> 7, (P.FF & 127) != 0, q);
+    const f32x4 acc = int4_tile<CH>(a_lane, a_tail, hres, hoff, s_sc, P.FF >> 7, (P.FF & 127) != 0, q);
     if (valid) {
         const int64_t o = static_cast<int64_t>(p) * P.H + m0 + 4 * q;
         if (P.out_dt == F32) {
@@ -932,9 +937,9 @@ __global__ __launch_bounds__(256) void gate_up_int4_dec_kernel(FfnParams P) {
         const int row = t * P.FF + int4_tile_base(u0 + tt, P.FF) + (r & 8) + perm8(r & 7);
         const uint32_t* srow = reinterpret_cast<const uint32_t*>(blob + P.os13) + (row * G + k0 / 64) / 2;
         sa[tt] = *reinterpret_cast<const u32x4*>(srow + 4 * (8 * q < ng ? q : 0));
-        const uint8_t* a_row = blob + P.o13 + row * (H / 2) + k0 / 2 + 16 * q;
+        const uint8_t* a_lane = blob + P.o13 + int4_code_off(row, G, k0 / 2 + 16 * q);   // tiled: double step i 2 KB further
 #pragma unroll
-        for (int i = 0; i < NDW; ++i) a[tt][i] = *reinterpret_cast<const u32x4*>(a_row + 64 * min(i, nds - 1));
+        for (int i = 0; i < NDW; ++i) a[tt][i] = *reinterpret_cast<const u32x4*>(a_lane + 2048 * min(i, nds - 1));
     }
 
     for (int i = tid; i < 2 * GUD_RT * GS; i += 256) xsum[i] = 0;
@@ -1093,11 +1098,12 @@ __global__ __launch_bounds__(256) void down_int4_dec_kernel(FfnParams P) {
     float sv[TPW][SPL];
 #pragma unroll
     for (int tt = 0; tt < TPW; ++tt) {
-        const uint8_t* a_row = blob + P.o2 + static_cast<int64_t>(m0 + 16 * tt + r) * (FF / 2);
+        const int arow = m0 + 16 * tt + r;
+        const uint8_t* a_lane = blob + P.o2 + int4_code_off(arow, FF / 64, 16 * q);   // tiled: double step i 2 KB further
 #pragma unroll
-        for (int i = 0; i < NDS; ++i) a[tt][i] = *reinterpret_cast<const u32x4*>(a_row + 64 * i + 16 * q);
+        for (int i = 0; i < NDS; ++i) a[tt][i] = *reinterpret_cast<const u32x4*>(a_lane + 2048 * i);
         at[tt] = u32x2{0u, 0u};
-        if (TAIL) at[tt] = *reinterpret_cast<const u32x2*>(a_row + 64 * NDS + 8 * q);
+        if (TAIL) at[tt] = *reinterpret_cast<const u32x2*>(blob + P.o2 + int4_code_off(arow, FF / 64, 64 * NDS + 8 * q));
     }
     {
         const uint16_t* sc = reinterpret_cast<const uint16_t*>(blob + P.os2);
@@ -1322,6 +1328,7 @@ static bool try_fast(const FfnParams& P, int phases, hipStream_t s) {
 
 template <int FMT>
 static void launch_phases(const FfnParams& P, int phases, hipStream_t s) {
+    static_assert(FMT != W_INT4, "int4 blobs hold tiled codes: the int4 kernels read them");
     constexpr int KSTEP = Geo<FMT>::KSTEP;
     if (try_fast<FMT>(P, phases, s)) return;
     if (phases & 1) {

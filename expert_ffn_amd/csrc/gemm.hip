@@ -253,8 +253,9 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void ffn_int4_gemm_kernel(FfnParam
                 lrow[nb] = 64 * nsub + 32 * nb + c32;
             }
         }
-        const uint8_t* wp0 = blob + o_codes + static_cast<int64_t>(wrow[0]) * (S.K / 2) + 16 * hh;
-        const uint8_t* wp1 = blob + o_codes + static_cast<int64_t>(wrow[1]) * (S.K / 2) + 16 * hh;
+        // codes in the blob's tiled layout: group g of the lane's row 1 KB * g further
+        const uint8_t* wp0 = blob + o_codes + int4_code_off(wrow[0], G, 16 * hh);
+        const uint8_t* wp1 = blob + o_codes + int4_code_off(wrow[1], G, 16 * hh);
         // staging: wave w copies (group gi, K step s) = (w >> 2, w & 3) of the 4
         // route blocks; rows past the tile (and blocks 2, 3 of a wide tile) read
         // zeros without a memory access
@@ -299,8 +300,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void ffn_int4_gemm_kernel(FfnParam
         u32x4 wr[D][2];
         auto fill = [&](int d) {
             const int g = min(d, G - 1);
-            wr[d][0] = *reinterpret_cast<const u32x4*>(wp0 + 32 * g);
-            wr[d][1] = *reinterpret_cast<const u32x4*>(wp1 + 32 * g);
+            wr[d][0] = *reinterpret_cast<const u32x4*>(wp0 + 1024 * g);
+            wr[d][1] = *reinterpret_cast<const u32x4*>(wp1 + 1024 * g);
         };
 #pragma unroll
         for (int d = 0; d < D - 2; ++d) fill(d);
@@ -351,14 +352,15 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void ffn_int4_gemm_kernel(FfnParam
                 for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = corr[mb][nb] * -136.0f;
         }
         if (XD) {
-            // stage 0, the last two weight groups of the ring, stage 1: the
+            // stage 0, weight group D - 2, stage 1, weight group D - 1: the
             // same order as in the loop, so each chunk's wait below is exact
             dma_stage(0, 0);
             __builtin_amdgcn_sched_barrier(0);
             fill(D - 2);
-            fill(D - 1);
             __builtin_amdgcn_sched_barrier(0);
             dma_stage(1, 1);
+            __builtin_amdgcn_sched_barrier(0);
+            fill(D - 1);
         } else {
             load_stage(1, xr);
             __builtin_amdgcn_sched_barrier(0);   // keep the issue order
@@ -376,13 +378,14 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void ffn_int4_gemm_kernel(FfnParam
                 const uint8_t* xb = xbuf + (XD ? bcur : (cu & 1)) * XBUF;
                 if (XD) {
                     // Stage c was requested two chunks ago; after it this wave
-                    // issued at most 6 vector-memory operations (one chunk's 2
-                    // weight loads, stage c + 1's 4 copies, the next 2 weight
-                    // loads), so vmcnt <= 6 means its copies have landed.  The
-                    // barrier makes that true for every wave, and also ends the
-                    // reads of stage c - 1, whose buffer stage c + 2 now takes.
-                    // (The compiler does not track LDS DMA completion itself.)
-                    __builtin_amdgcn_s_waitcnt(0x0F76);   // vmcnt(6), lgkm/exp not waited
+                    // issued 8 vector-memory operations (the 2 weight loads of
+                    // that chunk, stage c + 1's 4 copies, the next 2 weight
+                    // loads; likewise in the prologue), so vmcnt <= 8 means its
+                    // copies have landed.  The barrier makes that true for every
+                    // wave, and also ends the reads of stage c - 1, whose buffer
+                    // stage c + 2 now takes.  (The compiler does not track LDS DMA
+                    // completion itself.)
+                    __builtin_amdgcn_s_waitcnt(0x0F78);   // vmcnt(8), lgkm/exp not waited
                     __builtin_amdgcn_s_barrier();
                     dma_stage(min(c + 2, NC - 1), bcur == 0 ? 2 : bcur - 1);
                 } else {
@@ -445,8 +448,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void ffn_int4_gemm_kernel(FfnParam
                     }
                     // refill the slot with group g + D (past the end: the last group again)
                     const int gn = min(g + D, G - 1);
-                    wr[slot][0] = *reinterpret_cast<const u32x4*>(wp0 + 32 * gn);
-                    wr[slot][1] = *reinterpret_cast<const u32x4*>(wp1 + 32 * gn);
+                    wr[slot][0] = *reinterpret_cast<const u32x4*>(wp0 + 1024 * gn);
+                    wr[slot][1] = *reinterpret_cast<const u32x4*>(wp1 + 1024 * gn);
                 }
                 if (XD)
                     bcur = bcur == 2 ? 0 : bcur + 1;

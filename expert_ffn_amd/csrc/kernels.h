@@ -16,7 +16,8 @@ hipError_t launch_route_permute(const float* logits, int T, int E, int k, int re
                                 int* n_dropped, hipStream_t s);
 hipError_t launch_combine(const void* out_routes, int out_dt, const float* w, const int* route_pos,
                           int T, int k, int H, void* y, int y_dt, hipStream_t s);
-hipError_t launch_quantize(int fmt, const uint16_t* w, int N, int K, void* q, void* scales,
+// tiled: int4 codes in the blob's 32-row tiles (N a multiple of 32), else row-major
+hipError_t launch_quantize(int fmt, const uint16_t* w, int N, int K, void* q, void* scales, bool tiled,
                            hipStream_t s);
 
 // Everything the expert-FFN kernels read and write.

@@ -38,7 +38,7 @@ __global__ __launch_bounds__(256) void quant_int8_kernel(const uint16_t* __restr
 // s_i = bf16(fp32(a * (20 - i)) / 140), i.e. clip alpha = (20 - i) / 20 of a / 7.
 __global__ __launch_bounds__(256) void quant_int4_kernel(const uint16_t* __restrict__ w, int N,
                                                          int K, uint8_t* __restrict__ q,
-                                                         uint16_t* __restrict__ s) {
+                                                         uint16_t* __restrict__ s, int tiled) {
     const int G = K / 64;
     const int64_t gid = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
     if (gid >= static_cast<int64_t>(N) * G) return;
@@ -69,7 +69,8 @@ __global__ __launch_bounds__(256) void quant_int4_kernel(const uint16_t* __restr
     }
     s[gid] = best_s;
     const float sc = bf16_to_f32(best_s);
-    uint8_t* out = q + static_cast<int64_t>(r) * (K / 2) + static_cast<int64_t>(g) * 32;
+    // the group's 32 bytes: row-major codes, or the blob's 32-row tiles
+    uint8_t* out = q + (tiled ? int4_code_off(r, G, 32 * g) : static_cast<int64_t>(r) * (K / 2) + static_cast<int64_t>(g) * 32);
     for (int b = 0; b < 32; ++b) {
         int lo = 0, hi = 0;
         if (sc != 0.0f) {
@@ -80,7 +81,7 @@ __global__ __launch_bounds__(256) void quant_int4_kernel(const uint16_t* __restr
     }
 }
 
-hipError_t launch_quantize(int fmt, const uint16_t* w, int N, int K, void* q, void* scales,
+hipError_t launch_quantize(int fmt, const uint16_t* w, int N, int K, void* q, void* scales, bool tiled,
                            hipStream_t s) {
     if (N <= 0 || K <= 0) return hipSuccess;
     if (fmt == W_INT8) {
@@ -90,7 +91,7 @@ hipError_t launch_quantize(int fmt, const uint16_t* w, int N, int K, void* q, vo
         const int64_t groups = static_cast<int64_t>(N) * (K / 64);
         hipLaunchKernelGGL(quant_int4_kernel, dim3(static_cast<uint32_t>((groups + 255) / 256)),
                            dim3(256), 0, s, w, N, K, static_cast<uint8_t*>(q),
-                           static_cast<uint16_t*>(scales));
+                           static_cast<uint16_t*>(scales), tiled ? 1 : 0);
     }
     return hipGetLastError();
 }

@@ -80,7 +80,12 @@ uint64_t moe_expert_bytes(int32_t wfmt, int32_t H, int32_t FF);
  *   int4: w13 [2FF, H/2] | bf16 [2FF, H/64] | w2 [H, FF/2] | bf16 [H, FF/64]
  * Rows are K-contiguous (K = H for w13, FF for w2).  w13 rows 0..FF-1 are the
  * gate projection, FF..2FF-1 the up projection.  int4 byte b of a row holds
- * element 2b in its low nibble and 2b+1 in its high nibble, each as q + 8.
+ * element 2b in its low nibble and 2b+1 in its high nibble, each as q + 8;
+ * the int4 code blocks are stored in tiles of 32 rows: byte b of row n is at
+ * ((n / 32) * (K / 64) + b / 32) * 1024 + (n % 32) * 32 + b % 32, so that the
+ * 32 bytes of one 64-element group of 32 consecutive rows are 1 KB of
+ * contiguous memory (one wide load for the kernels).  moe_quantize writes the
+ * codes row-major; moe_pack_expert writes them tiled.
  */
 moe_status moe_blob_layout(int32_t wfmt, int32_t H, int32_t FF, uint64_t* off);
 

@@ -272,10 +272,33 @@ void oracle_quantize_int4(const uint16_t* w, int32_t N, int32_t K, uint8_t* q, u
  *   int8: w13 int8 [2FF,H] | w13 scale fp32 [2FF] | w2 int8 [H,FF] | w2 scale fp32 [H]
  *   int4: w13 nibbles [2FF,H/2] | w13 scale bf16 [2FF,H/64] | w2 nibbles [H,FF/2] |
  *         w2 scale bf16 [H,FF/64]
+ *         The nibble blocks are tiled (a storage order of this library, not
+ *         of the pages): rows in blocks of 32, and within a block the 32 bytes
+ *         of each 64-element group of the 32 rows stored together, so byte b
+ *         (element 2b low, 2b+1 high) of row n sits at
+ *         ((n / 32) * (K / 64) + b / 32) * 1024 + (n % 32) * 32 + b % 32.
  * off[0..3] = start of w13 codes, w13 scales, w2 codes, w2 scales (for bf16 the
  * scale entries equal the next block's start); off[4] = blob bytes.
  */
 static uint64_t up256(uint64_t x) { return (x + 255u) / 256u * 256u; }
+
+/* offset of byte b of row n in a tiled int4 nibble block of K columns */
+static int64_t int4_tiled(int32_t n, int32_t K, int32_t b)
+{
+    return ((int64_t)(n / 32) * (K / 64) + b / 32) * 1024 + (int64_t)(n % 32) * 32 + b % 32;
+}
+
+/* quantise W [N, K] (N a multiple of 32) into a tiled nibble block */
+static int quantize_int4_tiled(const uint16_t* w, int32_t N, int32_t K, uint8_t* q, uint16_t* s)
+{
+    uint8_t* rm = (uint8_t*)malloc((size_t)N * (size_t)(K / 2));
+    if (!rm) return ORA_EARG;
+    oracle_quantize_int4(w, N, K, rm, s);
+    for (int32_t n = 0; n < N; ++n)
+        for (int32_t b = 0; b < K / 2; ++b) q[int4_tiled(n, K, b)] = rm[(int64_t)n * (K / 2) + b];
+    free(rm);
+    return ORA_OK;
+}
 
 int oracle_blob_layout(int32_t fmt, int32_t H, int32_t FF, uint64_t* off)
 {
@@ -317,8 +340,9 @@ int oracle_pack_expert(int32_t fmt, const uint16_t* w13, const uint16_t* w2, int
         oracle_quantize_int8(w13, 2 * FF, H, (int8_t*)(blob + off[0]), (float*)(blob + off[1]));
         oracle_quantize_int8(w2, H, FF, (int8_t*)(blob + off[2]), (float*)(blob + off[3]));
     } else {
-        oracle_quantize_int4(w13, 2 * FF, H, blob + off[0], (uint16_t*)(blob + off[1]));
-        oracle_quantize_int4(w2, H, FF, blob + off[2], (uint16_t*)(blob + off[3]));
+        if (quantize_int4_tiled(w13, 2 * FF, H, blob + off[0], (uint16_t*)(blob + off[1])) != ORA_OK ||
+            quantize_int4_tiled(w2, H, FF, blob + off[2], (uint16_t*)(blob + off[3])) != ORA_OK)
+            return ORA_EARG;
     }
     return ORA_OK;
 }
@@ -345,7 +369,7 @@ static double weight_at(const uint8_t* blob, const uint64_t* off, int32_t fmt, i
     }
     uint16_t sb;
     memcpy(&sb, scales + 2 * ((int64_t)row * (K / 64) + col / 64), 2);
-    uint8_t byte = codes[(int64_t)row * (K / 2) + col / 2];
+    uint8_t byte = codes[int4_tiled(row, K, col / 2)];
     int32_t u = (col & 1) ? (byte >> 4) : (byte & 0xF);
     return (double)bf16_bits_to_f32(sb) * (double)(u - 8);
 }

@@ -132,6 +132,23 @@ def test_dequant_reads_the_format(ora):
         assert np.array_equal(ora.dequant(blob, fmt, H, FF, 1), ora.bf16_to_f32(w2))
 
 
+def test_int4_blob_tiles_the_row_major_codes(ora):
+    # the blob's int4 code blocks are the quantiser's row-major codes in tiles
+    # of 32 rows: [N/32][K/64][32 rows][32 bytes]; the scales stay row-major
+    H, FF = 192, 128
+    r = np.random.default_rng(11)
+    w13 = synth.to_bf16_bits(r.normal(0, 0.02, (2 * FF, H)).astype(np.float32))
+    w2 = synth.to_bf16_bits(r.normal(0, 0.02, (H, FF)).astype(np.float32))
+    blob = ora.pack_expert(2, w13, w2, H, FF)
+    off = ora.blob_layout(2, H, FF)
+    for w, o_codes, o_scales in ((w13, off[0], off[1]), (w2, off[2], off[3])):
+        N, K = w.shape
+        q, sc = ora.quantize_int4(w)
+        tiles = blob[o_codes:o_codes + N * K // 2].reshape(N // 32, K // 64, 32, 32)
+        assert np.array_equal(tiles.transpose(0, 2, 1, 3).reshape(N, K // 2), q)
+        assert np.array_equal(blob[o_scales:o_scales + N * K // 32].view(np.uint16).reshape(N, K // 64), sc)
+
+
 # ----------------------------------------------------------- activation ----
 def test_activations_match_torch(ora):
     g = np.linspace(-12, 12, 4001)
