@@ -21,13 +21,14 @@
 // by an MFMA of the row scales with the activations' group sums (bf16 hi + lo),
 // -136 * sum_g s[n][g] * X[m][g].
 //
-// Work items are (expert, 128-route tile, N tile); one workgroup of 8 waves
-// per CU walks the items.  Wave (mh, nq): routes 64 mh .. 64 mh + 63 of the
-// tile (two 32-route blocks) times 64 weight rows (two 32-row blocks).  The K
-// loop runs over chunks of two 64-groups: the activations of a chunk are
-// loaded into registers one chunk ahead and written to one of two LDS
-// buffers; each wave keeps the weights of the next 2*DC groups in flight in
-// registers.
+// Work items are (expert, route tile, N tile); two workgroups of 4 waves per
+// CU walk the items (one of 8 waves is a build option).  Wave (mh, nq): routes
+// 64 mh .. 64 mh + 63 of the tile (two 32-route blocks) times 64 weight rows
+// (two 32-row blocks).  The K loop runs over 64-groups: a group's activations
+// (a 128-byte piece of each route row of the tile) are copied by LDS DMA two
+// groups ahead into a ring of three stages, whole cache lines per copy, XOR
+// swizzled in LDS; each wave keeps the weights of the next 2*DC groups in flight
+// in registers, one 1 KB load per group and 32 rows from the blob's tiled codes.
 #include "common.h"
 #include "kernels.h"
 
@@ -256,9 +257,10 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void ffn_int4_gemm_kernel(FfnParam
         // codes in the blob's tiled layout: group g of the lane's row 1 KB * g further
         const uint8_t* wp0 = blob + o_codes + int4_code_off(wrow[0], G, 16 * hh);
         const uint8_t* wp1 = blob + o_codes + int4_code_off(wrow[1], G, 16 * hh);
-        // staging: wave w copies (group gi, K step s) = (w >> 2, w & 3) of the 4
-        // route blocks; rows past the tile (and blocks 2, 3 of a wide tile) read
-        // zeros without a memory access
+        // Register staging (8-wave workgroups): a stage is [group][K step s]
+        // [route block] 1 KB fragment blocks; wave w copies (group gi, K step s) =
+        // (w >> 2, w & 3) of the 4 route blocks.  Rows past the tile (and blocks
+        // 2, 3 of a wide tile) read zeros without a memory access.
         const int sgi = wave >> 2, ss = wave & 3;
         const rsrc_t ares = make_rsrc(abase, static_cast<uint32_t>(asum_rows) * arow_stride * 2);
         uint32_t aoff[4];
@@ -269,6 +271,26 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void ffn_int4_gemm_kernel(FfnParam
             const int r = ok ? (MODE == 0 ? P.sorted_route[p] / P.k : p) : 0;
             aoff[mb4] = ok ? static_cast<uint32_t>((r * arow_stride + 16 * ss + 8 * hh) * 2) : NO_LANE;
         }
+        // LDS DMA staging (4-wave workgroups): a stage is [128 tile rows][128 B]
+        // (one 64-group of K), the 16-byte chunk j of row R at position
+        // j ^ swz(R), swz(R) = (R & 7) ^ ((R >> 3) & 3): fragment reads of 8 or 16
+        // consecutive rows hit distinct banks.  Wave w copies rows 32 w .. 32 w + 31,
+        // 8 rows (whole 128-byte lines) per copy: lane l takes row 32 w + 8 i + l / 8,
+        // position l % 8.
+        uint32_t adm[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int R = 32 * (wave & 3) + 8 * i + (lane >> 3);
+            const int p = beg + R;
+            const bool ok = p < end && (!wide || R < 64);
+            const int r = ok ? (MODE == 0 ? P.sorted_route[p] / P.k : p) : 0;
+            const int j = (lane & 7) ^ ((lane >> 3) & 7) ^ i;
+            adm[i] = ok ? static_cast<uint32_t>((r * arow_stride + 8 * j) * 2) : NO_LANE;
+        }
+        // fragment (row c32 of a 32-row block, chunk 2 s + hh) in that layout
+        uint32_t aro[4];
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4) aro[s4] = c32 * 128 + (((2 * s4 + hh) ^ (c32 & 7) ^ ((c32 >> 3) & 3)) * 16);
         auto load_stage = [&](int c, u32x4* xr) {
             const uint32_t g = static_cast<uint32_t>(min(SG * c + sgi, G - 1)) * 128;
 #pragma unroll
@@ -285,11 +307,11 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void ffn_int4_gemm_kernel(FfnParam
         auto dma_stage = [&](int c, int buf) {
             const uint32_t g = static_cast<uint32_t>(min(SG * c + sgi, G - 1)) * 128;
 #pragma unroll
-            for (int mb4 = 0; mb4 < 4; ++mb4)
+            for (int i = 0; i < 4; ++i)
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(
                     ares, reinterpret_cast<__attribute__((address_space(3))) void*>(
-                              reinterpret_cast<uintptr_t>(xbuf + buf * XBUF + ((sgi * 4 + ss) * 4 + mb4) * 1024)),
-                    16, aoff[mb4] + g, 0, 0, 0);
+                              reinterpret_cast<uintptr_t>(xbuf + buf * XBUF + (32 * (wave & 3) + 8 * i) * 128)),
+                    16, adm[i], g, 0, 0);
         };
 
         // Load order = order of need, as in the K loop below (stage c + 1, then
@@ -406,18 +428,18 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void ffn_int4_gemm_kernel(FfnParam
                         // fragments are read and its weights expanded while this
                         // step's MFMAs run
                         const int mblk = wide ? 0 : 2 * mh;
-                        const uint8_t* xa = xb + (gi * 16 + mblk) * 1024 + lane * 16;
+                        const uint8_t* xa = XD ? xb + mblk * 4096 : xb + (gi * 16 + mblk) * 1024 + lane * 16;
                         const float sc0 = bf16_to_f32(ssc[lrow[0] * G + g]), sc1 = bf16_to_f32(ssc[lrow[1] * G + g]);
                         f32x16 part[2][2];
-                        u32x4 a0 = *reinterpret_cast<const u32x4*>(xa);
-                        u32x4 a1 = *reinterpret_cast<const u32x4*>(xa + 1024);
+                        u32x4 a0 = *reinterpret_cast<const u32x4*>(xa + (XD ? aro[0] : 0));
+                        u32x4 a1 = *reinterpret_cast<const u32x4*>(xa + (XD ? aro[0] + 4096 : 1024));
                         u32x4 b0 = deq_int4(wr[slot][0][0]), b1 = deq_int4(wr[slot][1][0]);
 #pragma unroll
                         for (int s = 0; s < 4; ++s) {
                             u32x4 na0, na1, nb0, nb1;
                             if (s < 3) {
-                                na0 = *reinterpret_cast<const u32x4*>(xa + (s + 1) * 4096);
-                                na1 = *reinterpret_cast<const u32x4*>(xa + (s + 1) * 4096 + 1024);
+                                na0 = *reinterpret_cast<const u32x4*>(xa + (XD ? aro[s + 1] : (s + 1) * 4096));
+                                na1 = *reinterpret_cast<const u32x4*>(xa + (XD ? aro[s + 1] + 4096 : (s + 1) * 4096 + 1024));
                             }
                             if (s == 0) {
                                 const f32x16 z = {};
