@@ -229,13 +229,25 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void ffn_int4_gemm_kernel(FfnParam
             const uint8_t* sblk = blob + o_scales;
             const int half = (MODE == 0 ? 32 * NQ : 64 * NQ) * nw * G * 2;    // bytes of one contiguous row run
             const int nruns = MODE == 0 ? 2 : 1;
-            for (int i = tid; i < nruns * half / 16; i += NTH) {
-                const int run = i / (half / 16), o = (i - run * (half / 16)) * 16;
-                const int r0 = MODE == 0 ? run * P.FF + n0 : n0;            // first matrix row of the run
-                const int64_t src = static_cast<int64_t>(r0) * G * 2 + o;
-                const bool ok = src + 16 <= static_cast<int64_t>(S.nrows) * G * 2;
-                const u32x4 v = ok ? *reinterpret_cast<const u32x4*>(sblk + src) : u32x4{0, 0, 0, 0};
-                *reinterpret_cast<u32x4*>(reinterpret_cast<uint8_t*>(ssc) + run * half + o) = v;
+            // batches of up to 3 chunks per thread: the loads of a batch, then its stores
+            const int nch = nruns * half / 16;
+            for (int i0 = 0; i0 < nch; i0 += 3 * NTH) {
+                u32x4 v[3];
+#pragma unroll
+                for (int j = 0; j < 3; ++j) {
+                    const int i = i0 + tid + NTH * j;
+                    const int run = i / (half / 16), o = (i - run * (half / 16)) * 16;
+                    const int r0 = MODE == 0 ? run * P.FF + n0 : n0;            // first matrix row of the run
+                    const int64_t src = static_cast<int64_t>(r0) * G * 2 + o;
+                    const bool ok = i < nch && src + 16 <= static_cast<int64_t>(S.nrows) * G * 2;
+                    v[j] = ok ? *reinterpret_cast<const u32x4*>(sblk + src) : u32x4{0, 0, 0, 0};
+                }
+#pragma unroll
+                for (int j = 0; j < 3; ++j) {
+                    const int i = i0 + tid + NTH * j;
+                    const int run = i / (half / 16), o = (i - run * (half / 16)) * 16;
+                    if (i < nch) *reinterpret_cast<u32x4*>(reinterpret_cast<uint8_t*>(ssc) + run * half + o) = v[j];
+                }
             }
         }
 
