@@ -360,8 +360,8 @@ def main():
         summarize_trace(*args.summarize_trace, command=args.command)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(see DESIGN.md for how the path would shard); run with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU only: the expert FFN here runs on one GPU and has no "
+              "multi-GPU path; run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -422,7 +422,7 @@ def main():
     ms_per_step = elapsed / args.steps * 1e3
     tok_s = T * args.steps / elapsed
 
-    # algorithmic bytes (SURVEY's units): distinct experts' packed bytes + x, y, logits, indices
+    # algorithmic bytes: each distinct expert's packed bytes once, plus x, y, logits and the route indices
     off = lib.blob_layout(fmt, H, FF)
     w13_bytes = off[2]                    # w13 codes + scales (+ alignment, none at this shape)
     per_layer_io = T * H * 2 * 2 + T * E * 4 + T * k * 4 * 4 + (E + 1) * 4

@@ -15,7 +15,8 @@ ARCH = os.environ.get("EXPERT_FFN_ARCH", "gfx950")
 HIPCC = "/opt/rocm/bin/hipcc" if os.path.exists("/opt/rocm/bin/hipcc") else "hipcc"
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
-    # packed fp32 VALU ops off ("Build")
+    # no packed fp32 VALU instructions (v_pk_fma_f32 and the like): the compiler
+    # would otherwise form them from ordinary float code; this library keeps them out
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     # MFMA accumulators in ordinary VGPRs: no v_accvgpr moves around each MFMA
     "-mllvm", "-amdgpu-mfma-vgpr-form=1",
