@@ -39,17 +39,25 @@ struct PermLds {
     int count[PERM_MAX_E];
     int base[PERM_MAX_E];
     int res[PERM_MAX_E];
-    int wcnt[PERM_WAVES][PERM_MAX_E];
+    int wcnt[PERM_WAVES][PERM_MAX_E];   // per (wave, expert) count of the current block
     int drop;
     int total;
 };
 
 // Steps of the grouping for one workgroup of PERM_THREADS threads.  res: is
 // expert tid resident (tid < E); id0: the expert of route tid (tid < R, else
-// -1); routes of later blocks of 1024 are read from ids.
-__device__ __forceinline__ void permute_steps(PermLds& S, const int* __restrict__ ids, int id0, int res, int R,
-                                              int E, int* __restrict__ offsets, int* __restrict__ sorted_route,
-                                              int* __restrict__ route_pos, int* __restrict__ n_dropped) {
+// -1); routes of later blocks of 1024 are read from ids.  Each thread holds its
+// routes of IB blocks at a time (one load each, all requested at once), so for
+// up to IB blocks neither the histogram nor the positions wait for memory once
+// per block.  With wpre ([PERM_WAVES][PERM_MAX_E] in LDS, IB > 1) a block's
+// per-expert wave offsets are formed once by the expert's thread; without it
+// each route adds up the counts of the earlier waves itself (fewer steps for a
+// single block).
+template <int PERM_IB>
+__device__ __forceinline__ void permute_steps(PermLds& S, int (*wpre)[PERM_MAX_E], const int* __restrict__ ids, int id0,
+                                              int res, int R, int E, int* __restrict__ offsets,
+                                              int* __restrict__ sorted_route, int* __restrict__ route_pos,
+                                              int* __restrict__ n_dropped) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     if (tid < E) {
         S.count[tid] = 0;
@@ -59,12 +67,35 @@ __device__ __forceinline__ void permute_steps(PermLds& S, const int* __restrict_
     if (tid == 0) S.drop = 0;
     __syncthreads();
 
+    // the kept expert (or -1) of route b0 + 1024 j + tid, j < PERM_IB
+    auto load_batch = [&](int b0, int* ev) {
+        int raw[PERM_IB];
+#pragma unroll
+        for (int j = 0; j < PERM_IB; ++j) {
+            const int i = b0 + j * PERM_THREADS + tid;
+            raw[j] = (b0 == 0 && j == 0) ? id0 : (i < R ? ids[i] : -1);
+        }
+#pragma unroll
+        for (int j = 0; j < PERM_IB; ++j) {
+            const int v = raw[j];
+            ev[j] = (v >= 0 && v < E && S.res[v]) ? v : -1;
+        }
+    };
+    constexpr int BATCH = PERM_IB * PERM_THREADS;
+    int ev0[PERM_IB];   // the first batch, kept for the positions
+
     // 1. histogram of kept routes, count of dropped ones
-    for (int i = tid; i - tid < R; i += PERM_THREADS) {
-        const int e = i == tid ? id0 : (i < R ? ids[i] : -1);
-        const bool keep = e >= 0 && e < E && S.res[e];
-        if (keep) atomicAdd(&S.count[e], 1);
-        const int nd = __popcll(__ballot(i < R && !keep));
+    for (int b0 = 0; b0 < R; b0 += BATCH) {
+        int ev[PERM_IB];
+        load_batch(b0, ev);
+        int nd = 0;
+#pragma unroll
+        for (int j = 0; j < PERM_IB; ++j) {
+            const int i = b0 + j * PERM_THREADS + tid;
+            if (ev[j] >= 0) atomicAdd(&S.count[ev[j]], 1);
+            nd += __popcll(__ballot(i < R && ev[j] < 0));
+            if (b0 == 0) ev0[j] = ev[j];
+        }
         if (lane == 0 && nd) atomicAdd(&S.drop, nd);
     }
     __syncthreads();
@@ -90,45 +121,77 @@ __device__ __forceinline__ void permute_steps(PermLds& S, const int* __restrict_
     }
     __syncthreads();
 
-    // 3. stable positions, one block of 1024 routes at a time
+    // 3. stable positions, one block of 1024 routes at a time: the lanes of a
+    // wave with the same kept expert (one ballot per bit of the id) give each
+    // route its rank and the wave's count; a route's position is base[e] plus
+    // the counts of earlier waves plus its rank, and base[e] then moves past
+    // the block
     const int nbits = E > 1 ? 32 - __clz(E - 1) : 0;   // bits of an expert id
-    for (int blk = 0; blk < R; blk += PERM_THREADS) {
-        const int i = blk + tid;
-        int e = -1;
-        if (i < R) {
-            const int v = blk == 0 ? id0 : ids[i];
-            if (v >= 0 && v < E && S.res[v]) e = v;
+    for (int b0 = 0; b0 < R; b0 += BATCH) {
+        int ev[PERM_IB];
+        if (b0 == 0) {
+#pragma unroll
+            for (int j = 0; j < PERM_IB; ++j) ev[j] = ev0[j];
+        } else {
+            load_batch(b0, ev);
         }
-        // peers: the lanes of this wave with the same kept expert
-        uint64_t peers = __ballot(e >= 0);
-        for (int bit = 0; bit < nbits; ++bit) {
-            const bool mine = (e >> bit) & 1;
-            const uint64_t bb = __ballot(mine);
-            peers &= mine ? bb : ~bb;
-        }
-        const int rank = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(peers >> 32),
-                                                   __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(peers), 0));
-        if (e >= 0 && rank == 0) S.wcnt[wave][e] = __popcll(peers);
-        __syncthreads();
-        if (e >= 0) {
-            int pos = S.base[e] + rank;
-            for (int v = 0; v < wave; ++v) pos += S.wcnt[v][e];
-            sorted_route[pos] = i;
-            route_pos[i] = pos;
-        } else if (i < R) {
-            route_pos[i] = -1;
-        }
-        if (blk + PERM_THREADS < R) {   // set up the next block
-            __syncthreads();
-            for (int ee = tid; ee < E; ee += PERM_THREADS) {
-                int sum = 0;
-                for (int v = 0; v < PERM_WAVES; ++v) {
-                    sum += S.wcnt[v][ee];
-                    S.wcnt[v][ee] = 0;
-                }
-                S.base[ee] += sum;
+#pragma unroll
+        for (int j = 0; j < PERM_IB; ++j) {
+            const int blk = b0 + j * PERM_THREADS;
+            if (blk >= R) break;
+            const int i = blk + tid, e = ev[j];
+            uint64_t peers = __ballot(e >= 0);
+            for (int bit = 0; bit < nbits; ++bit) {
+                const bool mine = (e >> bit) & 1;
+                const uint64_t bb = __ballot(mine);
+                peers &= mine ? bb : ~bb;
             }
-            __syncthreads();
+            const int rank = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(peers >> 32),
+                                                       __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(peers), 0));
+            if (e >= 0 && rank == 0) S.wcnt[wave][e] = __popcll(peers);
+            __syncthreads();   // counts of the block in; positions of the last block read
+            if constexpr (PERM_IB > 1) {
+                for (int ee = tid; ee < E; ee += PERM_THREADS) {
+                    int run = S.base[ee];
+#pragma unroll
+                    for (int v = 0; v < PERM_WAVES; ++v) {
+                        const int c = S.wcnt[v][ee];
+                        wpre[v][ee] = run;
+                        S.wcnt[v][ee] = 0;
+                        run += c;
+                    }
+                    S.base[ee] = run;
+                }
+                __syncthreads();
+                if (e >= 0) {
+                    const int pos = wpre[wave][e] + rank;
+                    sorted_route[pos] = i;
+                    route_pos[i] = pos;
+                } else if (i < R) {
+                    route_pos[i] = -1;
+                }
+                continue;
+            }
+            if (e >= 0) {
+                int pos = S.base[e] + rank;
+                for (int v = 0; v < wave; ++v) pos += S.wcnt[v][e];
+                sorted_route[pos] = i;
+                route_pos[i] = pos;
+            } else if (i < R) {
+                route_pos[i] = -1;
+            }
+            if (blk + PERM_THREADS < R) {   // set up the next block
+                __syncthreads();
+                for (int ee = tid; ee < E; ee += PERM_THREADS) {
+                    int sum = 0;
+                    for (int v = 0; v < PERM_WAVES; ++v) {
+                        sum += S.wcnt[v][ee];
+                        S.wcnt[v][ee] = 0;
+                    }
+                    S.base[ee] += sum;
+                }
+                __syncthreads();
+            }
         }
     }
     // 4. positions past the kept routes
@@ -140,11 +203,12 @@ __global__ __launch_bounds__(PERM_THREADS) void permute_kernel(
     int* __restrict__ offsets, int* __restrict__ sorted_route, int* __restrict__ route_pos,
     int* __restrict__ n_dropped) {
     __shared__ PermLds S;
+    __shared__ int wpre[PERM_WAVES][PERM_MAX_E];
     const int tid = threadIdx.x;
     // both inputs requested at once: the residency of expert tid and route tid
     const int res = tid < E ? (slot_of[tid] >= 0) : 0;
     const int id0 = tid < R ? ids[tid] : -1;
-    permute_steps(S, ids, id0, res, R, E, offsets, sorted_route, route_pos, n_dropped);
+    permute_steps<8>(S, wpre, ids, id0, res, R, E, offsets, sorted_route, route_pos, n_dropped);
 }
 
 // Router top-k and grouping in one workgroup, for R = T k <= 1024: wave w
@@ -163,7 +227,7 @@ __global__ __launch_bounds__(PERM_THREADS) void route_permute_kernel(
     for (int t = tid >> 6; t < T; t += PERM_WAVES) route_token<NPL>(logits, t, E, k, renorm, ids, w, s_ids);
     __syncthreads();
     const int id0 = tid < R ? s_ids[tid] : -1;
-    permute_steps(S, ids, id0, res, R, E, offsets, sorted_route, route_pos, n_dropped);
+    permute_steps<1>(S, nullptr, ids, id0, res, R, E, offsets, sorted_route, route_pos, n_dropped);
 }
 
 hipError_t launch_route_permute(const float* logits, int T, int E, int k, int renorm, const int* slot_of,
