@@ -819,8 +819,8 @@ struct GudLds {             // offsets (bytes) into dynamic LDS
 __host__ __device__ inline GudLds gud_lds(int H) {
     GudLds L;
     const int G = H / 64, GS = (G + 39) & ~7, NGW = 2 * ((H / 128 + 1) / 2);
-    L.xs = 0;                                             // bf16 [RT][H]
-    L.xsum = GUD_RT * H * 2;                              // bf16 [2][RT][GS] hi, lo (zero past G)
+    L.xs = 0;                                             // bf16 [RT][H + 8] (rows 16 bytes apart in bank order)
+    L.xsum = GUD_RT * (H + 8) * 2;                        // bf16 [2][RT][GS] hi, lo (zero past G)
     L.sc = (L.xsum + 2 * GUD_RT * GS * 2 + 15) & ~15;     // float [4 waves][TPW][NGW][16]
     L.red = L.sc + 4 * GUD_TPW * NGW * 16 * 4;            // float [TPW][3][4][64]
     L.tok = L.red + GUD_TPW * 3 * 4 * 64 * 4;             // int [RT]
@@ -905,7 +905,7 @@ __global__ __launch_bounds__(256) void gate_up_int4_dec_kernel(FfnParams P) {
                 sum += __shfl_xor(sum, 4, 64);
                 sum += __shfl_xor(sum, 8, 64);
                 if (ok) {
-                    *reinterpret_cast<u32x4*>(xs + j * HC + 8 * blk) = o;
+                    *reinterpret_cast<u32x4*>(xs + j * (HC + 8) + 8 * blk) = o;
                     if ((blk & 13) == 0) {
                         const int gi = j * GS + (blk >> 4) * 2 + ((blk >> 1) & 1);
                         const uint32_t shi = pack_bf16x2(sum, 0.0f) & 0xFFFFu;
@@ -914,7 +914,7 @@ __global__ __launch_bounds__(256) void gate_up_int4_dec_kernel(FfnParams P) {
                     }
                 }
             } else if (ok) {
-                *reinterpret_cast<u32x4*>(xs + j * HC + 8 * blk) = xr[sb];
+                *reinterpret_cast<u32x4*>(xs + j * (HC + 8) + 8 * blk) = xr[sb];
             }
         }
         if (XT != BF16) {
@@ -947,7 +947,7 @@ __global__ __launch_bounds__(256) void gate_up_int4_dec_kernel(FfnParams P) {
     auto compute_tile = [&](int rt, int nr) {
         // column r of the MFMA is token slot r % RT (slots past nr are discarded)
         const int slot = r & (GUD_RT - 1);
-        const uint16_t* xrow = xs + slot * H + k0 + 32 * q;
+        const uint16_t* xrow = xs + slot * (H + 8) + k0 + 32 * q;   // 4 route rows on different banks
         const uint32_t* shi = reinterpret_cast<const uint32_t*>(xsum + slot * GS + k0 / 64 + 8 * q);
         const uint32_t* slo = reinterpret_cast<const uint32_t*>(xsum + GUD_RT * GS + slot * GS + k0 / 64 + 8 * q);
         const u32x4 xhi = {shi[0], shi[1], shi[2], shi[3]};
@@ -1053,7 +1053,9 @@ __global__ __launch_bounds__(256) void down_int4_dec_kernel(FfnParams P) {
     constexpr int NG = 2 * NDS + (TAIL ? 1 : 0);   // groups per row
     constexpr int SPL = (16 * NG + 63) / 64;       // scale values per lane and tile
     constexpr int RT = GUD_RT;
-    __shared__ __attribute__((aligned(16))) uint16_t hs[RT * 128 * (NDS + 1)];   // [RT][FF] bf16
+    // [RT][FF + 8] bf16: rows 16 bytes apart in bank order, so that the 4 route
+    // rows of a fragment read sit on different banks (FF + 8 <= 128 (NDS + 1))
+    __shared__ __attribute__((aligned(16))) uint16_t hs[RT * 128 * (NDS + 1)];
     __shared__ float s_scs[4][TPW][NG * 16];
     const int FF = P.FF;
     const int nblk = P.H / (64 * TPW);
@@ -1085,7 +1087,7 @@ __global__ __launch_bounds__(256) void down_int4_dec_kernel(FfnParams P) {
             const int i = tid + 256 * sb;
             if (i < nr * nbr) {
                 const int j = i / nbr, c = i - j * nbr;
-                *reinterpret_cast<u32x4*>(hs + j * FF + 8 * c) = hr[sb];
+                *reinterpret_cast<u32x4*>(hs + j * (FF + 8) + 8 * c) = hr[sb];
             }
         }
     };
@@ -1119,7 +1121,7 @@ __global__ __launch_bounds__(256) void down_int4_dec_kernel(FfnParams P) {
 
     auto compute_tile = [&](int rt, int nr) {
         const int slot = r & (RT - 1);
-        const uint16_t* hrow = hs + slot * FF + 32 * q;
+        const uint16_t* hrow = hs + slot * (FF + 8) + 32 * q;
         f32x4 acc[TPW];
 #pragma unroll
         for (int tt = 0; tt < TPW; ++tt) acc[tt] = f32x4{0, 0, 0, 0};
@@ -1137,7 +1139,7 @@ __global__ __launch_bounds__(256) void down_int4_dec_kernel(FfnParams P) {
             }
         }
         if (TAIL) {
-            const uint16_t* tr = hs + slot * FF + 128 * NDS + 16 * q;
+            const uint16_t* tr = hs + slot * (FF + 8) + 128 * NDS + 16 * q;
             const u32x4 b0 = *reinterpret_cast<const u32x4*>(tr), b1 = *reinterpret_cast<const u32x4*>(tr + 8);
 #pragma unroll
             for (int tt = 0; tt < TPW; ++tt)
