@@ -33,17 +33,16 @@
 namespace moe {
 
 template <int FMT> struct Geo;
-template <> struct Geo<W_INT4> { static constexpr int KSTEP = 64, MF = 2; using A = u32x2; };
 template <> struct Geo<W_INT8> { static constexpr int KSTEP = 64, MF = 2; using A = u32x4; };
 template <> struct Geo<W_BF16> { static constexpr int KSTEP = 32, MF = 1; using A = u32x4; };
 
 // bytes of one weight row of K elements
 template <int FMT> __host__ __device__ __forceinline__ int64_t row_bytes(int K) {
-    return FMT == W_INT4 ? K / 2 : (FMT == W_INT8 ? K : 2 * K);
+    return FMT == W_INT8 ? K : 2 * K;
 }
 // byte offset of lane group q's A fragment of step s inside a row
 template <int FMT> __device__ __forceinline__ int a_off(int s, int q) {
-    return FMT == W_INT4 ? s * 32 + q * 8 : (FMT == W_INT8 ? s * 64 + q * 16 : (s * 32 + q * 8) * 2);
+    return FMT == W_INT8 ? s * 64 + q * 16 : (s * 32 + q * 8) * 2;
 }
 // element offset of lane group q's B fragment of step s inside an activation row
 template <int FMT> __device__ __forceinline__ int b_off(int s, int q) {
@@ -100,14 +99,11 @@ __global__ __launch_bounds__(256) void prep_x_kernel(const void* __restrict__ x,
 // ------------------------------------------------- gate/up (first half) --
 // Workgroup = KSPLIT waves on one (expert, 16-row tile of FF); wave w covers
 // steps [w*spw, (w+1)*spw) of K = H for the gate rows n0.. and the up rows
-// FF+n0.. of that tile.  For int4 w2 the tile's rows are taken in the order
-// (i & 8) | perm8(i & 7), so that the four h values a lane ends with are four
-// consecutive entries of h in the w2 operand order.
+// FF+n0.. of that tile (bf16 and int8 weights; int4 has kernels of its own).
 template <int FMT, int KSPLIT, int NGC>
 __global__ __launch_bounds__(64 * KSPLIT) void gate_up_generic_kernel(FfnParams P) {
     using G = Geo<FMT>;
     using AF = typename G::A;
-    constexpr bool PERM_H = (FMT == W_INT4);
     extern __shared__ float smem[];
     const int ntile = P.FF >> 4;
     const int e = blockIdx.x / ntile, tile = blockIdx.x - e * ntile;
@@ -116,25 +112,14 @@ __global__ __launch_bounds__(64 * KSPLIT) void gate_up_generic_kernel(FfnParams 
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, r = lane & 15, q = lane >> 4;
     const uint8_t* blob = P.pool + static_cast<uint64_t>(P.slot_of[e]) * P.slot_bytes;
     const int n0 = tile << 4;
-    const int rho = PERM_H ? ((r & 8) | perm8(r & 7)) : r;
     const int64_t rs = row_bytes<FMT>(P.H);
-    const uint8_t* ag_row = blob + P.o13 + static_cast<int64_t>(n0 + rho) * rs;
-    const uint8_t* au_row = blob + P.o13 + static_cast<int64_t>(P.FF + n0 + rho) * rs;
+    const uint8_t* ag_row = blob + P.o13 + static_cast<int64_t>(n0 + r) * rs;
+    const uint8_t* au_row = blob + P.o13 + static_cast<int64_t>(P.FF + n0 + r) * rs;
     const int nsteps = P.H / G::KSTEP, spw = nsteps / KSPLIT, s0 = wave * spw;
 
-    float* s_sc = smem + wave * (2 * spw * 16);               // int4: [2][spw][16]
-    float* s_red = smem + (FMT == W_INT4 ? KSPLIT * 2 * spw * 16 : 0);  // [KSPLIT-1][8][64]
+    float* s_red = smem;   // [KSPLIT-1][8][64]
     f32x4 sg_row = {0, 0, 0, 0}, su_row = {0, 0, 0, 0};
-    if (FMT == W_INT4) {
-        const int Gr = P.H / 64;
-        const uint16_t* sc = reinterpret_cast<const uint16_t*>(blob + P.os13);
-        for (int idx = lane; idx < 32 * spw; idx += 64) {
-            const int tl = idx / (16 * spw), rem = idx - tl * 16 * spw;
-            const int i = rem / spw, gg = rem - i * spw;
-            const int row = tl * P.FF + n0 + ((i & 8) | perm8(i & 7));
-            s_sc[(tl * spw + gg) * 16 + i] = bf16_to_f32(sc[static_cast<int64_t>(row) * Gr + s0 + gg]);
-        }
-    } else if (FMT == W_INT8) {
+    if (FMT == W_INT8) {
         const float* sc = reinterpret_cast<const float*>(blob + P.os13);
         sg_row = *reinterpret_cast<const f32x4*>(sc + n0 + 4 * q);
         su_row = *reinterpret_cast<const f32x4*>(sc + P.FF + n0 + 4 * q);
@@ -142,7 +127,7 @@ __global__ __launch_bounds__(64 * KSPLIT) void gate_up_generic_kernel(FfnParams 
     __syncthreads();
 
     const f32x4 zero = {0, 0, 0, 0};
-    const u32x4 kbias = splat(FMT == W_INT4 ? 0xC308C308u : 0xC300C300u);  // bf16 -136 / -128
+    const u32x4 kbias = splat(0xC300C300u);  // bf16 -128
     for (int c0 = beg; c0 < end; c0 += 16) {
         const int p = c0 + r;
         const bool valid = p < end;
@@ -167,18 +152,7 @@ __global__ __launch_bounds__(64 * KSPLIT) void gate_up_generic_kernel(FfnParams 
 #pragma unroll
             for (int j = 0; j < NGC; ++j) {
                 if (sc0 + j < spw) {
-                    if constexpr (FMT == W_INT4) {
-                        f32x4 c = mfma16x16x32(kbias, b[j][0], zero);
-                        c = mfma16x16x32(kbias, b[j][1], c);
-                        f32x4 t = mfma16x16x32(deq_int4(ag[j][0]), b[j][0], c);
-                        t = mfma16x16x32(deq_int4(ag[j][1]), b[j][1], t);
-                        const f32x4 sg = *reinterpret_cast<const f32x4*>(s_sc + (sc0 + j) * 16 + 4 * q);
-                        accg += sg * t;
-                        t = mfma16x16x32(deq_int4(au[j][0]), b[j][0], c);
-                        t = mfma16x16x32(deq_int4(au[j][1]), b[j][1], t);
-                        const f32x4 su = *reinterpret_cast<const f32x4*>(s_sc + (spw + sc0 + j) * 16 + 4 * q);
-                        accu += su * t;
-                    } else if constexpr (FMT == W_INT8) {
+                    if constexpr (FMT == W_INT8) {
                         cc = mfma16x16x32(kbias, b[j][0], cc);
                         cc = mfma16x16x32(kbias, b[j][1], cc);
                         accg = mfma16x16x32(deq_int8(ag[j][0], ag[j][1]), b[j][0], accg);
@@ -242,22 +216,12 @@ __global__ __launch_bounds__(256) void down_generic_kernel(FfnParams P) {
     const uint8_t* a_row = blob + P.o2 + static_cast<int64_t>(m0 + r) * row_bytes<FMT>(P.FF);
     const int nsteps = P.FF / G::KSTEP;
 
-    float* s_sc = smem + wave * (nsteps * 16);  // int4: [nsteps][16]
     f32x4 s_row = {0, 0, 0, 0};
-    if (FMT == W_INT4) {
-        const int Gr = P.FF / 64;
-        const uint16_t* sc = reinterpret_cast<const uint16_t*>(blob + P.os2);
-        for (int idx = lane; idx < 16 * nsteps; idx += 64) {
-            const int i = idx / nsteps, gg = idx - i * nsteps;
-            s_sc[gg * 16 + i] = bf16_to_f32(sc[static_cast<int64_t>(m0 + i) * Gr + gg]);
-        }
-    } else if (FMT == W_INT8) {
+    if (FMT == W_INT8)
         s_row = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(blob + P.os2) + m0 + 4 * q);
-    }
-    __syncthreads();
 
     const f32x4 zero = {0, 0, 0, 0};
-    const u32x4 kbias = splat(FMT == W_INT4 ? 0xC308C308u : 0xC300C300u);
+    const u32x4 kbias = splat(0xC300C300u);   // bf16 -128
     for (int c0 = beg; c0 < end; c0 += 16) {
         const int p = c0 + r;
         const bool valid = p < end;
@@ -280,14 +244,7 @@ __global__ __launch_bounds__(256) void down_generic_kernel(FfnParams P) {
 #pragma unroll
             for (int j = 0; j < NGC; ++j) {
                 if (sc0 + j < nsteps) {
-                    if constexpr (FMT == W_INT4) {
-                        f32x4 t = mfma16x16x32(kbias, b[j][0], zero);
-                        t = mfma16x16x32(kbias, b[j][1], t);
-                        t = mfma16x16x32(deq_int4(a[j][0]), b[j][0], t);
-                        t = mfma16x16x32(deq_int4(a[j][1]), b[j][1], t);
-                        const f32x4 s = *reinterpret_cast<const f32x4*>(s_sc + (sc0 + j) * 16 + 4 * q);
-                        acc += s * t;
-                    } else if constexpr (FMT == W_INT8) {
+                    if constexpr (FMT == W_INT8) {
                         cc = mfma16x16x32(kbias, b[j][0], cc);
                         cc = mfma16x16x32(kbias, b[j][1], cc);
                         acc = mfma16x16x32(deq_int8(a[j][0], a[j][1]), b[j][0], acc);
@@ -320,26 +277,11 @@ __global__ __launch_bounds__(256) void down_generic_kernel(FfnParams P) {
 // loads are in flight.  Lanes past the group's last route read the group's
 // first route: their D columns are computed and never stored.
 
-// (rows of the tile held by D row i) for the w2 operand order of int4 h
-__device__ __forceinline__ int tile_row(bool perm, int i) { return perm ? ((i & 8) | perm8(i & 7)) : i; }
-
 // one step of the gate/up MFMAs for both tiles
 template <int FMT>
 __device__ __forceinline__ void step_gu(const typename Geo<FMT>::A& ag, const typename Geo<FMT>::A& au,
-                                        const u32x4* b, const f32x4& sg, const f32x4& su, f32x4& accg,
-                                        f32x4& accu, f32x4& cc) {
-    const f32x4 zero = {0, 0, 0, 0};
-    if constexpr (FMT == W_INT4) {
-        const u32x4 kb = splat(0xC308C308u);  // bf16 -136
-        f32x4 c = mfma16x16x32(kb, b[0], zero);
-        c = mfma16x16x32(kb, b[1], c);
-        f32x4 t = mfma16x16x32(deq_int4(ag[0]), b[0], c);
-        t = mfma16x16x32(deq_int4(ag[1]), b[1], t);
-        accg += sg * t;
-        t = mfma16x16x32(deq_int4(au[0]), b[0], c);
-        t = mfma16x16x32(deq_int4(au[1]), b[1], t);
-        accu += su * t;
-    } else if constexpr (FMT == W_INT8) {
+                                        const u32x4* b, f32x4& accg, f32x4& accu, f32x4& cc) {
+    if constexpr (FMT == W_INT8) {
         const u32x4 kb = splat(0xC300C300u);  // bf16 -128
         cc = mfma16x16x32(kb, b[0], cc);
         cc = mfma16x16x32(kb, b[1], cc);
@@ -359,9 +301,7 @@ void gate_up_fast_kernel(FfnParams P) {
     using G = Geo<FMT>;
     using AF = typename G::A;
     constexpr int MF = G::MF;
-    constexpr bool PERM_H = (FMT == W_INT4);
     constexpr int D = NG < 3 ? NG : 3;          // activation prefetch depth (steps)
-    constexpr int SPL = (32 * NG + 63) / 64;     // scale values staged per lane (int4)
     extern __shared__ float smem[];
     const int ntile = P.FF >> 4;
     const int e = blockIdx.x / ntile, tile = blockIdx.x - e * ntile;
@@ -372,7 +312,7 @@ void gate_up_fast_kernel(FfnParams P) {
     const int n0 = tile << 4;
     const int s0 = wave * NG;
     const int64_t rs = row_bytes<FMT>(P.H);
-    const uint8_t* ag_row = blob + P.o13 + static_cast<int64_t>(n0 + tile_row(PERM_H, r)) * rs;
+    const uint8_t* ag_row = blob + P.o13 + static_cast<int64_t>(n0 + r) * rs;
     const uint8_t* au_row = ag_row + static_cast<int64_t>(P.FF) * rs;
 
     // 1. route of this lane's column (invalid columns read route beg: their D
@@ -387,33 +327,10 @@ void gate_up_fast_kernel(FfnParams P) {
         ag[g] = *reinterpret_cast<const AF*>(ag_row + a_off<FMT>(s0 + g, q));
         au[g] = *reinterpret_cast<const AF*>(au_row + a_off<FMT>(s0 + g, q));
     }
-    // 3. scales: int4 staged to LDS as [tile][step][D row], int8 per row
-    float* s_sc = smem + wave * (32 * NG);
-    float* s_red = smem + (FMT == W_INT4 ? KSPLIT * 32 * NG : 0);
+    // 3. int8 row scales
+    float* s_red = smem;   // [KSPLIT-1][8][64]
     f32x4 sg_row = {0, 0, 0, 0}, su_row = {0, 0, 0, 0};
-    if constexpr (FMT == W_INT4) {
-        const int Gr = P.H / 64;
-        const uint16_t* sc = reinterpret_cast<const uint16_t*>(blob + P.os13);
-        float sv[SPL];
-#pragma unroll
-        for (int m = 0; m < SPL; ++m) {
-            const int idx = lane + 64 * m;
-            sv[m] = 0.0f;
-            if (idx < 32 * NG) {
-                const int rowi = idx / NG, g = idx - rowi * NG;   // rowi: tile*16 + D row
-                const int row = (rowi >> 4) * P.FF + n0 + tile_row(true, rowi & 15);
-                sv[m] = bf16_to_f32(sc[static_cast<int64_t>(row) * Gr + s0 + g]);
-            }
-        }
-#pragma unroll
-        for (int m = 0; m < SPL; ++m) {
-            const int idx = lane + 64 * m;
-            if (idx < 32 * NG) {
-                const int rowi = idx / NG, g = idx - rowi * NG;
-                s_sc[((rowi >> 4) * NG + g) * 16 + (rowi & 15)] = sv[m];
-            }
-        }
-    } else if constexpr (FMT == W_INT8) {
+    if constexpr (FMT == W_INT8) {
         const float* sc = reinterpret_cast<const float*>(blob + P.os13);
         sg_row = *reinterpret_cast<const f32x4*>(sc + n0 + 4 * q);
         su_row = *reinterpret_cast<const f32x4*>(sc + P.FF + n0 + 4 * q);
@@ -431,12 +348,7 @@ void gate_up_fast_kernel(FfnParams P) {
     f32x4 accg = zero, accu = zero, cc = zero;
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
-        f32x4 sg = zero, su = zero;
-        if constexpr (FMT == W_INT4) {
-            sg = *reinterpret_cast<const f32x4*>(s_sc + g * 16 + 4 * q);
-            su = *reinterpret_cast<const f32x4*>(s_sc + (NG + g) * 16 + 4 * q);
-        }
-        step_gu<FMT>(ag[g], au[g], b[g % D], sg, su, accg, accu, cc);
+        step_gu<FMT>(ag[g], au[g], b[g % D], accg, accu, cc);
         if (g + D < NG) {
 #pragma unroll
             for (int m = 0; m < MF; ++m)
@@ -482,7 +394,6 @@ void down_fast_kernel(FfnParams P) {
     constexpr int MF = G::MF;
     constexpr int RTW = 4 / KS;
     constexpr int D = NG < 3 ? NG : 3;
-    constexpr int SPL = (16 * NG + 63) / 64;
     extern __shared__ float smem[];
     const int nblk = P.H / (16 * RTW);
     const int e = blockIdx.x / nblk, blk = blockIdx.x - e * nblk;
@@ -500,31 +411,9 @@ void down_fast_kernel(FfnParams P) {
     AF a[NG];
 #pragma unroll
     for (int g = 0; g < NG; ++g) a[g] = *reinterpret_cast<const AF*>(a_row + a_off<FMT>(s0 + g, q));
-    float* s_sc = smem + wave * (16 * NG);
-    float* s_red = smem + (FMT == W_INT4 ? 4 * 16 * NG : 0);
+    float* s_red = smem;   // [3][4][64] when K is split
     f32x4 s_row = {0, 0, 0, 0};
-    if constexpr (FMT == W_INT4) {
-        const int Gr = P.FF / 64;
-        const uint16_t* sc = reinterpret_cast<const uint16_t*>(blob + P.os2);
-        float sv[SPL];
-#pragma unroll
-        for (int m = 0; m < SPL; ++m) {
-            const int idx = lane + 64 * m;
-            sv[m] = 0.0f;
-            if (idx < 16 * NG) {
-                const int i = idx / NG, g = idx - i * NG;
-                sv[m] = bf16_to_f32(sc[static_cast<int64_t>(m0 + i) * Gr + s0 + g]);
-            }
-        }
-#pragma unroll
-        for (int m = 0; m < SPL; ++m) {
-            const int idx = lane + 64 * m;
-            if (idx < 16 * NG) {
-                const int i = idx / NG, g = idx - i * NG;
-                s_sc[g * 16 + i] = sv[m];
-            }
-        }
-    } else if constexpr (FMT == W_INT8) {
+    if constexpr (FMT == W_INT8) {
         s_row = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(blob + P.os2) + m0 + 4 * q);
     }
     const uint16_t* hrow = P.h + static_cast<int64_t>(valid ? p : beg) * P.FF;
@@ -540,14 +429,7 @@ void down_fast_kernel(FfnParams P) {
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
         const u32x4* bg = b[g % D];
-        if constexpr (FMT == W_INT4) {
-            const u32x4 kb = splat(0xC308C308u);
-            f32x4 t = mfma16x16x32(kb, bg[0], zero);
-            t = mfma16x16x32(kb, bg[1], t);
-            t = mfma16x16x32(deq_int4(a[g][0]), bg[0], t);
-            t = mfma16x16x32(deq_int4(a[g][1]), bg[1], t);
-            acc += *reinterpret_cast<const f32x4*>(s_sc + g * 16 + 4 * q) * t;
-        } else if constexpr (FMT == W_INT8) {
+        if constexpr (FMT == W_INT8) {
             const u32x4 kb = splat(0xC300C300u);
             cc = mfma16x16x32(kb, bg[0], cc);
             cc = mfma16x16x32(kb, bg[1], cc);
@@ -814,7 +696,7 @@ constexpr int GUD_RT = 4;   // routes per route tile
 constexpr int GUD_TPW = 1;  // 16-row tiles per workgroup
 
 struct GudLds {             // offsets (bytes) into dynamic LDS
-    int xs, xsum, sc, red, tok, total;
+    int xs, xsum, sc, red, total;
 };
 __host__ __device__ inline GudLds gud_lds(int H) {
     GudLds L;
@@ -823,8 +705,7 @@ __host__ __device__ inline GudLds gud_lds(int H) {
     L.xsum = GUD_RT * (H + 8) * 2;                        // bf16 [2][RT][GS] hi, lo (zero past G)
     L.sc = (L.xsum + 2 * GUD_RT * GS * 2 + 15) & ~15;     // float [4 waves][TPW][NGW][16]
     L.red = L.sc + 4 * GUD_TPW * NGW * 16 * 4;            // float [TPW][3][4][64]
-    L.tok = L.red + GUD_TPW * 3 * 4 * 64 * 4;             // int [RT]
-    L.total = L.tok + GUD_RT * 4;
+    L.total = L.red + GUD_TPW * 3 * 4 * 64 * 4;
     return L;
 }
 
@@ -848,7 +729,6 @@ __global__ __launch_bounds__(256) void gate_up_int4_dec_kernel(FfnParams P) {
     uint16_t* xsum = reinterpret_cast<uint16_t*>(lds + L.xsum);
     float* s_sc = reinterpret_cast<float*>(lds + L.sc) + wave * (GUD_TPW * NGW * 16);
     float* s_red = reinterpret_cast<float*>(lds + L.red);
-    int* toks = reinterpret_cast<int*>(lds + L.tok);
     const int t = wave >> 1, part = wave & 1;
     const int ds0 = part * NDT / KS, nds = (part + 1) * NDT / KS - ds0;
     const int ng = 2 * nds, k0 = 128 * ds0;
@@ -1285,10 +1165,7 @@ FfnWorkspace ffn_workspace(int T, int k, int H, int FF) {
 
 template <int FMT, int KSPLIT>
 static void launch_gate_up_generic(const FfnParams& P, hipStream_t s) {
-    constexpr int KSTEP = Geo<FMT>::KSTEP;
-    const int spw = P.H / KSTEP / KSPLIT;
-    size_t smem = (KSPLIT - 1) * 8 * 64 * sizeof(float);
-    if (FMT == W_INT4) smem += static_cast<size_t>(KSPLIT) * 2 * spw * 16 * sizeof(float);
+    const size_t smem = (KSPLIT - 1) * 8 * 64 * sizeof(float);
     const dim3 grid(P.E * (P.FF / 16)), block(64 * KSPLIT);
     hipLaunchKernelGGL((gate_up_generic_kernel<FMT, KSPLIT, 4>), grid, block, smem, s, P);
 }
@@ -1296,16 +1173,14 @@ static void launch_gate_up_generic(const FfnParams& P, hipStream_t s) {
 // fast-path shapes: (steps per wave, waves splitting K) with steps * waves = the step count
 template <int FMT, int NG, int KSPLIT>
 static void launch_gate_up_fast(const FfnParams& P, hipStream_t s) {
-    size_t smem = (KSPLIT - 1) * 8 * 64 * sizeof(float);
-    if (FMT == W_INT4) smem += static_cast<size_t>(KSPLIT) * 32 * NG * sizeof(float);
+    const size_t smem = (KSPLIT - 1) * 8 * 64 * sizeof(float);
     hipLaunchKernelGGL((gate_up_fast_kernel<FMT, NG, KSPLIT>), dim3(P.E * (P.FF / 16), (P.T + 15) / 16), dim3(64 * KSPLIT),
                        smem, s, P);
 }
 
 template <int FMT, int NG, int KS>
 static void launch_down_fast(const FfnParams& P, hipStream_t s) {
-    size_t smem = (KS > 1 ? 3 * 4 * 64 * sizeof(float) : 0);
-    if (FMT == W_INT4) smem += 4 * 16 * NG * sizeof(float);
+    const size_t smem = (KS > 1 ? 3 * 4 * 64 * sizeof(float) : 0);
     hipLaunchKernelGGL((down_fast_kernel<FMT, NG, KS>), dim3(P.E * (P.H / (16 * (4 / KS))), (P.T + 15) / 16), dim3(256),
                        smem, s, P);
 }
@@ -1343,9 +1218,7 @@ static void launch_phases(const FfnParams& P, int phases, hipStream_t s) {
             launch_gate_up_generic<FMT, 1>(P, s);
     }
     if (phases & 2) {
-        const int nsteps = P.FF / KSTEP;
-        const size_t smem = FMT == W_INT4 ? 4 * static_cast<size_t>(nsteps) * 16 * sizeof(float) : 0;
-        hipLaunchKernelGGL((down_generic_kernel<FMT, 4>), dim3(P.E * (P.H / 64)), dim3(256), smem, s, P);
+        hipLaunchKernelGGL((down_generic_kernel<FMT, 4>), dim3(P.E * (P.H / 64)), dim3(256), 0, s, P);
     }
 }
 
