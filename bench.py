@@ -82,7 +82,8 @@ class StackRunner:
         from expert_ffn_amd.layer import MoeLayer
         self.L = len(logits)
         self.T = T
-        self.ml = MoeLayer(E, k, H, FF, fmt, T, device=pool.device)
+        # per-route outputs in bf16: half the bytes of the down write and the combine read
+        self.ml = MoeLayer(E, k, H, FF, fmt, T, device=pool.device, out_dtype=torch.bfloat16)
         ml = self.ml
         self.slot_d = [torch.from_numpy(slots[l].copy()).to(pool.device) for l in range(self.L)]
         c = lib.lib()
@@ -99,10 +100,10 @@ class StackRunner:
                                            P(ml.n_dropped), s))
             perm = (_no_call, ())
             ffn_args = (P(pool), sb, slot, E, H, FF, fmt, 0, P(xs[l]), 1, T, k, P(ml.offsets),
-                        P(ml.sorted_route), P(ml.out_routes), 0, P(ml.ws), ws, s)
+                        P(ml.sorted_route), P(ml.out_routes), 1, P(ml.ws), ws, s)
             gu = (c.moe_ffn_gate_up, ffn_args)
             dn = (c.moe_ffn_down, ffn_args)
-            comb = (c.moe_combine, (P(ml.out_routes), 0, P(ml.topk_w), P(ml.route_pos), T, k, H,
+            comb = (c.moe_combine, (P(ml.out_routes), 1, P(ml.topk_w), P(ml.route_pos), T, k, H,
                                     P(ml.y), 1, s))
             self.calls.append((route, perm, gu, dn, comb))
         del R
