@@ -333,6 +333,78 @@ def measure_configs(lib, dev, seed, copies=4, reps=20):
     return out
 
 
+def measure_slot_fill(lib, dev, seed, n=64, reps=7):
+    """Slot fill of Gemma-shaped int4 experts (prain README, "int4 experts on
+    RDNA2": one DMA through a pinned buffer, then one unpack kernel).  n
+    distinct canonical blobs (random bytes: the fill moves bytes, their values
+    do not matter) in pinned host memory and in device memory; timed with
+    events on one stream: the plain pinned host -> device copy, the unpack
+    kernel alone (device source), and the whole fill from host (copy into a
+    staging buffer, then the kernel)."""
+    import torch
+    H, FF, fmt = G["H"], G["FF"], lib.W_INT4_G64
+    sb = lib.expert_bytes(fmt, H, FF)
+    g = torch.Generator().manual_seed(seed + 17)
+    host = torch.randint(0, 256, (n, sb), dtype=torch.uint8, generator=g).pin_memory()
+    src = host.to(dev)
+    slots = torch.empty((n, sb), dtype=torch.uint8, device=dev)
+    staging = torch.empty((2, sb), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.Stream()
+
+    def timed(body):   # median over passes of us per expert
+        with torch.cuda.stream(stream):
+            body()
+            torch.cuda.synchronize()
+            ts = []
+            for _ in range(reps):
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                body()
+                b.record(stream)
+                torch.cuda.synchronize()
+                ts.append(a.elapsed_time(b) * 1e3 / n)
+        return float(np.median(ts))
+
+    def copy_only():
+        for i in range(n):
+            staging[i & 1].copy_(host[i], non_blocking=True)
+
+    def unpack_only():
+        for i in range(n):
+            lib.fill_slot(fmt, src[i], H, FF, slots[i], stream=stream)
+
+    def fill_from_host():
+        for i in range(n):
+            lib.fill_slot(fmt, host[i], H, FF, slots[i], staging=staging[i & 1], stream=stream)
+
+    def fill_direct():
+        for i in range(n):
+            lib.fill_slot(fmt, host[i], H, FF, slots[i], stream=stream, direct=True)
+
+    # interleaved rounds, median of the round medians (the bus is shared and noisy)
+    runs = {f: [] for f in (copy_only, unpack_only, fill_from_host, fill_direct)}
+    for _ in range(3):
+        for f in runs:
+            runs[f].append(timed(f))
+    t_copy, t_unpack, t_fill, t_direct = (float(np.median(v)) for v in runs.values())
+    # every fill must reproduce the device-source result byte for byte
+    check = slots.clone()
+    with torch.cuda.stream(stream):
+        unpack_only()
+    torch.cuda.synchronize()
+    same = bool(torch.equal(check, slots))
+    return dict(metric="int4 expert slot fill", unit="GB/s", config=dict(
+                    workload=f"Gemma-4-26B-A4B int4 expert (H={H}, FF={FF}), {n} experts per pass"),
+                expert_bytes=sb, h2d_GBps=round(sb / (t_copy * 1e-6) / 1e9, 2),
+                unpack_hbm_GBps=round(2 * sb / (t_unpack * 1e-6) / 1e9, 1),
+                unpack_us_per_expert=round(t_unpack, 2), h2d_us_per_expert=round(t_copy, 2),
+                fill_from_host_us_per_expert=round(t_fill, 2),
+                fill_from_host_GBps=round(sb / (t_fill * 1e-6) / 1e9, 2),
+                fill_direct_us_per_expert=round(t_direct, 2),
+                fill_direct_GBps=round(sb / (t_direct * 1e-6) / 1e9, 2),
+                fills_agree=same)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -353,6 +425,8 @@ def main():
     ap.add_argument("--configs", action="store_true",
                     help="instead of the stack step: single-layer timings of the other workloads "
                          "(one JSON object per line)")
+    ap.add_argument("--slot-fill", action="store_true",
+                    help="instead of the stack step: int4 expert slot fill rates (one JSON line)")
     args = ap.parse_args()
     if args.summarize_pmc:
         summarize_pmc(*args.summarize_pmc, commands=args.command)
@@ -370,6 +444,9 @@ def main():
     import expert_ffn_amd as lib
     lib.lib()
     dev = torch.device("cuda:0")
+    if args.slot_fill:
+        print(json.dumps(measure_slot_fill(lib, dev, args.seed)), flush=True)
+        return
     if args.configs:
         for r in measure_configs(lib, dev, args.seed):
             print(json.dumps(r), flush=True)

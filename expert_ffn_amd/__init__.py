@@ -52,9 +52,13 @@ def lib():
         L.moe_quantize.argtypes = [i32, P, i32, i32, P, P, P]
         L.moe_pack_expert.argtypes = [i32, P, P, i32, i32, P, P]
         L.moe_set_ffn_path.argtypes = [i32]
+        L.moe_fill_slot.argtypes = [i32, P, i32, i32, i32, P, P, P]
+        L.moe_verify_slot.argtypes = [i32, P, i32, i32, P, P, P]
+        L.moe_slot_admit.argtypes = [P, i32, P, i32, i32]
         for name in ("moe_blob_layout", "moe_route_topk", "moe_permute", "moe_route_permute", "moe_expert_ffn",
                      "moe_ffn_gate_up", "moe_ffn_down", "moe_combine", "moe_quantize",
-                     "moe_pack_expert", "moe_set_ffn_path"):
+                     "moe_pack_expert", "moe_set_ffn_path", "moe_fill_slot", "moe_verify_slot",
+                     "moe_slot_admit"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -170,3 +174,28 @@ def pack_expert(fmt: int, w13_bf16, w2_bf16, blob, stream=None):
     FF = w2_bf16.shape[1]
     _check(lib().moe_pack_expert(fmt, _ptr(w13_bf16), _ptr(w2_bf16), H, FF, _ptr(blob),
                                  _stream(stream)))
+
+
+def fill_slot(fmt: int, src, H: int, FF: int, slot, staging=None, stream=None, direct=False):
+    """Canonical blob src (host: one copy into staging, then the unpack kernel,
+    or with direct=True the kernel reading the pinned blob itself; device: the
+    kernel alone) -> slot, byte for byte the packed blob."""
+    on_host = 0 if src.is_cuda else (2 if direct else 1)
+    _check(lib().moe_fill_slot(fmt, _ptr(src), on_host, H, FF, _ptr(staging), _ptr(slot), _stream(stream)))
+
+
+def verify_slot(fmt: int, src, H: int, FF: int, slot, mismatches, stream=None):
+    """mismatches[0] <- 16-byte chunks of slot that differ from the fill of src."""
+    _check(lib().moe_verify_slot(fmt, _ptr(src), H, FF, _ptr(slot), _ptr(mismatches), _stream(stream)))
+
+
+def slot_admit(slot_of, owner, expert: int) -> int:
+    """Host int32 tables slot_of [E], owner [S]: expert's slot, claiming the
+    lowest free one if it is not resident; raises when none is free."""
+    import torch
+    assert slot_of.dtype == torch.int32 and owner.dtype == torch.int32
+    assert not slot_of.is_cuda and not owner.is_cuda and slot_of.is_contiguous() and owner.is_contiguous()
+    j = lib().moe_slot_admit(_ptr(slot_of), slot_of.numel(), _ptr(owner), owner.numel(), expert)
+    if j < 0:
+        raise MoeError(1, lib().moe_last_error().decode())
+    return j

@@ -34,6 +34,12 @@ bool dt_ok(int32_t d) { return d == MOE_F32 || d == MOE_BF16; }
 
 uint64_t up256(uint64_t x) { return (x + 255u) / 256u * 256u; }
 
+bool overlap(const void* a, const void* b, uint64_t n) {
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return x < y + n && y < x + n;
+}
+bool al16(const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; }
+
 // layout of a blob; false if the shape does not fit the format
 bool layout(int32_t wfmt, int32_t H, int32_t FF, uint64_t* off) {
     if (H < 1 || FF < 1 || !fmt_ok(wfmt)) return false;
@@ -262,6 +268,71 @@ moe_status moe_pack_expert(int32_t wfmt, const uint16_t* w13_bf16, const uint16_
     e = moe::launch_quantize(wfmt, w13_bf16, 2 * FF, H, b + off[0], b + off[1], true, s);
     if (e == hipSuccess) e = moe::launch_quantize(wfmt, w2_bf16, H, FF, b + off[2], b + off[3], true, s);
     return hip_status(fn, e);
+}
+
+moe_status moe_fill_slot(int32_t wfmt, const void* src, int32_t src_on_host, int32_t H, int32_t FF,
+                         void* staging, void* slot, void* stream) {
+    const char* fn = "moe_fill_slot";
+    if (!src || !slot) return fail(MOE_E_ARG, fn, "null pointer argument");
+    if (!fmt_ok(wfmt)) return fail(MOE_E_ARG, fn, "unknown weight format %d", wfmt);
+    uint64_t off[5];
+    if (!layout(wfmt, H, FF, off)) return fail(MOE_E_SHAPE, fn, "H=%d FF=%d invalid for format %d", H, FF, wfmt);
+    if (off[4] >= (1ull << 31)) return fail(MOE_E_SHAPE, fn, "blob of %llu bytes is not below 2 GiB",
+                                            static_cast<unsigned long long>(off[4]));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const void* dev = src;
+    if (src_on_host == 2) {
+        // the kernel reads the pinned host blob itself (its device-side mapping)
+        void* mapped = nullptr;
+        if (hipHostGetDevicePointer(&mapped, const_cast<void*>(src), 0) != hipSuccess || !mapped) {
+            (void)hipGetLastError();
+            return fail(MOE_E_ARG, fn, "src is not pinned (hipHostMalloc) host memory");
+        }
+        if (!al16(mapped) || !al16(slot)) return fail(MOE_E_ARG, fn, "src and slot must be 16-byte aligned");
+        dev = mapped;
+    } else if (src_on_host) {
+        if (!staging) return fail(MOE_E_ARG, fn, "a host source needs a device staging buffer");
+        if (!al16(staging) || !al16(slot)) return fail(MOE_E_ARG, fn, "staging and slot must be 16-byte aligned");
+        if (overlap(staging, slot, off[4])) return fail(MOE_E_ARG, fn, "staging overlaps the slot");
+        const hipError_t e = hipMemcpyAsync(staging, src, off[4], hipMemcpyHostToDevice, s);
+        if (e != hipSuccess) return hip_status(fn, e);
+        dev = staging;
+    } else {
+        if (!al16(src) || !al16(slot)) return fail(MOE_E_ARG, fn, "src and slot must be 16-byte aligned");
+        if (overlap(src, slot, off[4])) return fail(MOE_E_ARG, fn, "src overlaps the slot");
+    }
+    return hip_status(fn, moe::launch_fill_slot(wfmt, dev, src_on_host == 2, H, FF, off, slot, s));
+}
+
+moe_status moe_verify_slot(int32_t wfmt, const void* src, int32_t H, int32_t FF, const void* slot,
+                           int32_t* mismatches, void* stream) {
+    const char* fn = "moe_verify_slot";
+    if (!src || !slot || !mismatches) return fail(MOE_E_ARG, fn, "null pointer argument");
+    if (!fmt_ok(wfmt)) return fail(MOE_E_ARG, fn, "unknown weight format %d", wfmt);
+    uint64_t off[5];
+    if (!layout(wfmt, H, FF, off)) return fail(MOE_E_SHAPE, fn, "H=%d FF=%d invalid for format %d", H, FF, wfmt);
+    if (off[4] >= (1ull << 31)) return fail(MOE_E_SHAPE, fn, "blob of %llu bytes is not below 2 GiB",
+                                            static_cast<unsigned long long>(off[4]));
+    if (!al16(src) || !al16(slot)) return fail(MOE_E_ARG, fn, "src and slot must be 16-byte aligned");
+    if (reinterpret_cast<uintptr_t>(mismatches) % 4) return fail(MOE_E_ARG, fn, "mismatches must be 4-byte aligned");
+    return hip_status(fn, moe::launch_verify_slot(wfmt, src, H, FF, off, slot, mismatches,
+                                                  static_cast<hipStream_t>(stream)));
+}
+
+int32_t moe_slot_admit(int32_t* slot_of, int32_t E, int32_t* owner, int32_t S, int32_t expert) {
+    const char* fn = "moe_slot_admit";
+    if (!slot_of || !owner) return fail(MOE_E_ARG, fn, "null pointer argument"), -1;
+    if (E < 1 || S < 0 || expert < 0 || expert >= E)
+        return fail(MOE_E_ARG, fn, "expert=%d outside [0, E=%d) or S=%d < 0", expert, E, S), -1;
+    const int32_t cur = slot_of[expert];
+    if (cur >= 0 && cur < S && owner[cur] == expert) return cur;
+    for (int32_t j = 0; j < S; ++j)
+        if (owner[j] < 0) {
+            owner[j] = expert;
+            slot_of[expert] = j;
+            return j;
+        }
+    return fail(MOE_E_ARG, fn, "no free slot among %d", S), -1;
 }
 
 }  // extern "C"

@@ -16,6 +16,14 @@ hipError_t launch_route_permute(const float* logits, int T, int E, int k, int re
                                 int* n_dropped, hipStream_t s);
 hipError_t launch_combine(const void* out_routes, int out_dt, const float* w, const int* route_pos,
                           int T, int k, int H, void* y, int y_dt, hipStream_t s);
+// canonical blob (int4 codes row-major) at src (device, or with host_src the
+// device mapping of pinned host memory) -> slot blob (int4 codes tiled);
+// off: the blob layout (5 entries, host)
+hipError_t launch_fill_slot(int fmt, const void* src, bool host_src, int H, int FF, const uint64_t* off, void* slot,
+                            hipStream_t s);
+// mismatches (device): 16-byte chunks of slot that differ from the canonical blob src
+hipError_t launch_verify_slot(int fmt, const void* src, int H, int FF, const uint64_t* off, const void* slot,
+                              int32_t* mismatches, hipStream_t s);
 // tiled: int4 codes in the blob's 32-row tiles (N a multiple of 32), else row-major
 hipError_t launch_quantize(int fmt, const uint16_t* w, int N, int K, void* q, void* scales, bool tiled,
                            hipStream_t s);

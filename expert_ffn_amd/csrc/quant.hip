@@ -81,6 +81,89 @@ __global__ __launch_bounds__(256) void quant_int4_kernel(const uint16_t* __restr
     }
 }
 
+// Canonical expert -> slot (prain README, "int4 experts on RDNA2": one unpack
+// kernel per expert copy): one pass over the blob in 16-byte chunks.  A chunk
+// of an int4 nibble block (rows of K / 2 bytes, a multiple of 32, so a chunk
+// never crosses a row or a 64-group) moves to its place in the 32-row tiles;
+// every other chunk (scales, padding, bf16 and int8 weights) keeps its offset.
+struct SlotMap {
+    uint32_t nchunks;     // blob bytes / 16
+    uint32_t o13, e13;    // w13 nibble block [o13, e13) (empty unless int4)
+    uint32_t rb13;        // its row bytes (H / 2)
+    uint32_t o2, e2, rb2; // the same for w2 (row bytes FF / 2)
+};
+
+__device__ __forceinline__ uint32_t slot_chunk(const SlotMap& m, uint32_t i) {
+    const uint32_t b = i * 16;
+    if (b >= m.o13 && b < m.e13) {
+        const uint32_t r = b - m.o13, n = r / m.rb13;
+        return (m.o13 + static_cast<uint32_t>(int4_code_off(n, m.rb13 / 32, r - n * m.rb13))) / 16;
+    }
+    if (b >= m.o2 && b < m.e2) {
+        const uint32_t r = b - m.o2, n = r / m.rb2;
+        return (m.o2 + static_cast<uint32_t>(int4_code_off(n, m.rb2 / 32, r - n * m.rb2))) / 16;
+    }
+    return i;
+}
+
+// HOST_SRC: src is the device mapping of pinned host memory (same code; a
+// separate instance so that traces tell the bus-bound fills apart)
+template <bool HOST_SRC>
+__global__ __launch_bounds__(256) void fill_slot_kernel(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
+                                                        SlotMap m) {
+    const uint32_t i = blockIdx.x * 256 + threadIdx.x;
+    if (i < m.nchunks) dst[slot_chunk(m, i)] = src[i];
+}
+
+// count of 16-byte chunks of the slot that differ from the canonical blob
+__global__ __launch_bounds__(256) void verify_slot_kernel(const u32x4* __restrict__ src,
+                                                          const u32x4* __restrict__ slot, SlotMap m,
+                                                          int32_t* __restrict__ bad) {
+    const uint32_t i = blockIdx.x * 256 + threadIdx.x;
+    bool diff = false;
+    if (i < m.nchunks) {
+        const u32x4 a = src[i], c = slot[slot_chunk(m, i)];
+        diff = a[0] != c[0] || a[1] != c[1] || a[2] != c[2] || a[3] != c[3];
+    }
+    const uint64_t v = __ballot(diff);
+    if (v && (threadIdx.x & 63) == 0) atomicAdd(bad, __popcll(v));
+}
+
+__global__ void zero_i32_kernel(int32_t* p) { *p = 0; }
+
+static SlotMap slot_map(int fmt, int H, int FF, const uint64_t* off) {
+    SlotMap m{};
+    m.nchunks = static_cast<uint32_t>(off[4] / 16);
+    if (fmt == W_INT4) {
+        m.o13 = static_cast<uint32_t>(off[0]);
+        m.e13 = m.o13 + static_cast<uint32_t>(FF) * H;   // 2FF rows of H / 2 bytes
+        m.rb13 = H / 2;
+        m.o2 = static_cast<uint32_t>(off[2]);
+        m.e2 = m.o2 + static_cast<uint32_t>(H) * (FF / 2);
+        m.rb2 = FF / 2;
+    } else {
+        m.rb13 = m.rb2 = 32;
+    }
+    return m;
+}
+
+hipError_t launch_fill_slot(int fmt, const void* src, bool host_src, int H, int FF, const uint64_t* off, void* slot,
+                            hipStream_t s) {
+    const SlotMap m = slot_map(fmt, H, FF, off);
+    hipLaunchKernelGGL(host_src ? fill_slot_kernel<true> : fill_slot_kernel<false>, dim3((m.nchunks + 255) / 256),
+                       dim3(256), 0, s, static_cast<const u32x4*>(src), static_cast<u32x4*>(slot), m);
+    return hipGetLastError();
+}
+
+hipError_t launch_verify_slot(int fmt, const void* src, int H, int FF, const uint64_t* off, const void* slot,
+                              int32_t* mismatches, hipStream_t s) {
+    const SlotMap m = slot_map(fmt, H, FF, off);
+    hipLaunchKernelGGL(zero_i32_kernel, dim3(1), dim3(1), 0, s, mismatches);
+    hipLaunchKernelGGL(verify_slot_kernel, dim3((m.nchunks + 255) / 256), dim3(256), 0, s,
+                       static_cast<const u32x4*>(src), static_cast<const u32x4*>(slot), m, mismatches);
+    return hipGetLastError();
+}
+
 hipError_t launch_quantize(int fmt, const uint16_t* w, int N, int K, void* q, void* scales, bool tiled,
                            hipStream_t s) {
     if (N <= 0 || K <= 0) return hipSuccess;

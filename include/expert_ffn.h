@@ -228,6 +228,53 @@ moe_status moe_pack_expert(int32_t wfmt, const uint16_t* w13_bf16, const uint16_
                            int32_t H, int32_t FF, void* blob, void* stream);
 
 /*
+ * Slot fill: make an expert resident (prain README, "int4 experts on RDNA2":
+ * each int4 expert copy is one DMA through a pinned staging buffer and one
+ * unpack kernel; Winery-Strata's ExpertCache fills and checks slots the same
+ * way, admit / fill_slot_blocking / verify_slot).
+ *
+ * The canonical form of an expert -- what a pack file or host cache holds --
+ * is the blob layout of moe_blob_layout with the int4 code blocks row-major
+ * (byte b of row n at n * K/2 + b, as moe_quantize writes them); bf16 and int8
+ * blobs are the same in both forms.  moe_fill_slot writes the slot form:
+ *   src_on_host != 0: src is the canonical blob in host memory (pinned,
+ *     hipHostMalloc, for an asynchronous copy; pageable memory works but the
+ *     runtime copies it synchronously); one host-to-device copy of
+ *     moe_expert_bytes() bytes into staging (device, caller-owned, at least
+ *     that size, 16-byte aligned, not overlapping slot), then one kernel that
+ *     writes slot from staging.
+ *   src_on_host == 2: src is the canonical blob in pinned host memory
+ *     (hipHostMalloc; anything else returns MOE_E_ARG); no copy: the kernel
+ *     reads it over the bus through its device mapping.  staging is unused.
+ *   src_on_host == 0: src is the canonical blob in device memory (16-byte
+ *     aligned, not overlapping slot); staging is unused and may be NULL.
+ * slot (device, 16-byte aligned, moe_expert_bytes() bytes) receives the blob
+ * byte for byte as moe_pack_expert would write it from the same weights.
+ * src and staging must stay valid until the stream reaches the copy and the
+ * kernel.  Blobs of 2 GiB or more return MOE_E_SHAPE.
+ */
+moe_status moe_fill_slot(int32_t wfmt, const void* src, int32_t src_on_host, int32_t H, int32_t FF,
+                         void* staging, void* slot, void* stream);
+
+/*
+ * Check a filled slot against the canonical blob src (both device, 16-byte
+ * aligned): *mismatches (device int32, overwritten) receives the number of
+ * 16-byte chunks of the slot that differ from what moe_fill_slot writes.
+ */
+moe_status moe_verify_slot(int32_t wfmt, const void* src, int32_t H, int32_t FF, const void* slot,
+                           int32_t* mismatches, void* stream);
+
+/*
+ * Host bookkeeping of a layer's expert -> slot table (host arrays): slot_of
+ * [E] (-1 = not resident) and owner [S] (the expert in each slot, -1 = free).
+ * Returns expert's slot when it is already resident, else claims the lowest
+ * free slot (updating both tables), else returns -1 (moe_last_error says why;
+ * also -1 for bad arguments).  Eviction is the caller's: set owner[j] and
+ * slot_of[owner[j]] to -1.  The device copy of slot_of is the caller's.
+ */
+int32_t moe_slot_admit(int32_t* slot_of, int32_t E, int32_t* owner, int32_t S, int32_t expert);
+
+/*
  * Kernel family moe_expert_ffn uses: 0 = by token count (default), 1 = the
  * streaming kernels for small per-expert groups, 2 = the LDS-tiled kernels for
  * large groups.  Process-wide setting for tests and measurement; not

@@ -63,6 +63,10 @@ def _declare(L):
     L.oracle_blob_layout.restype = ctypes.c_int
     L.oracle_pack_expert.argtypes = [i32, P, P, i32, i32, P]
     L.oracle_pack_expert.restype = ctypes.c_int
+    L.oracle_pack_expert_canonical.argtypes = [i32, P, P, i32, i32, P]
+    L.oracle_pack_expert_canonical.restype = ctypes.c_int
+    L.oracle_fill_slot.argtypes = [i32, P, i32, i32, P]
+    L.oracle_fill_slot.restype = ctypes.c_int
     L.oracle_dequant.argtypes = [P, i32, i32, i32, i32, P]
     L.oracle_dequant.restype = ctypes.c_int
     L.oracle_act.argtypes = [i32, P, P, i64]
@@ -158,6 +162,25 @@ def pack_expert(fmt: int, w13_bf16, w2_bf16, H: int, FF: int) -> np.ndarray:
     blob = np.empty(expert_bytes(fmt, H, FF), dtype=np.uint8)
     _check(lib().oracle_pack_expert(fmt, _p(w13), _p(w2), H, FF, _p(blob)), "pack_expert")
     return blob
+
+
+def pack_expert_canonical(fmt: int, w13_bf16, w2_bf16, H: int, FF: int) -> np.ndarray:
+    """The expert's canonical form: the blob layout with int4 codes row-major."""
+    w13 = np.ascontiguousarray(w13_bf16, dtype=np.uint16)
+    w2 = np.ascontiguousarray(w2_bf16, dtype=np.uint16)
+    assert w13.shape == (2 * FF, H) and w2.shape == (H, FF)
+    blob = np.empty(expert_bytes(fmt, H, FF), dtype=np.uint8)
+    _check(lib().oracle_pack_expert_canonical(fmt, _p(w13), _p(w2), H, FF, _p(blob)), "pack_expert_canonical")
+    return blob
+
+
+def fill_slot(fmt: int, canonical, H: int, FF: int) -> np.ndarray:
+    """Canonical form -> the slot form the kernels read."""
+    src = np.ascontiguousarray(canonical, dtype=np.uint8)
+    assert src.size == expert_bytes(fmt, H, FF)
+    slot = np.empty_like(src)
+    _check(lib().oracle_fill_slot(fmt, _p(src), H, FF, _p(slot)), "fill_slot")
+    return slot
 
 
 def dequant(blob, fmt: int, H: int, FF: int, which: int) -> np.ndarray:

@@ -347,6 +347,41 @@ int oracle_pack_expert(int32_t fmt, const uint16_t* w13, const uint16_t* w2, int
     return ORA_OK;
 }
 
+/* ------------------------------------------------------------ slot fill --
+ * [prain] "int4 experts on RDNA2": an expert copied into a cache slot goes
+ * through a staging buffer and one unpack step.  The canonical form of an
+ * expert is the blob layout above with the int4 nibble blocks row-major (byte b
+ * of row n at n * K/2 + b, as oracle_quantize_int4 writes them); the slot form
+ * is the tiled one.  bf16 and int8 blobs are the same in both forms.
+ */
+int oracle_pack_expert_canonical(int32_t fmt, const uint16_t* w13, const uint16_t* w2, int32_t H, int32_t FF,
+                                 uint8_t* blob)
+{
+    uint64_t off[5];
+    if (oracle_blob_layout(fmt, H, FF, off) != ORA_OK) return ORA_EARG;
+    if (fmt != ORA_W_INT4_G64) return oracle_pack_expert(fmt, w13, w2, H, FF, blob);
+    memset(blob, 0, off[4]);
+    oracle_quantize_int4(w13, 2 * FF, H, blob + off[0], (uint16_t*)(blob + off[1]));
+    oracle_quantize_int4(w2, H, FF, blob + off[2], (uint16_t*)(blob + off[3]));
+    return ORA_OK;
+}
+
+/* canonical blob -> slot blob: the nibble blocks tiled, every other byte as it is */
+int oracle_fill_slot(int32_t fmt, const uint8_t* canonical, int32_t H, int32_t FF, uint8_t* slot)
+{
+    uint64_t off[5];
+    if (oracle_blob_layout(fmt, H, FF, off) != ORA_OK) return ORA_EARG;
+    memcpy(slot, canonical, off[4]);
+    if (fmt != ORA_W_INT4_G64) return ORA_OK;
+    for (int which = 0; which < 2; ++which) {
+        const int32_t N = which ? H : 2 * FF, K = which ? FF : H;
+        const uint64_t o = which ? off[2] : off[0];
+        for (int32_t n = 0; n < N; ++n)
+            for (int32_t b = 0; b < K / 2; ++b) slot[o + int4_tiled(n, K, b)] = canonical[o + (int64_t)n * (K / 2) + b];
+    }
+    return ORA_OK;
+}
+
 /* ---------------------------------------------------------- dequantised --
  * The weight a packed blob stands for, as the format defines it:
  *   bf16: the bf16 value;  int8: s_row * q;  int4: s_(row,group) * (u - 8).

@@ -86,6 +86,35 @@ def test_host_validation_errors(L):
     assert rc == 2 and "H=60" in msg
     rc, msg = _call(L, "moe_set_ffn_path", 3)
     assert rc == 1
+    rc, msg = _call(L, "moe_fill_slot", 2, fake, 1, 2816, 704, None, fake, None)
+    assert rc == 1 and "staging" in msg
+    rc, msg = _call(L, "moe_fill_slot", 2, fake, 0, 2816, 704, None, fake, None)
+    assert rc == 1 and "overlaps" in msg
+    rc, msg = _call(L, "moe_fill_slot", 2, fake, 0, 2816, 700, None, P(1 << 30), None)
+    assert rc == 2 and "FF=700" in msg
+    rc, msg = _call(L, "moe_fill_slot", 1, P((1 << 20) + 8), 0, 2816, 704, None, P(1 << 30), None)
+    assert rc == 1 and "aligned" in msg
+    rc, msg = _call(L, "moe_verify_slot", 2, fake, 2816, 704, fake, None, None)
+    assert rc == 1
+
+
+def test_slot_admit_claims_the_lowest_free_slot(L):
+    import torch
+    E, S = 6, 3
+    slot_of = torch.full((E,), -1, dtype=torch.int32)
+    owner = torch.full((S,), -1, dtype=torch.int32)
+    assert L.slot_admit(slot_of, owner, 4) == 0
+    assert L.slot_admit(slot_of, owner, 1) == 1
+    assert L.slot_admit(slot_of, owner, 4) == 0          # already resident
+    owner[0] = -1                                        # evict expert 4
+    slot_of[4] = -1
+    assert L.slot_admit(slot_of, owner, 5) == 0
+    assert L.slot_admit(slot_of, owner, 2) == 2
+    with pytest.raises(L.MoeError, match="no free slot"):
+        L.slot_admit(slot_of, owner, 3)
+    assert slot_of.tolist() == [-1, 1, 2, -1, -1, 0] and owner.tolist() == [5, 1, 2]
+    with pytest.raises(L.MoeError):
+        L.slot_admit(slot_of, owner, 6)
 
 
 def test_workspace_grows_with_tokens(L):

@@ -337,3 +337,42 @@ def test_quantize_bit_exact_specials(L):
         torch.cuda.synchronize()
         assert np.array_equal(to_np(q).view(rq.dtype), rq)
         assert np.array_equal(to_np(s).view(rs.dtype), rs)
+
+
+@pytest.mark.parametrize("fmt", [0, 1, 2])
+@pytest.mark.parametrize("H,FF", [(128, 192), (2816, 704)])
+def test_fill_slot_bit_exact(L, fmt, H, FF):
+    # canonical blob (the oracle's) -> slot, from pinned host memory through a
+    # staging buffer and from device memory: every byte equals the oracle's
+    # packed blob; verify_slot counts 0, then 1 after one corrupted byte
+    import oracle as ora
+    log(f"fill_slot fmt={fmt} H={H} FF={FF}")
+    w13, w2 = synth.expert_weights(21, 0, 3, H, FF)
+    canon = ora.pack_expert_canonical(fmt, w13, w2, H, FF)
+    want = ora.pack_expert(fmt, w13, w2, H, FF)
+    sb = L.expert_bytes(fmt, H, FF)
+    pool = torch.full((3 * sb,), 0xAB, dtype=torch.uint8, device="cuda")
+    src_h = torch.from_numpy(canon).pin_memory()
+    staging = torch.empty(sb, dtype=torch.uint8, device="cuda")
+    L.fill_slot(fmt, src_h, H, FF, pool[sb:2 * sb], staging=staging)
+    src_d = torch.from_numpy(canon).cuda()
+    L.fill_slot(fmt, src_d, H, FF, pool[2 * sb:])
+    torch.cuda.synchronize()
+    got = to_np(pool)
+    assert np.array_equal(got[sb:2 * sb], want)
+    assert np.array_equal(got[2 * sb:], want)
+    assert (got[:sb] == 0xAB).all()                     # nothing written outside the slots
+    L.fill_slot(fmt, src_h, H, FF, pool[:sb], direct=True)   # the kernel reads the pinned blob
+    torch.cuda.synchronize()
+    assert np.array_equal(to_np(pool[:sb]), want)
+    with pytest.raises(L.MoeError, match="pinned"):
+        L.fill_slot(fmt, torch.from_numpy(canon), H, FF, pool[:sb], direct=True)
+    bad = torch.full((1,), -7, dtype=torch.int32, device="cuda")
+    L.verify_slot(fmt, src_d, H, FF, pool[sb:2 * sb], bad)
+    torch.cuda.synchronize()
+    assert int(bad.item()) == 0
+    off = L.blob_layout(fmt, H, FF)
+    pool[sb + off[2] + 5] ^= 1                          # one byte of the w2 block
+    L.verify_slot(fmt, src_d, H, FF, pool[sb:2 * sb], bad)
+    torch.cuda.synchronize()
+    assert int(bad.item()) == 1

@@ -149,6 +149,48 @@ def test_int4_blob_tiles_the_row_major_codes(ora):
         assert np.array_equal(blob[o_scales:o_scales + N * K // 32].view(np.uint16).reshape(N, K // 64), sc)
 
 
+@pytest.mark.parametrize("fmt", [0, 1, 2])
+def test_slot_fill_of_the_canonical_form_is_the_packed_blob(ora, fmt):
+    # canonical form: the blob layout with the int4 codes as the quantiser
+    # writes them (row-major); filling a slot from it gives the packed blob
+    H, FF = 128, 192
+    r = np.random.default_rng(12 + fmt)
+    w13 = synth.to_bf16_bits(r.normal(0, 0.02, (2 * FF, H)).astype(np.float32))
+    w2 = synth.to_bf16_bits(r.normal(0, 0.02, (H, FF)).astype(np.float32))
+    canon = ora.pack_expert_canonical(fmt, w13, w2, H, FF)
+    off = ora.blob_layout(fmt, H, FF)
+    assert canon.size == off[4] == ora.expert_bytes(fmt, H, FF)
+    if fmt == 2:
+        for w, o_codes, o_scales in ((w13, off[0], off[1]), (w2, off[2], off[3])):
+            N, K = w.shape
+            q, sc = ora.quantize_int4(w)
+            assert np.array_equal(canon[o_codes:o_codes + N * K // 2].reshape(N, K // 2), q)
+            assert np.array_equal(canon[o_scales:o_scales + N * K // 32].view(np.uint16).reshape(N, K // 64), sc)
+        # padding between the blocks is zero
+        used = np.zeros(off[4], bool)
+        for o, n in ((off[0], 2 * FF * H // 2), (off[1], 2 * FF * H // 32), (off[2], H * FF // 2), (off[3], H * FF // 32)):
+            used[o:o + n] = True
+        assert not canon[~used].any()
+    else:
+        assert np.array_equal(canon, ora.pack_expert(fmt, w13, w2, H, FF))
+    assert np.array_equal(ora.fill_slot(fmt, canon, H, FF), ora.pack_expert(fmt, w13, w2, H, FF))
+
+
+def test_slot_fill_moves_each_int4_code_byte_once(ora):
+    # a position-dependent byte pattern: each code byte lands where the tile
+    # formula says; scales and padding are copied as they are
+    H, FF = 128, 64
+    off = ora.blob_layout(2, H, FF)
+    canon = (np.arange(off[4], dtype=np.int64) * 7 % 251).astype(np.uint8)
+    slot = ora.fill_slot(2, canon, H, FF)
+    for o, N, K in ((off[0], 2 * FF, H), (off[2], H, FF)):
+        rm = canon[o:o + N * K // 2].reshape(N, K // 2)
+        t = slot[o:o + N * K // 2].reshape(N // 32, K // 64, 32, 32).transpose(0, 2, 1, 3).reshape(N, K // 2)
+        assert np.array_equal(t, rm)
+    assert np.array_equal(slot[off[1]:off[2]], canon[off[1]:off[2]])
+    assert np.array_equal(slot[off[3]:], canon[off[3]:])
+
+
 # ----------------------------------------------------------- activation ----
 def test_activations_match_torch(ora):
     g = np.linspace(-12, 12, 4001)
