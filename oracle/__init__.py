@@ -67,6 +67,8 @@ def _declare(L):
     L.oracle_pack_expert_canonical.restype = ctypes.c_int
     L.oracle_fill_slot.argtypes = [i32, P, i32, i32, P]
     L.oracle_fill_slot.restype = ctypes.c_int
+    L.oracle_min_weight.argtypes = [P, P, i32, i32, i32, P, ctypes.c_float, P, P, P]
+    L.oracle_min_weight.restype = ctypes.c_int
     L.oracle_dequant.argtypes = [P, i32, i32, i32, i32, P]
     L.oracle_dequant.restype = ctypes.c_int
     L.oracle_act.argtypes = [i32, P, P, i64]
@@ -181,6 +183,22 @@ def fill_slot(fmt: int, canonical, H: int, FF: int) -> np.ndarray:
     slot = np.empty_like(src)
     _check(lib().oracle_fill_slot(fmt, _p(src), H, FF, _p(slot)), "fill_slot")
     return slot
+
+
+def min_weight(ids, w, E: int, slot_of, share: float):
+    """[prain] "Trading quality for speed": (ids_out, w_out, miss_count) for
+    routes ids/w [T, k] at min_weight = share (fp32)."""
+    ids = np.ascontiguousarray(ids, dtype=np.int32)
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    slot_of = np.ascontiguousarray(slot_of, dtype=np.int32)
+    T, k = ids.shape
+    assert w.shape == (T, k) and slot_of.shape == (E,)
+    ids_out = np.empty_like(ids)
+    w_out = np.empty_like(w)
+    miss = np.empty(E, dtype=np.int32)
+    _check(lib().oracle_min_weight(_p(ids), _p(w), T, k, E, _p(slot_of), float(np.float32(share)), _p(ids_out),
+                                   _p(w_out), _p(miss)), "min_weight")
+    return ids_out, w_out, miss
 
 
 def dequant(blob, fmt: int, H: int, FF: int, which: int) -> np.ndarray:

@@ -174,6 +174,70 @@ int oracle_permute(const int32_t* ids, int32_t T, int32_t k, int32_t E, const in
     return ORA_OK;
 }
 
+/* ------------------------------------------------- min_weight routing --
+ * [prain] "Trading quality for speed": min_weight is the share of a token's
+ * router weight that must be computed.  Below 1 the token skips its lightest
+ * experts that are not resident once the share is reached, and the routes it
+ * keeps are scaled up to its full weight.  Readings (the page states the rule,
+ * not its arithmetic):
+ *   - the token's weight W = sum of its k weights; resident routes are always
+ *     kept; the others are taken heaviest first (equal weights: lower j first)
+ *     while the kept weight c is below min_weight * W, the rest skipped;
+ *   - kept routes are scaled by W / c when something was skipped; min_weight
+ *     >= 1 keeps every route unchanged (the hot path);
+ *   - routes with ids outside [0, E) are skipped and not counted in W;
+ *   - all of it in fp32 (the decision is a float comparison; both sides take
+ *     it in the kernel's precision), sums in the order just stated.
+ * Outputs: ids_out (skipped: -1), w_out (skipped: 0), and miss_count[e], the
+ * number of kept routes to a non-resident expert e (the copies a step needs).
+ */
+int oracle_min_weight(const int32_t* ids, const float* w, int32_t T, int32_t k, int32_t E, const int32_t* slot_of,
+                      float min_weight, int32_t* ids_out, float* w_out, int32_t* miss_count)
+{
+    if (!ids || !w || !slot_of || !ids_out || !w_out || !miss_count || T < 0 || k < 1 || k > 32 || E < 1)
+        return ORA_EARG;
+    for (int32_t e = 0; e < E; ++e) miss_count[e] = 0;
+    for (int32_t t = 0; t < T; ++t) {
+        const int32_t* id = ids + (int64_t)t * k;
+        const float* wt = w + (int64_t)t * k;
+        int valid[32], res[32], keep[32];
+        float W = 0.0f, c = 0.0f;
+        for (int32_t j = 0; j < k; ++j) {
+            valid[j] = id[j] >= 0 && id[j] < E;
+            res[j] = valid[j] && slot_of[id[j]] >= 0;
+            keep[j] = res[j];
+            if (valid[j]) W += wt[j];
+        }
+        if (min_weight >= 1.0f) {
+            for (int32_t j = 0; j < k; ++j) keep[j] = valid[j];
+        } else {
+            for (int32_t j = 0; j < k; ++j)
+                if (res[j]) c += wt[j];
+            const float target = min_weight * W;
+            int done[32] = {0};
+            for (;;) {   /* the heaviest non-resident route not yet decided */
+                int32_t b = -1;
+                for (int32_t j = 0; j < k; ++j)
+                    if (valid[j] && !res[j] && !done[j] && (b < 0 || wt[j] > wt[b])) b = j;
+                if (b < 0) break;
+                done[b] = 1;
+                if (c >= target) continue;   /* share reached: skip */
+                keep[b] = 1;
+                c += wt[b];
+            }
+        }
+        int skipped = 0;
+        for (int32_t j = 0; j < k; ++j) skipped |= valid[j] && !keep[j];
+        const float scale = (skipped && c > 0.0f) ? W / c : 1.0f;
+        for (int32_t j = 0; j < k; ++j) {
+            ids_out[(int64_t)t * k + j] = keep[j] ? id[j] : -1;
+            w_out[(int64_t)t * k + j] = keep[j] ? (skipped ? wt[j] * scale : wt[j]) : 0.0f;
+            if (keep[j] && !res[j]) miss_count[id[j]] += 1;
+        }
+    }
+    return ORA_OK;
+}
+
 /* --------------------------------------------------------- quantisation --
  * [prain] "Expert formats": int8 experts carry an fp32 scale per row; int4
  * experts carry a bf16 scale per 64 elements, chosen by an MSE clip search;
