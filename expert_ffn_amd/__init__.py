@@ -52,12 +52,13 @@ def lib():
         L.moe_quantize.argtypes = [i32, P, i32, i32, P, P, P]
         L.moe_pack_expert.argtypes = [i32, P, P, i32, i32, P, P]
         L.moe_set_ffn_path.argtypes = [i32]
+        L.moe_min_weight.argtypes = [P, P, i32, i32, i32, P, ctypes.c_float, P, P, P, P]
         L.moe_fill_slot.argtypes = [i32, P, i32, i32, i32, P, P, P]
         L.moe_verify_slot.argtypes = [i32, P, i32, i32, P, P, P]
         L.moe_slot_admit.argtypes = [P, i32, P, i32, i32]
         for name in ("moe_blob_layout", "moe_route_topk", "moe_permute", "moe_route_permute", "moe_expert_ffn",
                      "moe_ffn_gate_up", "moe_ffn_down", "moe_combine", "moe_quantize",
-                     "moe_pack_expert", "moe_set_ffn_path", "moe_fill_slot", "moe_verify_slot",
+                     "moe_pack_expert", "moe_set_ffn_path", "moe_min_weight", "moe_fill_slot", "moe_verify_slot",
                      "moe_slot_admit"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -199,3 +200,10 @@ def slot_admit(slot_of, owner, expert: int) -> int:
     if j < 0:
         raise MoeError(1, lib().moe_last_error().decode())
     return j
+
+
+def min_weight(ids, w, E: int, slot_of, share: float, ids_out, w_out, miss_count, stream=None):
+    """min_weight partial routing of topk ids/w [T, k] (outputs may alias them)."""
+    T, k = ids.shape
+    _check(lib().moe_min_weight(_ptr(ids), _ptr(w), T, k, E, _ptr(slot_of), ctypes.c_float(share), _ptr(ids_out),
+                                _ptr(w_out), _ptr(miss_count), _stream(stream)))

@@ -127,6 +127,20 @@ moe_status moe_route_topk(const float* logits, int32_t T, int32_t E, int32_t k, 
                                                  static_cast<hipStream_t>(stream)));
 }
 
+moe_status moe_min_weight(const int32_t* topk_ids, const float* topk_w, int32_t T, int32_t k, int32_t E,
+                          const int32_t* slot_of, float min_weight, int32_t* ids_out, float* w_out,
+                          int32_t* miss_count, void* stream) {
+    const char* fn = "moe_min_weight";
+    if (!slot_of || !miss_count || (T > 0 && (!topk_ids || !topk_w || !ids_out || !w_out)))
+        return fail(MOE_E_ARG, fn, "null pointer argument");
+    if (T < 0) return fail(MOE_E_SHAPE, fn, "T=%d < 0", T);
+    if (E < 1 || E > 512) return fail(MOE_E_SHAPE, fn, "E=%d outside [1, 512]", E);
+    if (k < 1 || k > 32) return fail(MOE_E_SHAPE, fn, "k=%d outside [1, 32]", k);
+    if (min_weight != min_weight) return fail(MOE_E_ARG, fn, "min_weight is NaN");
+    return hip_status(fn, moe::launch_min_weight(topk_ids, topk_w, T, k, E, slot_of, min_weight, ids_out, w_out,
+                                                 miss_count, static_cast<hipStream_t>(stream)));
+}
+
 moe_status moe_permute(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E,
                        const int32_t* slot_of, int32_t* expert_offsets, int32_t* sorted_route,
                        int32_t* route_pos, int32_t* n_dropped, void* stream) {

@@ -8,6 +8,9 @@ namespace moe {
 
 hipError_t launch_route_topk(const float* logits, int T, int E, int k, int renorm, int* ids,
                              float* w, hipStream_t s);
+// min_weight partial routing: ids_out / w_out (may alias ids / w), miss [E] (zeroed here)
+hipError_t launch_min_weight(const int* ids, const float* w, int T, int k, int E, const int* slot_of, float share,
+                             int* ids_out, float* w_out, int* miss, hipStream_t s);
 hipError_t launch_permute(const int* ids, int R, int E, const int* slot_of, int* offsets,
                           int* sorted_route, int* route_pos, int* n_dropped, hipStream_t s);
 // route + permute: one fused launch for T k <= 1024 (and T <= 64), else the two

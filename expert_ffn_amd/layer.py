@@ -7,7 +7,7 @@ from __future__ import annotations
 
 import torch
 
-from . import (ACT_GELU_TANH, F32, combine, expert_ffn, ffn_down, ffn_gate_up, permute,
+from . import (ACT_GELU_TANH, F32, combine, expert_ffn, ffn_down, ffn_gate_up, min_weight, permute,
                route_topk, workspace_bytes)
 
 
@@ -24,6 +24,7 @@ class MoeLayer:
         self.sorted_route = torch.empty(T_max * k, dtype=i32, device=d)
         self.route_pos = torch.empty(T_max * k, dtype=i32, device=d)
         self.n_dropped = torch.empty(1, dtype=i32, device=d)
+        self.miss_count = torch.zeros(E, dtype=i32, device=d)
         self.out_routes = torch.empty((T_max * k, H), dtype=out_dtype, device=d)
         nbytes = workspace_bytes(T_max, k, E, H, FF, fmt)
         self.ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=d)
@@ -38,8 +39,27 @@ class MoeLayer:
     def route(self, logits, stream=None):
         T = logits.shape[0]
         route_topk(logits, self.k, self.topk_ids[:T], self.topk_w[:T], self.renorm, stream)
+        self.group(T, stream)
+
+    def select(self, logits, share, stream=None):
+        """Top-k, then min_weight partial routing at `share` in place; leaves
+        in miss_count the kept routes per non-resident expert (the experts to
+        fill before group())."""
+        T = logits.shape[0]
+        route_topk(logits, self.k, self.topk_ids[:T], self.topk_w[:T], self.renorm, stream)
+        min_weight(self.topk_ids[:T], self.topk_w[:T], self.E, self._slot_of, share, self.topk_ids[:T],
+                   self.topk_w[:T], self.miss_count, stream)
+
+    def group(self, T, stream=None):
+        """Permute the current top-k routes against the bound slot table."""
         permute(self.topk_ids[:T], self.E, self._slot_of, self.offsets, self.sorted_route[:T * self.k],
                 self.route_pos[:T * self.k], self.n_dropped, stream)
+
+    def ffn(self, x, stream=None):
+        T = x.shape[0]
+        expert_ffn(self._pool, self._slot_bytes, self._slot_of, self.E, self.H, self.FF, self.fmt,
+                   self.act, x, self.k, self.offsets, self.sorted_route[:T * self.k],
+                   self.out_routes[:T * self.k], self.ws, stream)
 
     def gate_up(self, x, stream=None):
         ffn_gate_up(self._pool, self._slot_bytes, self._slot_of, self.E, self.H, self.FF, self.fmt,
@@ -64,9 +84,7 @@ class MoeLayer:
         """The whole layer for T = logits.shape[0] tokens; returns the y view."""
         T = logits.shape[0]
         self.route(logits, stream)
-        expert_ffn(self._pool, self._slot_bytes, self._slot_of, self.E, self.H, self.FF, self.fmt,
-                   self.act, x, self.k, self.offsets, self.sorted_route[:T * self.k],
-                   self.out_routes[:T * self.k], self.ws, stream)
+        self.ffn(x, stream)
         self.combine(T, stream)
         return self.y[:T]
 

@@ -146,6 +146,32 @@ moe_status moe_route_permute(const float* logits, int32_t T, int32_t E, int32_t 
                              int32_t* sorted_route, int32_t* route_pos, int32_t* n_dropped, void* stream);
 
 /*
+ * min_weight partial routing (prain README, "Trading quality for speed": the
+ * share of each token's router weight that must be computed; below 1 a token
+ * skips its lightest experts that are not resident once it has that share,
+ * and the routes it keeps are scaled up to its full weight).  For token t
+ * with routes j (topk_ids / topk_w device [T, k], as moe_route_topk writes
+ * them), in fp32:
+ *   W = sum of w_j over routes with 0 <= id_j < E (in j order); resident
+ *   routes (slot_of[id_j] >= 0) are kept; the non-resident ones are taken
+ *   heaviest first (equal weights: lower j first) while the kept weight c
+ *   (resident sum in j order, then each taken weight) is below
+ *   min_weight * W; the rest, and ids outside [0, E), are skipped.
+ *   If a valid route was skipped, kept weights become w_j * (W / c).
+ *   min_weight >= 1 keeps every valid route unchanged (the full routing).
+ * ids_out (device int32 [T, k]): the id, or -1 for a skipped route (which
+ * moe_permute then drops); w_out (device fp32 [T, k]): the weight, 0 for a
+ * skipped route.  They may alias topk_ids / topk_w.  miss_count (device int32
+ * [E], overwritten): per expert, the kept routes that need it while it is not
+ * resident -- the experts to copy in (moe_fill_slot) before the FFN.
+ * 1 <= k <= 32, E <= 512; NaN min_weight returns MOE_E_ARG.  T = 0 only
+ * zeroes miss_count (the route pointers may then be NULL).
+ */
+moe_status moe_min_weight(const int32_t* topk_ids, const float* topk_w, int32_t T, int32_t k, int32_t E,
+                          const int32_t* slot_of, float min_weight, int32_t* ids_out, float* w_out,
+                          int32_t* miss_count, void* stream);
+
+/*
  * The expert FFN of every kept route (prain README, "Expert formats": an
  * expert is its w13 and w2; weights are dequantised inside the kernels):
  *   for the route at position p (route i = sorted_route[p], token t = i / k,

@@ -42,12 +42,12 @@ def build_pool(seed, layer, E, H, FF, fmt, slot_of, n_slots=None, device="cuda")
     return pool, sb
 
 
-def oracle_layer(seed, layer, E, k, H, FF, fmt, act, logits, x_f32, slot_of, tokens):
+def oracle_layer(seed, layer, E, k, H, FF, fmt, act, logits, x_f32, slot_of, tokens, routes_in=None):
     """Oracle route + permute for all tokens, FFN and combine for the sampled
     tokens, with blobs the oracle packs itself (only the experts those tokens
-    need)."""
+    need).  routes_in = (ids, w) replaces the oracle's own top-k."""
     T = logits.shape[0]
-    ids, w = ora.route_topk(logits, k)
+    ids, w = ora.route_topk(logits, k) if routes_in is None else routes_in
     offsets, sorted_route, route_pos, nd = ora.permute(ids, E, slot_of)
     tokens = np.asarray(tokens, dtype=np.int32)
     need = sorted({int(e) for e in ids[tokens].reshape(-1) if slot_of[e] >= 0})

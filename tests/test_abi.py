@@ -96,6 +96,11 @@ def test_host_validation_errors(L):
     assert rc == 1 and "aligned" in msg
     rc, msg = _call(L, "moe_verify_slot", 2, fake, 2816, 704, fake, None, None)
     assert rc == 1
+    rc, msg = _call(L, "moe_min_weight", fake, fake, 4, 8, 128, fake, ctypes.c_float(float("nan")), fake, fake,
+                    fake, None)
+    assert rc == 1 and "NaN" in msg
+    rc, msg = _call(L, "moe_min_weight", fake, fake, 4, 33, 128, fake, ctypes.c_float(0.5), fake, fake, fake, None)
+    assert rc == 2 and "k=33" in msg
 
 
 def test_slot_admit_claims_the_lowest_free_slot(L):

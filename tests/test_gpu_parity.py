@@ -376,3 +376,88 @@ def test_fill_slot_bit_exact(L, fmt, H, FF):
     L.verify_slot(fmt, src_d, H, FF, pool[sb:2 * sb], bad)
     torch.cuda.synchronize()
     assert int(bad.item()) == 1
+
+
+# ------------------------------------------------------------ min_weight ----
+@pytest.mark.parametrize("T,E,k,n_res", [(1, 128, 8, 15), (16, 128, 8, 15), (1000, 128, 8, 64), (300, 64, 32, 20),
+                                         (0, 128, 8, 15)])
+def test_min_weight_bit_exact(L, T, E, k, n_res):
+    # routes from the oracle's top-k on seeded logits (plus planted ties and
+    # invalid ids); every share: ids, weights (fp32 bits) and miss counts exact
+    import oracle as ora
+    log(f"min_weight T={T} E={E} k={k} resident={n_res}")
+    r = np.random.default_rng(T + E + k)
+    ids, w = ora.route_topk(synth.logits(3, 0, T, E, None), k) if T else (np.zeros((0, k), np.int32),
+                                                                            np.zeros((0, k), np.float32))
+    if T >= 4:
+        w[1, :] = np.float32(1.0 / k)                  # all weights tied
+        ids[2, 0] = -1                                 # invalid ids
+        ids[3, k - 1] = E
+    slot_of = np.full(E, -1, np.int32)
+    slot_of[r.choice(E, n_res, replace=False)] = np.arange(n_res, dtype=np.int32)
+    slot_d = torch.from_numpy(slot_of).cuda()
+    for share in (0.0, 0.4, 0.6, 0.95, 1.0):
+        ids_d = torch.from_numpy(ids).cuda()
+        w_d = torch.from_numpy(w).cuda()
+        io = torch.full_like(ids_d, 77)
+        wo = torch.full_like(w_d, 77.0)
+        miss = torch.full((E,), 55, dtype=torch.int32, device="cuda")
+        L.min_weight(ids_d, w_d, E, slot_d, share, io, wo, miss)
+        rio, rwo, rmiss = ora.min_weight(ids, w, E, slot_of, share)
+        torch.cuda.synchronize()
+        assert np.array_equal(to_np(io), rio), share
+        assert np.array_equal(to_np(wo).view(np.uint32), rwo.view(np.uint32)), share
+        assert np.array_equal(to_np(miss), rmiss), share
+        L.min_weight(ids_d, w_d, E, slot_d, share, ids_d, w_d, miss)     # in place
+        torch.cuda.synchronize()
+        assert np.array_equal(to_np(ids_d), rio) and np.array_equal(to_np(w_d).view(np.uint32), rwo.view(np.uint32))
+
+
+@pytest.mark.parametrize("share", [0.6, 0.4])
+def test_min_weight_miss_step(L, share):
+    # the serving step with a small resident set (15 of 128 experts, as with
+    # 450 slots over 30 layers): select, copy the missed experts into free
+    # slots, then group, FFN and combine; y against the oracle run on the
+    # oracle's own selection with the same residency
+    from expert_ffn_amd.layer import MoeLayer
+    import oracle as ora
+    from gpu_common import host_weights
+    c = synth.CONFIGS["int4_stack"]
+    E, k, H, FF, T, f = c["E"], c["k"], c["H"], c["FF"], 16, L.W_INT4_G64
+    log(f"min_weight miss step share={share}")
+    slot_of = np.full(E, -1, np.int32)
+    slot_of[np.arange(0, E, 9)[:15]] = np.arange(15, dtype=np.int32)
+    pool, sb = build_pool(5, 0, E, H, FF, f, slot_of, n_slots=E)
+    logits = synth.logits(5, 0, T, E, None)
+    x_d, x_f32 = _x(5, 0, T, H, "bf16")
+    ml = MoeLayer(E, k, H, FF, f, T, out_dtype=torch.float32)
+    slot_d = torch.from_numpy(slot_of).cuda()
+    ml.bind(pool, sb, slot_d)
+    ml.select(torch.from_numpy(logits).cuda(), share)
+    miss = to_np(ml.miss_count)
+    W = host_weights(5, 0, E, H, FF)
+    filled = slot_of.copy()
+    nxt = 15
+    for e in np.flatnonzero(miss):
+        L.pack_expert(f, torch.from_numpy(W[e][0].view(np.int16)).cuda(),
+                      torch.from_numpy(W[e][1].view(np.int16)).cuda(), pool[nxt * sb:(nxt + 1) * sb])
+        filled[e] = nxt
+        nxt += 1
+    slot_d.copy_(torch.from_numpy(filled))
+    ml.group(T)
+    ml.ffn(x_d)
+    ml.combine(T)
+    torch.cuda.synchronize()
+    ids, w = ora.route_topk(logits, k)
+    sid, sw, smiss = ora.min_weight(ids, w, E, slot_of, share)
+    assert np.array_equal(to_np(ml.topk_ids[:T]), sid)
+    assert np.max(np.abs(to_np(ml.topk_w[:T]) - sw)) <= 2e-5
+    assert np.array_equal(miss, smiss)
+    full = int((slot_of[ids] < 0).sum())
+    log(f"    copies: {int(smiss.sum())} routes to {int((smiss > 0).sum())} experts (full routing: {full} routes)")
+    assert smiss.sum() < full
+    tokens = np.arange(T, dtype=np.int32)
+    ref = oracle_layer(5, 0, E, k, H, FF, f, 0, logits, x_f32, filled, tokens, routes_in=(sid, sw))
+    err, med = row_rel_err(to_np(ml.y[:T])[tokens], ref["y"])
+    log(f"    y: max row-rel err {err:.3e}, median {med:.3e}")
+    assert err <= TOL[f]
