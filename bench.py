@@ -405,6 +405,109 @@ def measure_slot_fill(lib, dev, seed, n=64, reps=7):
                 fills_agree=same)
 
 
+def measure_miss_step(lib, dev, seed, tokens=16, n_res=15, shares=(1.0, 0.6, 0.4)):
+    """Decode (one token per step) through the 30-layer int4 stack when only
+    n_res of each layer's 128 experts are resident (450 slots over 30 layers,
+    as in prain's agent setup), for several min_weight shares (prain README,
+    "Trading quality for speed").  Per layer: top-k and min_weight on the
+    device, the miss counts back to the host, one slot fill per missed expert
+    from pinned host memory (DMA + unpack), then grouping, the expert FFN and
+    the combine; the filled slots are released again after the layer (a
+    fixed resident set).  The host copies are layer 0's blobs for every
+    layer: the fill moves bytes, and a copy's cost does not depend on them."""
+    import ctypes
+    import torch
+    from expert_ffn_amd.layer import MoeLayer
+    E, k, H, FF, Lyr = G["E"], G["k"], G["H"], G["FF"], synth.CONFIGS["int4_stack"]["L"]
+    fmt = lib.W_INT4_G64
+    log(f"packing the {Lyr}-layer int4 stack ...")
+    pool, sb, slots = build_stack(lib, seed, Lyr, E, H, FF, fmt, dev)
+    logits, xs = layer_inputs(seed + 1, Lyr, tokens, E, H, dev)
+    r = np.random.default_rng(seed + 23)
+    host = torch.empty((E, sb), dtype=torch.uint8).pin_memory()
+    for e in range(E):
+        host[e].copy_(pool[int(slots[0, e]) * sb:(int(slots[0, e]) + 1) * sb])
+    staging = torch.empty((E, sb), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.Stream()
+    c = lib.lib()
+    P = ctypes.c_void_p
+    s = P(stream.cuda_stream)
+    ml = MoeLayer(E, k, H, FF, fmt, 1, device=dev, out_dtype=torch.bfloat16)
+    miss_h = torch.zeros(E, dtype=torch.int32).pin_memory()
+
+    def run(share, resident):
+        base = []
+        for l in range(Lyr):
+            t = torch.full((E,), -1, dtype=torch.int32)
+            keep = np.arange(E) if resident >= E else r.choice(E, resident, replace=False)
+            t[torch.from_numpy(keep)] = torch.from_numpy(slots[l][keep].astype(np.int32))
+            base.append(t.pin_memory())
+        tab = [b.clone().pin_memory() for b in base]
+        slot_d = [b.to(dev) for b in base]
+        ws = ml.ws.numel()
+        copies = 0
+
+        def token(i):
+            nonlocal copies
+            for l in range(Lyr):
+                sd = P(slot_d[l].data_ptr())
+                lg, x = logits[l][i:i + 1], xs[l][i:i + 1]
+                assert not c.moe_route_topk(P(lg.data_ptr()), 1, E, k, 1, P(ml.topk_ids.data_ptr()),
+                                            P(ml.topk_w.data_ptr()), s)
+                assert not c.moe_min_weight(P(ml.topk_ids.data_ptr()), P(ml.topk_w.data_ptr()), 1, k, E, sd,
+                                            ctypes.c_float(share), P(ml.topk_ids.data_ptr()),
+                                            P(ml.topk_w.data_ptr()), P(ml.miss_count.data_ptr()), s)
+                miss_h.copy_(ml.miss_count, non_blocking=True)
+                stream.synchronize()
+                missed = np.flatnonzero(miss_h.numpy())
+                if missed.size:
+                    tab[l].copy_(base[l])
+                    # the layer's copies back to back on the copy engine, then the unpacks
+                    # (the same DMA + unpack per expert, one engine hand-off per layer)
+                    for j, e in enumerate(missed):
+                        staging[j].copy_(host[e], non_blocking=True)
+                    for j, e in enumerate(missed):
+                        sl = int(slots[l, e])
+                        assert not c.moe_fill_slot(fmt, P(staging[j].data_ptr()), 0, H, FF, None,
+                                                   P(pool.data_ptr() + sl * sb), s)
+                        tab[l][e] = sl
+                    slot_d[l].copy_(tab[l], non_blocking=True)
+                    copies += missed.size
+                assert not c.moe_permute(P(ml.topk_ids.data_ptr()), 1, k, E, sd, P(ml.offsets.data_ptr()),
+                                         P(ml.sorted_route.data_ptr()), P(ml.route_pos.data_ptr()),
+                                         P(ml.n_dropped.data_ptr()), s)
+                assert not c.moe_expert_ffn(P(pool.data_ptr()), sb, sd, E, H, FF, fmt, 0, P(x.data_ptr()), 1, 1,
+                                            k, P(ml.offsets.data_ptr()), P(ml.sorted_route.data_ptr()),
+                                            P(ml.out_routes.data_ptr()), 1, P(ml.ws.data_ptr()), ws, s)
+                assert not c.moe_combine(P(ml.out_routes.data_ptr()), 1, P(ml.topk_w.data_ptr()),
+                                         P(ml.route_pos.data_ptr()), 1, k, H, P(ml.y.data_ptr()), 1, s)
+                if missed.size:
+                    slot_d[l].copy_(base[l], non_blocking=True)     # release the filled slots
+
+        with torch.cuda.stream(stream):
+            token(0)
+            stream.synchronize()
+            copies = 0
+            t0 = time.perf_counter()
+            for i in range(1, tokens):
+                token(i)
+            stream.synchronize()
+            dt = time.perf_counter() - t0
+        n = tokens - 1
+        return dict(min_weight=share, resident_per_layer=int(min(resident, E)),
+                    tokens_per_s=round(n / dt, 2), ms_per_token=round(dt / n * 1e3, 2),
+                    experts_copied_per_token=round(copies / n, 1),
+                    GB_copied_per_token=round(copies / n * sb / 1e9, 3))
+
+    rows = [run(sh, n_res) for sh in shares]
+    ref = run(1.0, E)
+    return dict(metric="decode tokens/s with expert misses", unit="tokens/s",
+                config=dict(workload=f"Gemma-4-26B-A4B int4 stack, {Lyr} layers, one token per step, "
+                                     f"{n_res} of {E} experts resident per layer, misses copied from pinned "
+                                     f"host memory", tokens=tokens - 1),
+                rows=rows, all_resident=ref)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -425,6 +528,9 @@ def main():
     ap.add_argument("--configs", action="store_true",
                     help="instead of the stack step: single-layer timings of the other workloads "
                          "(one JSON object per line)")
+    ap.add_argument("--miss-step", action="store_true",
+                    help="instead of the stack step: decode with 15 of 128 experts resident per layer and "
+                         "misses copied in, at min_weight 1.0 / 0.6 / 0.4 (one JSON line)")
     ap.add_argument("--slot-fill", action="store_true",
                     help="instead of the stack step: int4 expert slot fill rates (one JSON line)")
     args = ap.parse_args()
@@ -444,6 +550,9 @@ def main():
     import expert_ffn_amd as lib
     lib.lib()
     dev = torch.device("cuda:0")
+    if args.miss_step:
+        print(json.dumps(measure_miss_step(lib, dev, args.seed)), flush=True)
+        return
     if args.slot_fill:
         print(json.dumps(measure_slot_fill(lib, dev, args.seed)), flush=True)
         return
