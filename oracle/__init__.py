@@ -67,6 +67,8 @@ def _declare(L):
     L.oracle_pack_expert_canonical.restype = ctypes.c_int
     L.oracle_fill_slot.argtypes = [i32, P, i32, i32, P]
     L.oracle_fill_slot.restype = ctypes.c_int
+    L.oracle_router_logits.argtypes = [P, P, i32, i32, i32, P]
+    L.oracle_router_logits.restype = ctypes.c_int
     L.oracle_min_weight.argtypes = [P, P, i32, i32, i32, P, ctypes.c_float, P, P, P]
     L.oracle_min_weight.restype = ctypes.c_int
     L.oracle_dequant.argtypes = [P, i32, i32, i32, i32, P]
@@ -183,6 +185,18 @@ def fill_slot(fmt: int, canonical, H: int, FF: int) -> np.ndarray:
     slot = np.empty_like(src)
     _check(lib().oracle_fill_slot(fmt, _p(src), H, FF, _p(slot)), "fill_slot")
     return slot
+
+
+def router_logits(x_f32, w_router) -> np.ndarray:
+    """fp64 router logits x [T, H] . Wr [E, H]^T."""
+    x = np.ascontiguousarray(x_f32, dtype=np.float32)
+    wr = np.ascontiguousarray(w_router, dtype=np.float32)
+    T, H = x.shape
+    E = wr.shape[0]
+    assert wr.shape == (E, H)
+    out = np.empty((T, E), dtype=np.float64)
+    _check(lib().oracle_router_logits(_p(x), _p(wr), T, H, E, _p(out)), "router_logits")
+    return out
 
 
 def min_weight(ids, w, E: int, slot_of, share: float):

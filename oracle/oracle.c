@@ -174,6 +174,23 @@ int oracle_permute(const int32_t* ids, int32_t T, int32_t k, int32_t E, const in
     return ORA_OK;
 }
 
+/* --------------------------------------------------------- router GEMV --
+ * [prain] (its measurements: the router is an fp32 GEMV whose logits feed the
+ * top-k): logits[t][e] = sum_h x[t][h] * Wr[e][h], x the token's hidden state
+ * (its fp32 value), Wr the fp32 router weight [E, H]; summed in fp64.
+ */
+int oracle_router_logits(const float* x, const float* wr, int32_t T, int32_t H, int32_t E, double* logits)
+{
+    if (!x || !wr || !logits || T < 0 || H < 1 || E < 1) return ORA_EARG;
+    for (int32_t t = 0; t < T; ++t)
+        for (int32_t e = 0; e < E; ++e) {
+            double acc = 0.0;
+            for (int32_t h = 0; h < H; ++h) acc += (double)x[(int64_t)t * H + h] * (double)wr[(int64_t)e * H + h];
+            logits[(int64_t)t * E + e] = acc;
+        }
+    return ORA_OK;
+}
+
 /* ------------------------------------------------- min_weight routing --
  * [prain] "Trading quality for speed": min_weight is the share of a token's
  * router weight that must be computed.  Below 1 the token skips its lightest

@@ -13,6 +13,8 @@ tensor id, layer, expert])):
   activations x   fp32 N(0, 1); bf16 by rounding
   expert weights  fp32 N(0, 0.02) -> bf16, w13 [2FF, H] and w2 [H, FF]
   slot table      a seeded permutation of the L*E slots of a pool, [L, E]
+  router weight   fp32 N(0, 1/H) [E, H], so that x . Wr has unit spread like
+                  the synthetic logits
 The shapes are those of a Gemma-4-26B-A4B MoE layer (E = 128, top-8, H = 2816,
 FF = 704) and of a tiny layer (E = 4, top-2, H = 64, FF = 32).  The GPU stack
 generator draws the same distributions with torch's device generator, for
@@ -22,7 +24,7 @@ from __future__ import annotations
 
 import numpy as np
 
-T_LOGITS, T_X, T_W13, T_W2, T_SLOTS, T_ZIPF = 1, 2, 3, 4, 5, 6
+T_LOGITS, T_X, T_W13, T_W2, T_SLOTS, T_ZIPF, T_ROUTER = 1, 2, 3, 4, 5, 6, 7
 WEIGHT_STD = 0.02
 
 GEMMA = dict(E=128, k=8, H=2816, FF=704)
@@ -60,6 +62,12 @@ def x_f32(seed: int, layer: int, T: int, H: int) -> np.ndarray:
 
 def x_bf16(seed: int, layer: int, T: int, H: int) -> np.ndarray:
     return to_bf16_bits(x_f32(seed, layer, T, H))
+
+
+def router_weight(seed: int, layer: int, E: int, H: int) -> np.ndarray:
+    """fp32 [E, H] router weight."""
+    return (rng(seed, T_ROUTER, layer).standard_normal((E, H), dtype=np.float32)
+            * np.float32(1.0 / np.sqrt(H))).astype(np.float32)
 
 
 def expert_weights(seed: int, layer: int, e: int, H: int, FF: int, std: float = WEIGHT_STD):

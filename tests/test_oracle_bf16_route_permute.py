@@ -137,3 +137,17 @@ def test_permute_brute_force(ora, T, k, E, drop):
     # numpy's stable argsort gives the same order
     key = np.where(dropped, E, flat)
     assert np.array_equal(np.argsort(key, kind="stable")[:n], sorted_route[:n])
+
+
+# ---------------------------------------------------------- router GEMV ----
+def test_router_logits_is_the_matrix_product(ora):
+    # the fp64 sum equals numpy's fp64 product (another implementation of the
+    # same definition) to rounding; one-hot hidden states pick router columns
+    x = synth.x_f32(4, 0, 9, 320)
+    wr = synth.router_weight(4, 0, 12, 320)
+    got = ora.router_logits(x, wr)
+    want = x.astype(np.float64) @ wr.astype(np.float64).T
+    assert np.max(np.abs(got - want)) <= 1e-12 * np.max(np.abs(want))
+    eye = np.eye(320, dtype=np.float32)[[0, 7, 319]]
+    assert np.array_equal(ora.router_logits(eye, wr), wr[:, [0, 7, 319]].T.astype(np.float64))
+    assert ora.router_logits(np.zeros((2, 320), np.float32), wr).max() == 0.0
