@@ -405,6 +405,65 @@ def measure_slot_fill(lib, dev, seed, n=64, reps=7):
                 fills_agree=same)
 
 
+def measure_router(lib, dev, seed, reps=200):
+    """Router GEMV + top-k at the Gemma shape (E = 128, H = 2816, top-8, bf16
+    hidden states, fp32 router weight): moe_router_topk (partial GEMV, then
+    slice sums + top-k) against torch's fp32 matmul of the widened x followed
+    by moe_route_topk.
+    Each variant is captured once in a HIP graph of `reps` calls over
+    different token blocks of a larger x (the weight stays in cache either
+    way: it is 1.44 MB) and replayed; time per call."""
+    import torch
+    E, k, H = G["E"], G["k"], G["H"]
+    wr = torch.from_numpy(synth.router_weight(seed, 0, E, H)).to(dev)
+    stream = torch.cuda.Stream()
+    rows = []
+    for T in (1, 16, 64, 1024):
+        copies = max(1, min(64, (64 << 20) // (T * H * 2)))
+        x = torch.from_numpy(synth.x_bf16(seed, 0, T * copies, H).view(np.int16)).to(dev).view(torch.bfloat16)
+        xs = [x[i * T:(i + 1) * T] for i in range(copies)]
+        logits = torch.empty((T, E), dtype=torch.float32, device=dev)
+        ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+        w = torch.empty((T, k), dtype=torch.float32, device=dev)
+        cnt = torch.empty(lib.router_ws_bytes(T, H, E), dtype=torch.uint8, device=dev)
+
+        def fused(i):
+            lib.router_topk(xs[i % copies], wr, k, logits, cnt, ids, w, stream=stream)
+
+        def split(i):
+            torch.mm(xs[i % copies].float(), wr.t(), out=logits)
+            lib.route_topk(logits, k, ids, w, 1, stream)
+
+        out = dict(T=T)
+        for name, f in (("fused", fused), ("split", split)):
+            with torch.cuda.stream(stream):
+                for i in range(3):
+                    f(i)
+                torch.cuda.synchronize()
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=stream):
+                    for i in range(reps):
+                        f(i)
+                g.replay()
+                torch.cuda.synchronize()
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                for _ in range(5):
+                    g.replay()
+                b.record(stream)
+                torch.cuda.synchronize()
+                out[f"{name}_us"] = round(a.elapsed_time(b) * 1e3 / (5 * reps), 2)
+                del g
+        flops = 2.0 * T * E * H
+        out["fused_tflops"] = round(flops / (out["fused_us"] * 1e-6) / 1e12, 2)
+        out["fused_frac_fp32"] = round(out["fused_tflops"] / 157.3, 4)
+        rows.append(out)
+        log(json.dumps(out))
+    return dict(metric="router GEMV + top-k", unit="us per call",
+                config=dict(workload=f"Gemma-4-26B-A4B router: E={E}, H={H}, top-{k}, bf16 x, fp32 weight"),
+                rows=rows)
+
+
 def measure_miss_step(lib, dev, seed, tokens=16, n_res=15, shares=(1.0, 0.6, 0.4)):
     """Decode (one token per step) through the 30-layer int4 stack when only
     n_res of each layer's 128 experts are resident (450 slots over 30 layers,
@@ -528,6 +587,8 @@ def main():
     ap.add_argument("--configs", action="store_true",
                     help="instead of the stack step: single-layer timings of the other workloads "
                          "(one JSON object per line)")
+    ap.add_argument("--router", action="store_true",
+                    help="instead of the stack step: router GEMV + top-k timings, fused and split (one JSON line)")
     ap.add_argument("--miss-step", action="store_true",
                     help="instead of the stack step: decode with 15 of 128 experts resident per layer and "
                          "misses copied in, at min_weight 1.0 / 0.6 / 0.4 (one JSON line)")
@@ -550,6 +611,9 @@ def main():
     import expert_ffn_amd as lib
     lib.lib()
     dev = torch.device("cuda:0")
+    if args.router:
+        print(json.dumps(measure_router(lib, dev, args.seed)), flush=True)
+        return
     if args.miss_step:
         print(json.dumps(measure_miss_step(lib, dev, args.seed)), flush=True)
         return

@@ -52,13 +52,16 @@ def lib():
         L.moe_quantize.argtypes = [i32, P, i32, i32, P, P, P]
         L.moe_pack_expert.argtypes = [i32, P, P, i32, i32, P, P]
         L.moe_set_ffn_path.argtypes = [i32]
+        L.moe_router_ws_bytes.argtypes = [i32, i32, i32]
+        L.moe_router_ws_bytes.restype = sz
+        L.moe_router_topk.argtypes = [P, i32, i32, i32, P, i32, i32, i32, P, P, sz, P, P, P]
         L.moe_min_weight.argtypes = [P, P, i32, i32, i32, P, ctypes.c_float, P, P, P, P]
         L.moe_fill_slot.argtypes = [i32, P, i32, i32, i32, P, P, P]
         L.moe_verify_slot.argtypes = [i32, P, i32, i32, P, P, P]
         L.moe_slot_admit.argtypes = [P, i32, P, i32, i32]
         for name in ("moe_blob_layout", "moe_route_topk", "moe_permute", "moe_route_permute", "moe_expert_ffn",
                      "moe_ffn_gate_up", "moe_ffn_down", "moe_combine", "moe_quantize",
-                     "moe_pack_expert", "moe_set_ffn_path", "moe_min_weight", "moe_fill_slot", "moe_verify_slot",
+                     "moe_pack_expert", "moe_set_ffn_path", "moe_router_topk", "moe_min_weight", "moe_fill_slot", "moe_verify_slot",
                      "moe_slot_admit"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -207,3 +210,16 @@ def min_weight(ids, w, E: int, slot_of, share: float, ids_out, w_out, miss_count
     T, k = ids.shape
     _check(lib().moe_min_weight(_ptr(ids), _ptr(w), T, k, E, _ptr(slot_of), ctypes.c_float(share), _ptr(ids_out),
                                 _ptr(w_out), _ptr(miss_count), _stream(stream)))
+
+
+def router_ws_bytes(T: int, H: int, E: int) -> int:
+    """Bytes of the workspace router_topk needs for T tokens."""
+    return int(lib().moe_router_ws_bytes(T, H, E))
+
+
+def router_topk(x, w_router, k: int, logits, ws, ids, w, renorm: int = 1, stream=None):
+    """fp32 router GEMV of x [T, H] with w_router [E, H], then the top-k (two launches)."""
+    T, H = x.shape
+    E = w_router.shape[0]
+    _check(lib().moe_router_topk(_ptr(x), _dt(x), T, H, _ptr(w_router), E, k, renorm, _ptr(logits), _ptr(ws),
+                                 ws.numel() * ws.element_size(), _ptr(ids), _ptr(w), _stream(stream)))

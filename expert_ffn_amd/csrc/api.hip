@@ -127,6 +127,35 @@ moe_status moe_route_topk(const float* logits, int32_t T, int32_t E, int32_t k, 
                                                  static_cast<hipStream_t>(stream)));
 }
 
+size_t moe_router_ws_bytes(int32_t T, int32_t H, int32_t E) {
+    if (T <= 0 || H < 1 || E < 1) return 256;
+    return up256(static_cast<uint64_t>(moe::router_part_floats(T, H, E)) * 4);
+}
+
+moe_status moe_router_topk(const void* x, int32_t x_dtype, int32_t T, int32_t H, const float* w_router, int32_t E,
+                           int32_t k, int32_t renorm, float* logits, void* ws, size_t ws_bytes, int32_t* topk_ids,
+                           float* topk_w, void* stream) {
+    const char* fn = "moe_router_topk";
+    if (T < 0) return fail(MOE_E_SHAPE, fn, "T=%d < 0", T);
+    if (T > 0 && (!x || !w_router || !logits || !ws || !topk_ids || !topk_w))
+        return fail(MOE_E_ARG, fn, "null pointer argument");
+    if (!dt_ok(x_dtype)) return fail(MOE_E_ARG, fn, "unknown dtype %d", x_dtype);
+    if (E < 1 || E > 512) return fail(MOE_E_SHAPE, fn, "E=%d outside [1, 512]", E);
+    if (k < 1 || k > 32 || k > E) return fail(MOE_E_SHAPE, fn, "k=%d outside [1, min(E=%d, 32)]", k, E);
+    if (H < 64 || H % 64) return fail(MOE_E_SHAPE, fn, "H=%d is not a positive multiple of 64", H);
+    if (static_cast<int64_t>(T) * H >= (1ll << 31) || moe::router_part_floats(T, H, E) >= (1ll << 31))
+        return fail(MOE_E_SHAPE, fn, "T=%d too large", T);
+    if (T == 0) return MOE_OK;
+    if (ws_bytes < moe_router_ws_bytes(T, H, E))
+        return fail(MOE_E_WORKSPACE, fn, "ws_bytes=%zu < %zu", ws_bytes, moe_router_ws_bytes(T, H, E));
+    if (reinterpret_cast<uintptr_t>(x) % 16 || reinterpret_cast<uintptr_t>(w_router) % 16 ||
+        reinterpret_cast<uintptr_t>(ws) % 16)
+        return fail(MOE_E_ARG, fn, "x, w_router and ws must be 16-byte aligned");
+    return hip_status(fn, moe::launch_router_topk(x, x_dtype == MOE_F32, w_router, T, H, E, k, renorm, logits,
+                                                  static_cast<float*>(ws), topk_ids, topk_w,
+                                                  static_cast<hipStream_t>(stream)));
+}
+
 moe_status moe_min_weight(const int32_t* topk_ids, const float* topk_w, int32_t T, int32_t k, int32_t E,
                           const int32_t* slot_of, float min_weight, int32_t* ids_out, float* w_out,
                           int32_t* miss_count, void* stream) {

@@ -8,6 +8,11 @@ namespace moe {
 
 hipError_t launch_route_topk(const float* logits, int T, int E, int k, int renorm, int* ids,
                              float* w, hipStream_t s);
+// router GEMV + top-k: x [T, H] (fp32 or bf16), wr fp32 [E, H]; logits fp32 [T, E] out;
+// part fp32 [router_part_floats(T, H, E)] scratch (partial logits per H slice)
+int64_t router_part_floats(int T, int H, int E);
+hipError_t launch_router_topk(const void* x, bool xf32, const float* wr, int T, int H, int E, int k, int renorm,
+                              float* logits, float* part, int* ids, float* w, hipStream_t s);
 // min_weight partial routing: ids_out / w_out (may alias ids / w), miss [E] (zeroed here)
 hipError_t launch_min_weight(const int* ids, const float* w, int T, int k, int E, const int* slot_of, float share,
                              int* ids_out, float* w_out, int* miss, hipStream_t s);

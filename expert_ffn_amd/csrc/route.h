@@ -66,20 +66,16 @@ __device__ __forceinline__ float wave_sum_f32(float v) {
 // k chosen (renorm) or over all E, ids also to lds_ids if given.  Lane l holds
 // experts l + 64 s.  A round
 // takes the wave maximum of the ordered logits, then the lowest expert id
-// holding it (ballots, lowest s first, then lowest lane).
+// holding it (ballots, lowest s first, then lowest lane).  The logits are in
+// registers: val[s] = logit of expert lane + 64 s (ignored for experts >= E).
 template <int NPL>
-__device__ __forceinline__ void route_token(const float* __restrict__ logits, int t, int E, int k, int renorm,
-                                            int* __restrict__ ids, float* __restrict__ w, int* lds_ids = nullptr) {
+__device__ __forceinline__ void route_token_vals(const float (&val)[NPL], int t, int E, int k, int renorm,
+                                                 int* __restrict__ ids, float* __restrict__ w,
+                                                 int* lds_ids = nullptr) {
     const int lane = threadIdx.x & 63;
-    const float* l = logits + static_cast<int64_t>(t) * E;
     uint32_t key[NPL];
-    float val[NPL];
 #pragma unroll
-    for (int s = 0; s < NPL; ++s) {
-        const int e = lane + 64 * s;
-        val[s] = e < E ? l[e] : 0.0f;
-        key[s] = e < E ? logit_ord(val[s]) : 0u;
-    }
+    for (int s = 0; s < NPL; ++s) key[s] = lane + 64 * s < E ? logit_ord(val[s]) : 0u;
     int my_id = -1;
     float my_logit = 0.0f;
     for (int j = 0; j < k; ++j) {
@@ -124,6 +120,18 @@ __device__ __forceinline__ void route_token(const float* __restrict__ logits, in
         w[static_cast<int64_t>(t) * k + lane] = ex / den;
         if (lds_ids != nullptr) lds_ids[t * k + lane] = my_id;
     }
+}
+
+// The same, loading row t of logits [T, E] first.
+template <int NPL>
+__device__ __forceinline__ void route_token(const float* __restrict__ logits, int t, int E, int k, int renorm,
+                                            int* __restrict__ ids, float* __restrict__ w, int* lds_ids = nullptr) {
+    const int lane = threadIdx.x & 63;
+    const float* l = logits + static_cast<int64_t>(t) * E;
+    float val[NPL];
+#pragma unroll
+    for (int s = 0; s < NPL; ++s) val[s] = lane + 64 * s < E ? l[lane + 64 * s] : 0.0f;
+    route_token_vals<NPL>(val, t, E, k, renorm, ids, w, lds_ids);
 }
 
 }  // namespace moe

@@ -146,6 +146,29 @@ moe_status moe_route_permute(const float* logits, int32_t T, int32_t E, int32_t 
                              int32_t* sorted_route, int32_t* route_pos, int32_t* n_dropped, void* stream);
 
 /*
+ * Router GEMV fused with the top-k (prain README, "int4 experts on RDNA2":
+ * the router is an fp32 GEMV, tried there as a separate kernel): logits[t][e] =
+ * sum_h x[t][h] * w_router[e][h] in fp32 (bf16 x widened exactly), then the
+ * top-k and softmax weights of moe_route_topk on those logits: two launches
+ * (partial sums over 256-element slices of H, then per token the sum of the
+ * slices and the top-k), the full logits written once.
+ *   x         device [T, H], fp32 or bf16 (x_dtype), 16-byte aligned
+ *   w_router  device fp32 [E, H], 16-byte aligned
+ *   logits    device fp32 [T, E] out (the router logits)
+ *   ws        device workspace of ws_bytes >= moe_router_ws_bytes(T, H, E),
+ *             16-byte aligned (partial sums; no state between calls)
+ *   topk_ids, topk_w: as moe_route_topk.
+ * H % 64 == 0.  The sums run in a fixed order (per 256-element slice of H,
+ * then the slices in order), so results are reproducible; the logits differ
+ * from an fp64 product by fp32 rounding, and so may the order of experts whose
+ * logits tie within it.
+ */
+size_t moe_router_ws_bytes(int32_t T, int32_t H, int32_t E);
+moe_status moe_router_topk(const void* x, int32_t x_dtype, int32_t T, int32_t H, const float* w_router, int32_t E,
+                           int32_t k, int32_t renorm, float* logits, void* ws, size_t ws_bytes, int32_t* topk_ids,
+                           float* topk_w, void* stream);
+
+/*
  * min_weight partial routing (prain README, "Trading quality for speed": the
  * share of each token's router weight that must be computed; below 1 a token
  * skips its lightest experts that are not resident once it has that share,

@@ -175,8 +175,8 @@ int oracle_permute(const int32_t* ids, int32_t T, int32_t k, int32_t E, const in
 }
 
 /* --------------------------------------------------------- router GEMV --
- * [prain] (its measurements: the router is an fp32 GEMV whose logits feed the
- * top-k): logits[t][e] = sum_h x[t][h] * Wr[e][h], x the token's hidden state
+ * [prain] "int4 experts on RDNA2" (the router is an fp32 GEMV whose logits feed
+ * the top-k): logits[t][e] = sum_h x[t][h] * Wr[e][h], x the token's hidden state
  * (its fp32 value), Wr the fp32 router weight [E, H]; summed in fp64.
  */
 int oracle_router_logits(const float* x, const float* wr, int32_t T, int32_t H, int32_t E, double* logits)

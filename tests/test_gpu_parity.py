@@ -461,3 +461,56 @@ def test_min_weight_miss_step(L, share):
     err, med = row_rel_err(to_np(ml.y[:T])[tokens], ref["y"])
     log(f"    y: max row-rel err {err:.3e}, median {med:.3e}")
     assert err <= TOL[f]
+
+
+# ------------------------------------------------------- router GEMV + top-k ----
+@pytest.mark.parametrize("T,E,k,H,xdt", [(1, 128, 8, 2816, "bf16"), (16, 128, 8, 2816, "bf16"),
+                                         (1024, 128, 8, 2816, "bf16"), (37, 64, 4, 320, "f32"),
+                                         (5, 300, 8, 128, "bf16"), (3, 16, 2, 8192, "f32"), (0, 128, 8, 2816, "bf16"),
+                                         (100, 64, 4, 320, "f32"), (130, 300, 8, 192, "bf16")])
+def test_router_topk(L, T, E, k, H, xdt):
+    # logits against the fp64 product within an fp32 bound per element; ids
+    # exact wherever the oracle's logits separate the ranks by more than
+    # that bound (else the chosen logit must match the rank's within it);
+    # weights within 1e-5; a second call (over the first's workspace) identical
+    import oracle as ora
+    log(f"router_topk T={T} E={E} k={k} H={H} x={xdt}")
+    wr = synth.router_weight(9, 0, E, H)
+    if xdt == "bf16":
+        bits = synth.x_bf16(9, 0, T, H)
+        x_d = torch.from_numpy(bits.view(np.int16)).cuda().view(torch.bfloat16)
+        x_h = ora.bf16_to_f32(bits).reshape(T, H)
+    else:
+        x_h = synth.x_f32(9, 0, T, H)
+        x_d = torch.from_numpy(x_h).cuda()
+    wr_d = torch.from_numpy(wr).cuda()
+    cnt = torch.full((L.router_ws_bytes(T, H, E),), 0x7F, dtype=torch.uint8, device="cuda")
+    logits = torch.empty((T, E), dtype=torch.float32, device="cuda")
+    ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    L.router_topk(x_d, wr_d, k, logits, cnt, ids, w)
+    torch.cuda.synchronize()
+    got_l, got_i, got_w = to_np(logits), to_np(ids), to_np(w)
+    L.router_topk(x_d, wr_d, k, logits, cnt, ids, w)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_np(logits).view(np.uint32), got_l.view(np.uint32))
+    assert np.array_equal(to_np(ids), got_i) and np.array_equal(to_np(w), got_w)
+    if T == 0:
+        return
+    ref = ora.router_logits(x_h, wr)
+    bound = 64 * 2.0 ** -24 * (np.abs(x_h).astype(np.float64) @ np.abs(wr).astype(np.float64).T)
+    assert np.all(np.abs(got_l - ref) <= bound)
+    rid, rw = ora.route_topk(ref.astype(np.float32), k)
+    exact = 0
+    for t in range(T):
+        order = np.lexsort((np.arange(E), -ref[t]))
+        if np.array_equal(got_i[t], rid[t]):
+            exact += 1
+        else:
+            assert len(set(got_i[t].tolist())) == k
+            for j in range(k):   # a near tie: the chosen logit is the rank's within the bound
+                assert abs(ref[t, got_i[t, j]] - ref[t, order[j]]) <= 2 * bound[t].max()
+    log(f"    ids identical for {exact} of {T} tokens; max logit err {np.max(np.abs(got_l - ref)):.2e}")
+    same = np.all(got_i == rid, axis=1)
+    assert np.max(np.abs(got_w[same] - rw[same])) <= 1e-5
+    assert exact >= T - max(1, T // 100)
