@@ -69,6 +69,8 @@ def _declare(L):
     L.oracle_fill_slot.restype = ctypes.c_int
     L.oracle_router_logits.argtypes = [P, P, i32, i32, i32, P]
     L.oracle_router_logits.restype = ctypes.c_int
+    L.oracle_residency_refresh.argtypes = [P, i64, i32, i32, i32, P, P, P, P, P, P, P, P]
+    L.oracle_residency_refresh.restype = ctypes.c_int
     L.oracle_min_weight.argtypes = [P, P, i32, i32, i32, P, ctypes.c_float, P, P, P]
     L.oracle_min_weight.restype = ctypes.c_int
     L.oracle_dequant.argtypes = [P, i32, i32, i32, i32, P]
@@ -196,6 +198,26 @@ def router_logits(x_f32, w_router) -> np.ndarray:
     assert wr.shape == (E, H)
     out = np.empty((T, E), dtype=np.float64)
     _check(lib().oracle_router_logits(_p(x), _p(wr), T, H, E, _p(out)), "router_logits")
+    return out
+
+
+def residency_refresh(ids, E: int, budget: int, S: int, slot_of):
+    """[rlx_runtime expert_pool.rs] hit counts, target, paired promote/demote
+    and the new slot table; returns a dict of numpy arrays."""
+    ids = np.ascontiguousarray(ids, dtype=np.int32).reshape(-1)
+    slot_of = np.ascontiguousarray(slot_of, dtype=np.int32)
+    assert slot_of.shape == (E,)
+    out = dict(hits=np.empty(E, np.int32), target=np.empty(max(budget, 1), np.int32),
+               promote=np.empty(E, np.int32), promote_slot=np.empty(E, np.int32), demote=np.empty(E, np.int32),
+               counts=np.empty(3, np.int32), slot_of=np.empty(E, np.int32))
+    _check(lib().oracle_residency_refresh(_p(ids), ids.size, E, budget, S, _p(slot_of), _p(out["hits"]),
+                                          _p(out["target"]), _p(out["promote"]), _p(out["promote_slot"]),
+                                          _p(out["demote"]), _p(out["counts"]), _p(out["slot_of"])),
+           "residency_refresh")
+    nt, np_, nd = (int(v) for v in out["counts"])
+    out["target"] = out["target"][:budget]
+    out["promote"], out["promote_slot"] = out["promote"][:np_], out["promote_slot"][:np_]
+    out["demote"] = out["demote"][:nd]
     return out
 
 

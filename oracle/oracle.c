@@ -191,6 +191,78 @@ int oracle_router_logits(const float* x, const float* wr, int32_t T, int32_t H, 
     return ORA_OK;
 }
 
+/* ---------------------------------------------------- residency refresh --
+ * [rlx_runtime expert_pool.rs] (TIDE-style placement): count the hits of
+ * each expert in a step's routes, take the gpu_budget experts with the most
+ * hits (hits > 0; equal counts: lower expert id first) as the target, promote
+ * the target experts that are not resident (in target order) and demote as
+ * many resident experts outside the target (paired promote/demote); resident
+ * experts outside the target beyond that stay.  Readings (the page's set
+ * iteration has no order, and it keeps no slots):
+ *   - the experts that may be demoted are taken in ascending expert id;
+ *   - promotion j takes the slot of demotion j; promotions beyond the pairs
+ *     take the lowest free slots of [0, S) in ascending order (slots no
+ *     resident expert holds).  S >= budget guarantees enough.
+ * slot_of_out: demoted experts -1, promoted ones their slot, others as in
+ * slot_of_in.  counts = {targets, promotions, demotions}.
+ */
+int oracle_residency_refresh(const int32_t* ids, int64_t R, int32_t E, int32_t budget, int32_t S,
+                             const int32_t* slot_of_in, int32_t* hits, int32_t* target, int32_t* promote,
+                             int32_t* promote_slot, int32_t* demote, int32_t* counts, int32_t* slot_of_out)
+{
+    if (!ids || !slot_of_in || !hits || !target || !promote || !promote_slot || !demote || !counts ||
+        !slot_of_out || R < 0 || E < 1 || budget < 0 || budget > E || S < budget)
+        return ORA_EARG;
+    for (int32_t e = 0; e < E; ++e) hits[e] = 0;
+    for (int64_t i = 0; i < R; ++i)
+        if (ids[i] >= 0 && ids[i] < E) hits[ids[i]] += 1;
+    /* target: repeatedly the unpicked expert with the most hits (> 0), lowest id on ties */
+    int32_t* picked = (int32_t*)calloc((size_t)E, sizeof(int32_t));
+    int32_t* in_target = (int32_t*)calloc((size_t)E, sizeof(int32_t));
+    int32_t* used = (int32_t*)calloc((size_t)S + 1, sizeof(int32_t));
+    if (!picked || !in_target || !used) { free(picked); free(in_target); free(used); return ORA_EARG; }
+    int32_t nt = 0;
+    while (nt < budget) {
+        int32_t b = -1;
+        for (int32_t e = 0; e < E; ++e)
+            if (!picked[e] && hits[e] > 0 && (b < 0 || hits[e] > hits[b])) b = e;
+        if (b < 0) break;
+        picked[b] = 1;
+        in_target[b] = 1;
+        target[nt++] = b;
+    }
+    for (int32_t r = nt; r < budget; ++r) target[r] = -1;
+    int32_t np = 0;
+    for (int32_t r = 0; r < nt; ++r)
+        if (slot_of_in[target[r]] < 0) promote[np++] = target[r];
+    int32_t nd = 0;
+    for (int32_t e = 0; e < E && nd < np; ++e)
+        if (slot_of_in[e] >= 0 && !in_target[e]) demote[nd++] = e;
+    for (int32_t e = 0; e < E; ++e)
+        if (slot_of_in[e] >= 0 && slot_of_in[e] < S) used[slot_of_in[e]] = 1;
+    int32_t next_free = 0;
+    int rc = ORA_OK;
+    for (int32_t j = 0; j < np; ++j) {
+        if (j < nd) {
+            promote_slot[j] = slot_of_in[demote[j]];
+        } else {
+            while (next_free < S && used[next_free]) ++next_free;
+            if (next_free >= S) { rc = ORA_EARG; break; }
+            promote_slot[j] = next_free++;
+        }
+    }
+    for (int32_t e = 0; e < E; ++e) slot_of_out[e] = slot_of_in[e];
+    for (int32_t j = 0; j < nd; ++j) slot_of_out[demote[j]] = -1;
+    for (int32_t j = 0; j < np && rc == ORA_OK; ++j) slot_of_out[promote[j]] = promote_slot[j];
+    counts[0] = nt;
+    counts[1] = np;
+    counts[2] = nd;
+    free(picked);
+    free(in_target);
+    free(used);
+    return rc;
+}
+
 /* ------------------------------------------------- min_weight routing --
  * [prain] "Trading quality for speed": min_weight is the share of a token's
  * router weight that must be computed.  Below 1 the token skips its lightest
