@@ -43,9 +43,10 @@ def test_bf16_rounding_matches_torch(ora):
 
 # ------------------------------------------------------------- routing ----
 def test_route_topk_rlx_printed_vector(ora):
-    for name, inp, par, exp in read_golden("rlx_expert_pool_vectors.txt"):
-        if name != "top_by_count":
+    for row in read_golden("rlx_expert_pool_vectors.txt"):
+        if row[0] != "top_by_count":
             continue
+        _, inp, par, exp = row
         counts = np.array([[float(v) for v in inp.split()]], dtype=np.float32)
         ids, _ = ora.route_topk(counts, int(par))
         assert ids[0].tolist() == [int(v) for v in exp.split()]
@@ -94,9 +95,10 @@ def test_route_topk_weights(ora, zipf):
 
 # ----------------------------------------------------------- permutation --
 def test_permute_rlx_count_hits(ora):
-    for name, inp, par, exp in read_golden("rlx_expert_pool_vectors.txt"):
-        if name != "count_hits":
+    for row in read_golden("rlx_expert_pool_vectors.txt"):
+        if row[0] != "count_hits":
             continue
+        _, inp, par, exp = row
         ids = np.array([[int(v)] for v in inp.split()], dtype=np.int32)
         E = int(par)
         offsets, _, _, nd = ora.permute(ids, E, np.zeros(E, dtype=np.int32))
