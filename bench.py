@@ -464,6 +464,67 @@ def measure_router(lib, dev, seed, reps=200):
                 rows=rows)
 
 
+def measure_residency(lib, dev, seed, reps=200):
+    """The residency refresh kernel at the Gemma shape (E = 128, 15 resident
+    slots, budget 15) on one step's routes: decode (16 tokens x top-8) and a
+    prefill chunk (1024 x 8); uniform and Zipf(1.1) routing.  Graph replays of
+    `reps` calls, each starting from the same table (a copy back precedes the
+    refresh inside the graph; its time is measured alone and subtracted)."""
+    import torch
+    E, k = G["E"], G["k"]
+    budget = S = 15
+    rows = []
+    stream = torch.cuda.Stream()
+    base = torch.full((E,), -1, dtype=torch.int32, device=dev)
+    base[:S] = torch.arange(S, dtype=torch.int32, device=dev)
+    slot = base.clone()
+    outs = [torch.empty(n, dtype=torch.int32, device=dev) for n in (E, budget, E, E, E, 3)]
+    for T, zipf in ((16, None), (1024, None), (16, 1.1), (1024, 1.1)):
+        ids_h, _ = _oracle_free_topk(synth.logits(seed, 0, T, E, zipf), k)
+        ids = torch.from_numpy(ids_h).to(dev)
+
+        def one(with_refresh):
+            slot.copy_(base)
+            if with_refresh:
+                lib.residency_refresh(ids, E, budget, S, slot, *outs, stream=stream)
+
+        t = {}
+        for name, flag in (("copy_only", False), ("refresh", True)):
+            with torch.cuda.stream(stream):
+                one(flag)
+                torch.cuda.synchronize()
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=stream):
+                    for _ in range(reps):
+                        one(flag)
+                g.replay()
+                torch.cuda.synchronize()
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                for _ in range(5):
+                    g.replay()
+                b.record(stream)
+                torch.cuda.synchronize()
+                t[name] = a.elapsed_time(b) * 1e3 / (5 * reps)
+                del g
+        one(True)
+        torch.cuda.synchronize()
+        c = outs[5].tolist()
+        rows.append(dict(T=T, routes=T * k, zipf=zipf, us_per_refresh=round(t["refresh"] - t["copy_only"], 2),
+                         promotions=c[1], demotions=c[2], MB_to_copy=round(c[1] * lib.expert_bytes(
+                             lib.W_INT4_G64, G["H"], G["FF"]) / 1e6, 2)))
+        log(json.dumps(rows[-1]))
+    return dict(metric="residency refresh", unit="us per call",
+                config=dict(workload=f"Gemma-4-26B-A4B layer: E={E}, top-{k}, {S} resident slots, budget {budget}"),
+                rows=rows)
+
+
+def _oracle_free_topk(logits, k):
+    """Top-k ids of host logits with numpy (larger first, equal: lower id) --
+    inputs for the refresh timing only."""
+    return np.argsort(-logits, axis=1, kind="stable")[:, :k].astype(np.int32), None
+
+
 def measure_miss_step(lib, dev, seed, tokens=16, n_res=15, shares=(1.0, 0.6, 0.4)):
     """Decode (one token per step) through the 30-layer int4 stack when only
     n_res of each layer's 128 experts are resident (450 slots over 30 layers,
@@ -587,6 +648,8 @@ def main():
     ap.add_argument("--configs", action="store_true",
                     help="instead of the stack step: single-layer timings of the other workloads "
                          "(one JSON object per line)")
+    ap.add_argument("--residency", action="store_true",
+                    help="instead of the stack step: residency refresh timings (one JSON line)")
     ap.add_argument("--router", action="store_true",
                     help="instead of the stack step: router GEMV + top-k timings, fused and split (one JSON line)")
     ap.add_argument("--miss-step", action="store_true",
@@ -611,6 +674,9 @@ def main():
     import expert_ffn_amd as lib
     lib.lib()
     dev = torch.device("cuda:0")
+    if args.residency:
+        print(json.dumps(measure_residency(lib, dev, args.seed)), flush=True)
+        return
     if args.router:
         print(json.dumps(measure_router(lib, dev, args.seed)), flush=True)
         return

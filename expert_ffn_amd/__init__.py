@@ -55,13 +55,18 @@ def lib():
         L.moe_router_ws_bytes.argtypes = [i32, i32, i32]
         L.moe_router_ws_bytes.restype = sz
         L.moe_router_topk.argtypes = [P, i32, i32, i32, P, i32, i32, i32, P, P, sz, P, P, P]
+        L.moe_residency_refresh.argtypes = [P, ctypes.c_int64, i32, i32, i32, P, P, P, P, P, P, P, P]
+        L.moe_refresh_due.argtypes = [i32, ctypes.c_int64, i32, i32]
+        L.moe_refresh_due.restype = i32
+        L.moe_budget_from_memory.argtypes = [u64, u64, u64, i32, i32, i32]
+        L.moe_budget_from_memory.restype = i32
         L.moe_min_weight.argtypes = [P, P, i32, i32, i32, P, ctypes.c_float, P, P, P, P]
         L.moe_fill_slot.argtypes = [i32, P, i32, i32, i32, P, P, P]
         L.moe_verify_slot.argtypes = [i32, P, i32, i32, P, P, P]
         L.moe_slot_admit.argtypes = [P, i32, P, i32, i32]
         for name in ("moe_blob_layout", "moe_route_topk", "moe_permute", "moe_route_permute", "moe_expert_ffn",
                      "moe_ffn_gate_up", "moe_ffn_down", "moe_combine", "moe_quantize",
-                     "moe_pack_expert", "moe_set_ffn_path", "moe_router_topk", "moe_min_weight", "moe_fill_slot", "moe_verify_slot",
+                     "moe_pack_expert", "moe_set_ffn_path", "moe_router_topk", "moe_residency_refresh", "moe_min_weight", "moe_fill_slot", "moe_verify_slot",
                      "moe_slot_admit"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -223,3 +228,20 @@ def router_topk(x, w_router, k: int, logits, ws, ids, w, renorm: int = 1, stream
     E = w_router.shape[0]
     _check(lib().moe_router_topk(_ptr(x), _dt(x), T, H, _ptr(w_router), E, k, renorm, _ptr(logits), _ptr(ws),
                                  ws.numel() * ws.element_size(), _ptr(ids), _ptr(w), _stream(stream)))
+
+
+def residency_refresh(ids, E: int, budget: int, n_slots: int, slot_of, hits, target, promote, promote_slot, demote,
+                      counts, stream=None):
+    """Hit counts, top-budget target and paired promote/demote; slot_of is rewritten in place."""
+    _check(lib().moe_residency_refresh(_ptr(ids), ids.numel(), E, budget, n_slots, _ptr(slot_of), _ptr(hits),
+                                       _ptr(target), _ptr(promote), _ptr(promote_slot), _ptr(demote), _ptr(counts),
+                                       _stream(stream)))
+
+
+def refresh_due(every: int, step: int, prefill_block: bool, offload: bool) -> bool:
+    return bool(lib().moe_refresh_due(every, step, int(prefill_block), int(offload)))
+
+
+def budget_from_memory(free_bytes: int, reserve_bytes: int, expert_bytes: int, layers: int, max_per_layer: int,
+                       E: int) -> int:
+    return int(lib().moe_budget_from_memory(free_bytes, reserve_bytes, expert_bytes, layers, max_per_layer, E))

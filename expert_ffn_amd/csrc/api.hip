@@ -8,6 +8,7 @@
 #include "../../include/expert_ffn.h"
 #include "common.h"
 #include "kernels.h"
+#include <algorithm>
 
 namespace {
 
@@ -154,6 +155,37 @@ moe_status moe_router_topk(const void* x, int32_t x_dtype, int32_t T, int32_t H,
     return hip_status(fn, moe::launch_router_topk(x, x_dtype == MOE_F32, w_router, T, H, E, k, renorm, logits,
                                                   static_cast<float*>(ws), topk_ids, topk_w,
                                                   static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_residency_refresh(const int32_t* ids, int64_t R, int32_t E, int32_t budget, int32_t n_slots,
+                                 int32_t* slot_of, int32_t* hits, int32_t* target, int32_t* promote,
+                                 int32_t* promote_slot, int32_t* demote, int32_t* counts, void* stream) {
+    const char* fn = "moe_residency_refresh";
+    if (!slot_of || !hits || !target || !promote || !promote_slot || !demote || !counts || (R > 0 && !ids))
+        return fail(MOE_E_ARG, fn, "null pointer argument");
+    if (R < 0) return fail(MOE_E_SHAPE, fn, "R=%lld < 0", static_cast<long long>(R));
+    if (E < 1 || E > 512) return fail(MOE_E_SHAPE, fn, "E=%d outside [1, 512]", E);
+    if (budget < 0 || budget > E) return fail(MOE_E_SHAPE, fn, "budget=%d outside [0, E=%d]", budget, E);
+    if (n_slots < budget || n_slots > 512)
+        return fail(MOE_E_SHAPE, fn, "n_slots=%d outside [budget=%d, 512]", n_slots, budget);
+    return hip_status(fn, moe::launch_residency_refresh(ids, R, E, budget, n_slots, slot_of, hits, target, promote,
+                                                        promote_slot, demote, counts,
+                                                        static_cast<hipStream_t>(stream)));
+}
+
+int32_t moe_refresh_due(int32_t every, int64_t step, int32_t prefill_block, int32_t offload) {
+    if (!offload) return 0;
+    if (prefill_block || every <= 1) return 1;
+    return step % every == 0 ? 1 : 0;
+}
+
+int32_t moe_budget_from_memory(uint64_t free_bytes, uint64_t reserve_bytes, uint64_t expert_bytes, int32_t layers,
+                               int32_t max_per_layer, int32_t E) {
+    const int64_t cap = std::min<int64_t>(max_per_layer, E);
+    if (expert_bytes == 0 || layers <= 0) return static_cast<int32_t>(std::max<int64_t>(cap, 0));
+    const uint64_t usable = free_bytes > reserve_bytes ? free_bytes - reserve_bytes : 0;
+    const uint64_t per_layer = usable / (expert_bytes * static_cast<uint64_t>(layers));
+    return static_cast<int32_t>(std::max<int64_t>(std::min<int64_t>(static_cast<int64_t>(std::min<uint64_t>(per_layer, 1u << 30)), cap), 0));
 }
 
 moe_status moe_min_weight(const int32_t* topk_ids, const float* topk_w, int32_t T, int32_t k, int32_t E,

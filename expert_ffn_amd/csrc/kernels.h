@@ -13,6 +13,10 @@ hipError_t launch_route_topk(const float* logits, int T, int E, int k, int renor
 int64_t router_part_floats(int T, int H, int E);
 hipError_t launch_router_topk(const void* x, bool xf32, const float* wr, int T, int H, int E, int k, int renorm,
                               float* logits, float* part, int* ids, float* w, hipStream_t s);
+// residency refresh: one workgroup, E <= 512, budget <= S <= 512; slot_of updated in place
+hipError_t launch_residency_refresh(const int* ids, int64_t R, int E, int budget, int S, int* slot_of, int* hits,
+                                    int* target, int* promote, int* promote_slot, int* demote, int* counts,
+                                    hipStream_t s);
 // min_weight partial routing: ids_out / w_out (may alias ids / w), miss [E] (zeroed here)
 hipError_t launch_min_weight(const int* ids, const float* w, int T, int k, int E, const int* slot_of, float share,
                              int* ids_out, float* w_out, int* miss, hipStream_t s);

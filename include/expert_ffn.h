@@ -169,6 +169,50 @@ moe_status moe_router_topk(const void* x, int32_t x_dtype, int32_t T, int32_t H,
                            float* topk_w, void* stream);
 
 /*
+ * Residency refresh from the device's routing (rlx_runtime expert_pool.rs,
+ * TIDE-style placement: count token hits per expert, take the budget most-hit
+ * experts, promote and demote in pairs to limit copies).  One launch:
+ *   hits[e]   (device int32 [E] out) routes of ids (device int32 [R], e.g. a
+ *             step's topk_ids) with id e; ids outside [0, E) are not counted
+ *   target    (device int32 [budget] out) the experts with hits > 0, most
+ *             hits first, equal counts lower id first, at most budget; the
+ *             rest -1
+ *   promote   (device int32 [E] out) the target experts not resident
+ *             (slot_of < 0), in target order; promote_slot the slot each
+ *             takes: the slot of the paired demotion, then the lowest slots
+ *             of [0, n_slots) that no resident expert holds
+ *   demote    (device int32 [E] out) resident experts outside the target, in
+ *             ascending id, as many as there are promotions (residents
+ *             beyond that stay)
+ *   counts    (device int32 [3] out) {targets, promotions, demotions}
+ *   slot_of   (device int32 [E], in and out) the layer's table, rewritten:
+ *             demoted -1, promoted their slot.  The caller copies each
+ *             promoted expert into its slot (moe_fill_slot) before the table
+ *             is used by a step.
+ * 1 <= E <= 512, 0 <= budget <= E, budget <= n_slots <= 512; the resident
+ * experts must hold distinct slots below n_slots.
+ */
+moe_status moe_residency_refresh(const int32_t* ids, int64_t R, int32_t E, int32_t budget, int32_t n_slots,
+                                 int32_t* slot_of, int32_t* hits, int32_t* target, int32_t* promote,
+                                 int32_t* promote_slot, int32_t* demote, int32_t* counts, void* stream);
+
+/*
+ * When to refresh (host; rlx_runtime expert_pool.rs, should_refresh): never
+ * without offload (budget < E); always for a prefill block or with every <= 1;
+ * otherwise on steps that are multiples of every.
+ */
+int32_t moe_refresh_due(int32_t every, int64_t step, int32_t prefill_block, int32_t offload);
+
+/*
+ * Experts per layer that fit in memory (host; rlx_runtime expert_pool.rs,
+ * gpu_expert_budget_from_vram): (free - reserve) / (expert_bytes * layers),
+ * at most min(max_per_layer, E); min(max_per_layer, E) when expert_bytes or
+ * layers is 0.
+ */
+int32_t moe_budget_from_memory(uint64_t free_bytes, uint64_t reserve_bytes, uint64_t expert_bytes, int32_t layers,
+                               int32_t max_per_layer, int32_t E);
+
+/*
  * min_weight partial routing (prain README, "Trading quality for speed": the
  * share of each token's router weight that must be computed; below 1 a token
  * skips its lightest experts that are not resident once it has that share,

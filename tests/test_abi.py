@@ -127,3 +127,22 @@ def test_workspace_grows_with_tokens(L):
     b = L.workspace_bytes(1024, 8, 128, 2816, 704, 2)
     assert 0 < a < b
     assert b >= 1024 * 8 * 704 * 2 + 1024 * 2816 * 2
+
+
+def test_refresh_schedule_and_budget_printed_vectors(L):
+    from conftest import read_golden
+    n = 0
+    for row in read_golden("rlx_expert_pool_vectors.txt"):
+        if row[0] == "refresh_due":
+            step, prefill, want = (int(v) for v in row[1:])
+            assert L.refresh_due(3, step, bool(prefill), True) == bool(want)
+            n += 1
+        elif row[0] == "budget":
+            args = [int(v) for v in row[1].split()]
+            b = L.budget_from_memory(*args)
+            assert b == int(row[2]) and 0 < b <= 128
+            n += 1
+    assert n == 6
+    assert not L.refresh_due(1, 0, True, False)          # no offload: never
+    assert L.refresh_due(1, 7, False, True)              # every forward
+    assert L.budget_from_memory(0, 0, 0, 20, 64, 32) == 32

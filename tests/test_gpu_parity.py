@@ -514,3 +514,57 @@ def test_router_topk(L, T, E, k, H, xdt):
     same = np.all(got_i == rid, axis=1)
     assert np.max(np.abs(got_w[same] - rw[same])) <= 1e-5
     assert exact >= T - max(1, T // 100)
+
+
+# ------------------------------------------------------ residency refresh ----
+def _refresh_gpu(L, ids, E, budget, S, slot_of):
+    d = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.int32)).cuda()
+    ids_d, slot_d = d(np.asarray(ids, np.int32).reshape(-1)), d(slot_of)
+    outs = {n: torch.full((m,), -9, dtype=torch.int32, device="cuda")
+            for n, m in (("hits", E), ("target", max(budget, 1)), ("promote", E), ("promote_slot", E),
+                         ("demote", E), ("counts", 3))}
+    L.residency_refresh(ids_d, E, budget, S, slot_d, outs["hits"], outs["target"], outs["promote"],
+                        outs["promote_slot"], outs["demote"], outs["counts"])
+    torch.cuda.synchronize()
+    o = {n: to_np(t) for n, t in outs.items()}
+    o["slot_of"] = to_np(slot_d)
+    return o
+
+
+@pytest.mark.parametrize("case", range(12))
+def test_residency_refresh_bit_exact(L, case):
+    # hit counts, target, promotions (with slots), demotions and the new table
+    # equal the oracle's; cases include Gemma decode (16 tokens x top-8) and
+    # prefill (1024 x 8) routing, empty routing, budget 0 and budget = E
+    import oracle as ora
+    r = np.random.default_rng(100 + case)
+    if case == 0:
+        E, budget, S, R = 128, 15, 15, 128
+    elif case == 1:
+        E, budget, S, R = 128, 15, 20, 8192
+    elif case == 2:
+        E, budget, S, R = 512, 200, 512, 3000
+    elif case == 3:
+        E, budget, S, R = 64, 0, 8, 100
+    elif case == 4:
+        E, budget, S, R = 32, 32, 32, 0
+    else:
+        E = int(r.integers(2, 513))
+        budget = int(r.integers(0, E + 1))
+        S = int(r.integers(max(budget, 1), 513))
+        R = int(r.integers(0, 5000))
+    n_res = int(r.integers(0, min(S, E) + 1))
+    slot_of = np.full(E, -1, np.int32)
+    slot_of[r.choice(E, n_res, replace=False)] = r.choice(S, n_res, replace=False)
+    ids = r.integers(-1, E + 1, R).astype(np.int32)
+    log(f"residency refresh case {case}: E={E} budget={budget} slots={S} routes={R} resident={n_res}")
+    got = _refresh_gpu(L, ids, E, budget, S, slot_of)
+    want = ora.residency_refresh(ids, E, budget, S, slot_of)
+    nt, np_, nd = (int(v) for v in want["counts"])
+    assert got["counts"].tolist() == [nt, np_, nd]
+    assert np.array_equal(got["hits"], want["hits"])
+    assert np.array_equal(got["target"][:budget], want["target"])
+    assert np.array_equal(got["promote"][:np_], want["promote"])
+    assert np.array_equal(got["promote_slot"][:np_], want["promote_slot"])
+    assert np.array_equal(got["demote"][:nd], want["demote"])
+    assert np.array_equal(got["slot_of"], want["slot_of"])

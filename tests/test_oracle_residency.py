@@ -47,6 +47,8 @@ def test_printed_vectors(ora):
             ids, mask = ([int(v) for v in x.split()] for x in f)
             r = ora.residency_refresh(ids, 4, 2, 2, _table(4, [0, 1]))   # a new pool: resident 0 .. budget-1
             assert (r["slot_of"] >= 0).astype(int).tolist() == mask
+        else:
+            continue   # host schedule rows: the library's helpers (test_abi.py)
         seen.add(name)
     assert seen == {"count_hits", "top_by_count", "placement", "refresh_mask"}
 
