@@ -139,8 +139,11 @@ def realised_routing(lib, runner, logits):
 
 
 def kernel_source_hash():
+    """Hash of the sources the gate/up decode kernel is compiled from (its
+    file and the headers it includes): counter figures taken on other
+    sources are not used."""
     h = hashlib.sha256()
-    for name in sorted(os.listdir(os.path.join(ROOT, "expert_ffn_amd", "csrc"))):
+    for name in ("common.h", "ffn.hip", "kernels.h"):
         with open(os.path.join(ROOT, "expert_ffn_amd", "csrc", name), "rb") as f:
             h.update(name.encode() + f.read())
     return h.hexdigest()[:16]
