@@ -16,7 +16,8 @@
  *   [prain]  prain/README.md -- sections "Expert formats", "int4 experts on
  *            RDNA2", "Trading quality for speed", "Profile".
  *   [rlx]    rlx_runtime/expert_pool.rs (docs.rs, rlx-runtime 0.2.2) --
- *            count_hits, target_gpu_from_counts and their unit tests.
+ *            count_hits, target_gpu_from_counts, apply_target_placement and
+ *            their unit tests.
  *   [strata] Winery-Strata src/core/remote_experts.cpp -- RemoteExperts::begin
  *            and RemoteExperts::finish.
  * Where the pages leave a step open, the reading taken is stated at the
