@@ -516,6 +516,68 @@ def test_router_topk(L, T, E, k, H, xdt):
     assert exact >= T - max(1, T // 100)
 
 
+def test_router_topk_softmax_over_all_and_k_equals_E(L):
+    # renorm = 0 (softmax over all E) and k = E (every expert, in rank order)
+    import oracle as ora
+    T, H = 24, 192
+    for E, k, renorm in ((16, 16, 1), (40, 5, 0), (3, 3, 0)):
+        wr = synth.router_weight(11, 0, E, H)
+        x_h = synth.x_f32(11, 0, T, H)
+        ws = torch.empty(L.router_ws_bytes(T, H, E), dtype=torch.uint8, device="cuda")
+        logits = torch.empty((T, E), dtype=torch.float32, device="cuda")
+        ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+        w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+        L.router_topk(torch.from_numpy(x_h).cuda(), torch.from_numpy(wr).cuda(), k, logits, ws, ids, w, renorm=renorm)
+        torch.cuda.synchronize()
+        ref = ora.router_logits(x_h, wr)
+        rid, rw = ora.route_topk(ref.astype(np.float32), k, renorm)
+        assert np.array_equal(to_np(ids), rid), (E, k, renorm)
+        assert np.max(np.abs(to_np(w) - rw)) <= 1e-5
+        if renorm or k == E:
+            assert np.allclose(to_np(w).sum(1), 1.0, atol=1e-5)
+
+
+def test_min_weight_share_zero_without_residents_empties_the_layer(L):
+    # share 0 and no resident expert: every route skipped, nothing to copy,
+    # and the layer's output is zero
+    from expert_ffn_amd.layer import MoeLayer
+    E, k, H, FF, T = 8, 2, 64, 64, 5
+    slot_of = torch.full((E,), -1, dtype=torch.int32, device="cuda")
+    pool = torch.zeros(L.expert_bytes(L.W_BF16, H, FF), dtype=torch.uint8, device="cuda")
+    ml = MoeLayer(E, k, H, FF, L.W_BF16, T, out_dtype=torch.float32)
+    ml.bind(pool, L.expert_bytes(L.W_BF16, H, FF), slot_of)
+    ml.select(torch.from_numpy(synth.logits(2, 0, T, E, None)).cuda(), 0.0)
+    ml.group(T)
+    x = torch.from_numpy(synth.x_bf16(2, 0, T, H).view(np.int16)).cuda().view(torch.bfloat16)
+    ml.ffn(x)
+    ml.combine(T)
+    torch.cuda.synchronize()
+    assert (to_np(ml.topk_ids[:T]) == -1).all() and not to_np(ml.topk_w[:T]).any()
+    assert not to_np(ml.miss_count).any()
+    assert int(to_np(ml.n_dropped)[0]) == T * k
+    assert not to_np(ml.y[:T]).any()
+
+
+@pytest.mark.parametrize("fmt", [0, 1, 2])
+def test_fill_slot_smallest_expert_and_errors(L, fmt):
+    # H = FF = 64 (one 64-group per row, one 32-row tile per w2 block), then
+    # the host-side rejections: staging overlapping the slot, a misaligned slot
+    import oracle as ora
+    H = FF = 64
+    w13, w2 = synth.expert_weights(31, 0, 0, H, FF)
+    canon = ora.pack_expert_canonical(fmt, w13, w2, H, FF)
+    sb = L.expert_bytes(fmt, H, FF)
+    buf = torch.zeros(3 * sb + 256, dtype=torch.uint8, device="cuda")
+    src_h = torch.from_numpy(canon).pin_memory()
+    L.fill_slot(fmt, src_h, H, FF, buf[:sb], staging=buf[sb:2 * sb])
+    torch.cuda.synchronize()
+    assert np.array_equal(to_np(buf[:sb]), ora.pack_expert(fmt, w13, w2, H, FF))
+    with pytest.raises(L.MoeError, match="overlaps"):
+        L.fill_slot(fmt, src_h, H, FF, buf[:sb], staging=buf[sb // 2:sb // 2 + sb])
+    with pytest.raises(L.MoeError, match="aligned"):
+        L.fill_slot(fmt, src_h, H, FF, buf[8:8 + sb], staging=buf[2 * sb + 256:])
+
+
 # ------------------------------------------------------ residency refresh ----
 def _refresh_gpu(L, ids, E, budget, S, slot_of):
     d = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.int32)).cuda()
