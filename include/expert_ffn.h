@@ -42,7 +42,7 @@ typedef enum {
     MOE_OK = 0,
     MOE_E_ARG = 1,          /* a null pointer, negative size or unknown enum    */
     MOE_E_SHAPE = 2,        /* sizes that break a shape rule above              */
-    MOE_E_UNSUPPORTED = 3,  /* a combination this build does not implement      */
+    MOE_E_UNSUPPORTED = 3,  /* a combination the library does not implement     */
     MOE_E_WORKSPACE = 4,    /* workspace smaller than moe_workspace_bytes()     */
     MOE_E_HIP = 5           /* the HIP runtime reported an error                */
 } moe_status;
