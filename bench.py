@@ -631,6 +631,136 @@ def measure_miss_step(lib, dev, seed, tokens=16, n_res=15, shares=(1.0, 0.6, 0.4
                 rows=rows, all_resident=ref)
 
 
+def measure_refresh_step(lib, dev, seed, tokens=33, S=15, every=4, share=1.0):
+    """Decode (one token per step) through 30 int4 layers with S = 15 resident
+    slots per layer, misses copied in as in the miss step, with and without a
+    residency refresh (rlx_runtime expert_pool.rs, TIDE-style: the budget
+    most-hit experts, paired promote/demote) every `every` tokens from the
+    hit counts of the last `every` tokens' routes; promoted experts are
+    copied into their slots (one DMA + unpack each).  Uniform and Zipf(1.1)
+    routing.  Each layer has its own region of S resident slots plus k miss
+    slots; the resident set starts as experts 0 .. S-1 (the crate's initial
+    pool).  The host copies are one layer's packed blobs, as in the miss
+    step: a copy's cost does not depend on the bytes."""
+    import ctypes
+    import torch
+    E, k, H, FF, Lyr = G["E"], G["k"], G["H"], G["FF"], synth.CONFIGS["int4_stack"]["L"]
+    fmt = lib.W_INT4_G64
+    sb = lib.expert_bytes(fmt, H, FF)
+    NS = S + k                                  # slots per layer region
+    log("packing one layer's experts for the host copies ...")
+    one = torch.empty(E * sb, dtype=torch.uint8, device=dev)
+    w13, w2 = synth.layer_weights_cuda(seed, 0, E, H, FF, dev)
+    for e in range(E):
+        lib.pack_expert(fmt, w13[e].view(torch.int16), w2[e].view(torch.int16), one[e * sb:(e + 1) * sb])
+    host = one.view(E, sb).cpu().pin_memory()
+    del one, w13, w2
+    pool = torch.empty(Lyr * NS * sb, dtype=torch.uint8, device=dev)
+    staging = torch.empty((E, sb), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.Stream()
+    c = lib.lib()
+    P = ctypes.c_void_p
+    s = P(stream.cuda_stream)
+    from expert_ffn_amd.layer import MoeLayer
+    ml = MoeLayer(E, k, H, FF, fmt, 1, device=dev, out_dtype=torch.bfloat16)
+    ws = ml.ws.numel()
+    miss_h = torch.zeros(E, dtype=torch.int32).pin_memory()
+    cnt_h = torch.zeros(3, dtype=torch.int32).pin_memory()
+    prom_h = torch.zeros(2 * E, dtype=torch.int32).pin_memory()
+    outs = [torch.empty(n, dtype=torch.int32, device=dev) for n in (E, S, E, E, E, 3)]
+    hits, target, promote, promote_slot, demote, counts = outs
+    rows = []
+    for zipf in (None, 1.1):
+        logits, xs = layer_inputs(seed + 5, Lyr, tokens, E, H, dev, zipf)
+        for refresh in (False, True):
+            # resident experts 0 .. S-1 in slots 0 .. S-1 of every layer's region
+            for l in range(Lyr):
+                for e in range(S):
+                    lib.fill_slot(fmt, host[e], H, FF, pool[(l * NS + e) * sb:(l * NS + e + 1) * sb],
+                                  staging=staging[e], stream=stream)
+            stream.synchronize()
+            base = []
+            for l in range(Lyr):
+                t = torch.full((E,), -1, dtype=torch.int32)
+                t[:S] = torch.arange(S, dtype=torch.int32)
+                base.append(t.to(dev))
+            tab = torch.full((E,), -1, dtype=torch.int32).pin_memory()
+            tmp_d = torch.empty(E, dtype=torch.int32, device=dev)
+            ring = [torch.full((every * k,), -1, dtype=torch.int32, device=dev) for _ in range(Lyr)]
+            copies = [0, 0]   # miss copies, promotion copies
+
+            def token(i):
+                for l in range(Lyr):
+                    pl = pool.data_ptr() + l * NS * sb
+                    lg, x = logits[l][i:i + 1], xs[l][i:i + 1]
+                    ids_p, w_p = P(ml.topk_ids.data_ptr()), P(ml.topk_w.data_ptr())
+                    assert not c.moe_route_topk(P(lg.data_ptr()), 1, E, k, 1, ids_p, w_p, s)
+                    ring[l][(i % every) * k:(i % every + 1) * k].copy_(ml.topk_ids[0], non_blocking=True)
+                    if refresh and i % every == every - 1:
+                        assert not c.moe_residency_refresh(P(ring[l].data_ptr()), every * k, E, S, S,
+                                                           P(base[l].data_ptr()), *(P(t.data_ptr()) for t in outs), s)
+                        cnt_h.copy_(counts, non_blocking=True)
+                        prom_h[:E].copy_(promote, non_blocking=True)
+                        prom_h[E:].copy_(promote_slot, non_blocking=True)
+                        stream.synchronize()
+                        npro = int(cnt_h[1])
+                        for j in range(npro):
+                            e, sl = int(prom_h[j]), int(prom_h[E + j])
+                            staging[j].copy_(host[e], non_blocking=True)
+                        for j in range(npro):
+                            e, sl = int(prom_h[j]), int(prom_h[E + j])
+                            assert not c.moe_fill_slot(fmt, P(staging[j].data_ptr()), 0, H, FF, None,
+                                                       P(pl + sl * sb), s)
+                        copies[1] += npro
+                    sd = P(base[l].data_ptr())
+                    assert not c.moe_min_weight(ids_p, w_p, 1, k, E, sd, ctypes.c_float(share), ids_p, w_p,
+                                                P(ml.miss_count.data_ptr()), s)
+                    miss_h.copy_(ml.miss_count, non_blocking=True)
+                    stream.synchronize()
+                    missed = np.flatnonzero(miss_h.numpy())
+                    if missed.size:
+                        tab.copy_(base[l])
+                        for j, e in enumerate(missed):
+                            staging[j].copy_(host[e], non_blocking=True)
+                        for j, e in enumerate(missed):
+                            assert not c.moe_fill_slot(fmt, P(staging[j].data_ptr()), 0, H, FF, None,
+                                                       P(pl + (S + j) * sb), s)
+                            tab[e] = S + j
+                        tmp_d.copy_(tab, non_blocking=True)
+                        sd = P(tmp_d.data_ptr())
+                        copies[0] += missed.size
+                    assert not c.moe_permute(ids_p, 1, k, E, sd, P(ml.offsets.data_ptr()),
+                                             P(ml.sorted_route.data_ptr()), P(ml.route_pos.data_ptr()),
+                                             P(ml.n_dropped.data_ptr()), s)
+                    assert not c.moe_expert_ffn(P(pl), sb, sd, E, H, FF, fmt, 0, P(x.data_ptr()), 1, 1, k,
+                                                P(ml.offsets.data_ptr()), P(ml.sorted_route.data_ptr()),
+                                                P(ml.out_routes.data_ptr()), 1, P(ml.ws.data_ptr()), ws, s)
+                    assert not c.moe_combine(P(ml.out_routes.data_ptr()), 1, w_p, P(ml.route_pos.data_ptr()), 1, k,
+                                             H, P(ml.y.data_ptr()), 1, s)
+                    if missed.size:
+                        stream.synchronize()   # tab and the miss slots are reused by the next layer
+
+            with torch.cuda.stream(stream):
+                for i in range(every):          # warm-up: one refresh interval
+                    token(i)
+                stream.synchronize()
+                copies[0] = copies[1] = 0
+                t0 = time.perf_counter()
+                for i in range(every, tokens):
+                    token(i)
+                stream.synchronize()
+                dt = time.perf_counter() - t0
+            n = tokens - every
+            rows.append(dict(zipf=zipf, refresh_every=every if refresh else None, tokens_per_s=round(n / dt, 2),
+                             ms_per_token=round(dt / n * 1e3, 2), miss_copies_per_token=round(copies[0] / n, 1),
+                             promotion_copies_per_token=round(copies[1] / n, 1)))
+            log(json.dumps(rows[-1]))
+    return dict(metric="decode tokens/s with expert misses and residency refresh", unit="tokens/s",
+                config=dict(workload=f"Gemma-4-26B-A4B int4, {Lyr} layers, one token per step, {S} of {E} experts "
+                                     f"resident per layer, misses copied from pinned host memory, min_weight {share}",
+                            tokens=tokens - every), rows=rows)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -651,6 +781,9 @@ def main():
     ap.add_argument("--configs", action="store_true",
                     help="instead of the stack step: single-layer timings of the other workloads "
                          "(one JSON object per line)")
+    ap.add_argument("--refresh-step", action="store_true",
+                    help="instead of the stack step: decode with misses, with and without a residency refresh "
+                         "every 4 tokens, uniform and Zipf routing (one JSON line)")
     ap.add_argument("--residency", action="store_true",
                     help="instead of the stack step: residency refresh timings (one JSON line)")
     ap.add_argument("--router", action="store_true",
@@ -677,6 +810,9 @@ def main():
     import expert_ffn_amd as lib
     lib.lib()
     dev = torch.device("cuda:0")
+    if args.refresh_step:
+        print(json.dumps(measure_refresh_step(lib, dev, args.seed)), flush=True)
+        return
     if args.residency:
         print(json.dumps(measure_residency(lib, dev, args.seed)), flush=True)
         return
