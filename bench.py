@@ -13,6 +13,16 @@ GB/s of the step, the roofline of the dominant kernel (the gate/up half of the
 expert FFN, timed with HIP events on its own stream in an instrumented pass of
 the same steps), the 1024-token prefill chunk through the same stack (MFMA
 utilisation), and the CPU oracle timed on a bounded sample on this host.
+
+Other measurements, each instead of the step and printing its own JSON line:
+  --configs        single-layer timings of the other workloads (bf16 / int8 /
+                   int4, decode and prefill, uniform and Zipf routing)
+  --slot-fill      int4 expert slot fill: pinned DMA, unpack, and both
+  --miss-step      decode with 15 of 128 experts resident, misses copied in,
+                   at min_weight 1.0 / 0.6 / 0.4
+  --refresh-step   the same with a residency refresh every 4 tokens
+  --router         router GEMV + top-k against matmul + top-k
+  --residency      the residency refresh kernel alone
 """
 from __future__ import annotations
 
