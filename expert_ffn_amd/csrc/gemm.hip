@@ -52,7 +52,7 @@ constexpr int GM_ROWS = 128;   // routes per narrow tile
 // tile twice as wide: half the activation traffic per weight byte); larger
 // ones take 128-route narrow tiles.
 #ifndef GEMM_WIDE_MAX
-#define GEMM_WIDE_MAX 64
+#define GEMM_WIDE_MAX 96
 #endif
 constexpr int GM_GBUF = 16384; // one group of a stage: [4 K steps][4 route blocks] x 1 KB
 // A workgroup of NW waves (4 or 8): wave (mh, nq), NQ = NW / 2 column blocks
