@@ -595,15 +595,14 @@ def measure_miss_step(lib, dev, seed, tokens=16, n_res=15, shares=(1.0, 0.6, 0.4
                 missed = np.flatnonzero(miss_h.numpy())
                 if missed.size:
                     tab[l].copy_(base[l])
-                    # the layer's copies back to back on the copy engine, then the unpacks
-                    # (the same DMA + unpack per expert, one engine hand-off per layer)
-                    for j, e in enumerate(missed):
-                        staging[j].copy_(host[e], non_blocking=True)
-                    for j, e in enumerate(missed):
-                        sl = int(slots[l, e])
-                        assert not c.moe_fill_slot(fmt, P(staging[j].data_ptr()), 0, H, FF, None,
-                                                   P(pool.data_ptr() + sl * sb), s)
-                        tab[l][e] = sl
+                    # the layer's copies back to back on the copy engine, then one
+                    # unpack launch for all of them (moe_fill_slots)
+                    n = missed.size
+                    srcs = (P * n)(*[host[e].data_ptr() for e in missed])
+                    dsts = (P * n)(*[pool.data_ptr() + int(slots[l, e]) * sb for e in missed])
+                    assert not c.moe_fill_slots(fmt, n, srcs, H, FF, P(staging.data_ptr()), dsts, s)
+                    for e in missed:
+                        tab[l][e] = int(slots[l, e])
                     slot_d[l].copy_(tab[l], non_blocking=True)
                     copies += missed.size
                 assert not c.moe_permute(P(ml.topk_ids.data_ptr()), 1, k, E, sd, P(ml.offsets.data_ptr()),
@@ -714,13 +713,10 @@ def measure_refresh_step(lib, dev, seed, tokens=33, S=15, every=4, share=1.0):
                         prom_h[E:].copy_(promote_slot, non_blocking=True)
                         stream.synchronize()
                         npro = int(cnt_h[1])
-                        for j in range(npro):
-                            e, sl = int(prom_h[j]), int(prom_h[E + j])
-                            staging[j].copy_(host[e], non_blocking=True)
-                        for j in range(npro):
-                            e, sl = int(prom_h[j]), int(prom_h[E + j])
-                            assert not c.moe_fill_slot(fmt, P(staging[j].data_ptr()), 0, H, FF, None,
-                                                       P(pl + sl * sb), s)
+                        if npro:
+                            srcs = (P * npro)(*[host[int(prom_h[j])].data_ptr() for j in range(npro)])
+                            dsts = (P * npro)(*[pl + int(prom_h[E + j]) * sb for j in range(npro)])
+                            assert not c.moe_fill_slots(fmt, npro, srcs, H, FF, P(staging.data_ptr()), dsts, s)
                         copies[1] += npro
                     sd = P(base[l].data_ptr())
                     assert not c.moe_min_weight(ids_p, w_p, 1, k, E, sd, ctypes.c_float(share), ids_p, w_p,
@@ -730,11 +726,11 @@ def measure_refresh_step(lib, dev, seed, tokens=33, S=15, every=4, share=1.0):
                     missed = np.flatnonzero(miss_h.numpy())
                     if missed.size:
                         tab.copy_(base[l])
+                        n = missed.size
+                        srcs = (P * n)(*[host[e].data_ptr() for e in missed])
+                        dsts = (P * n)(*[pl + (S + j) * sb for j in range(n)])
+                        assert not c.moe_fill_slots(fmt, n, srcs, H, FF, P(staging.data_ptr()), dsts, s)
                         for j, e in enumerate(missed):
-                            staging[j].copy_(host[e], non_blocking=True)
-                        for j, e in enumerate(missed):
-                            assert not c.moe_fill_slot(fmt, P(staging[j].data_ptr()), 0, H, FF, None,
-                                                       P(pl + (S + j) * sb), s)
                             tab[e] = S + j
                         tmp_d.copy_(tab, non_blocking=True)
                         sd = P(tmp_d.data_ptr())

@@ -62,11 +62,12 @@ def lib():
         L.moe_budget_from_memory.restype = i32
         L.moe_min_weight.argtypes = [P, P, i32, i32, i32, P, ctypes.c_float, P, P, P, P]
         L.moe_fill_slot.argtypes = [i32, P, i32, i32, i32, P, P, P]
+        L.moe_fill_slots.argtypes = [i32, i32, P, i32, i32, P, P, P]
         L.moe_verify_slot.argtypes = [i32, P, i32, i32, P, P, P]
         L.moe_slot_admit.argtypes = [P, i32, P, i32, i32]
         for name in ("moe_blob_layout", "moe_route_topk", "moe_permute", "moe_route_permute", "moe_expert_ffn",
                      "moe_ffn_gate_up", "moe_ffn_down", "moe_combine", "moe_quantize",
-                     "moe_pack_expert", "moe_set_ffn_path", "moe_router_topk", "moe_residency_refresh", "moe_min_weight", "moe_fill_slot", "moe_verify_slot",
+                     "moe_pack_expert", "moe_set_ffn_path", "moe_router_topk", "moe_residency_refresh", "moe_min_weight", "moe_fill_slot", "moe_fill_slots", "moe_verify_slot",
                      "moe_slot_admit"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -191,6 +192,16 @@ def fill_slot(fmt: int, src, H: int, FF: int, slot, staging=None, stream=None, d
     kernel alone) -> slot, byte for byte the packed blob."""
     on_host = 0 if src.is_cuda else (2 if direct else 1)
     _check(lib().moe_fill_slot(fmt, _ptr(src), on_host, H, FF, _ptr(staging), _ptr(slot), _stream(stream)))
+
+
+def fill_slots(fmt: int, srcs, H: int, FF: int, slots, staging, stream=None):
+    """Canonical blobs srcs (host tensors) -> slots (device tensors): the
+    copies back to back into staging, then one unpack kernel for all."""
+    n = len(srcs)
+    assert len(slots) == n
+    src_arr = (ctypes.c_void_p * max(n, 1))(*[t.data_ptr() for t in srcs])
+    dst_arr = (ctypes.c_void_p * max(n, 1))(*[t.data_ptr() for t in slots])
+    _check(lib().moe_fill_slots(fmt, n, src_arr, H, FF, _ptr(staging), dst_arr, _stream(stream)))
 
 
 def verify_slot(fmt: int, src, H: int, FF: int, slot, mismatches, stream=None):

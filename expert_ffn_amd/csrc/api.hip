@@ -379,6 +379,33 @@ moe_status moe_fill_slot(int32_t wfmt, const void* src, int32_t src_on_host, int
     return hip_status(fn, moe::launch_fill_slot(wfmt, dev, src_on_host == 2, H, FF, off, slot, s));
 }
 
+moe_status moe_fill_slots(int32_t wfmt, int32_t n, const void* const* srcs, int32_t H, int32_t FF, void* staging,
+                          void* const* slots, void* stream) {
+    const char* fn = "moe_fill_slots";
+    if (n < 0 || n > moe::FILL_MAX) return fail(MOE_E_SHAPE, fn, "n=%d outside [0, %d]", n, moe::FILL_MAX);
+    if (!fmt_ok(wfmt)) return fail(MOE_E_ARG, fn, "unknown weight format %d", wfmt);
+    uint64_t off[5];
+    if (!layout(wfmt, H, FF, off)) return fail(MOE_E_SHAPE, fn, "H=%d FF=%d invalid for format %d", H, FF, wfmt);
+    if (off[4] >= (1ull << 31)) return fail(MOE_E_SHAPE, fn, "blob of %llu bytes is not below 2 GiB",
+                                            static_cast<unsigned long long>(off[4]));
+    if (n == 0) return MOE_OK;
+    if (!srcs || !slots || !staging) return fail(MOE_E_ARG, fn, "null pointer argument");
+    if (!al16(staging)) return fail(MOE_E_ARG, fn, "staging must be 16-byte aligned");
+    for (int32_t j = 0; j < n; ++j) {
+        if (!srcs[j] || !slots[j]) return fail(MOE_E_ARG, fn, "null pointer for expert %d", j);
+        if (!al16(slots[j])) return fail(MOE_E_ARG, fn, "slot %d is not 16-byte aligned", j);
+        const uintptr_t a = reinterpret_cast<uintptr_t>(slots[j]), b = reinterpret_cast<uintptr_t>(staging);
+        if (a < b + n * off[4] && b < a + off[4]) return fail(MOE_E_ARG, fn, "slot %d overlaps the staging buffer", j);
+    }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    uint8_t* st = static_cast<uint8_t*>(staging);
+    for (int32_t j = 0; j < n; ++j) {
+        const hipError_t e = hipMemcpyAsync(st + j * off[4], srcs[j], off[4], hipMemcpyHostToDevice, s);
+        if (e != hipSuccess) return hip_status(fn, e);
+    }
+    return hip_status(fn, moe::launch_fill_slots(wfmt, staging, n, H, FF, off, slots, s));
+}
+
 moe_status moe_verify_slot(int32_t wfmt, const void* src, int32_t H, int32_t FF, const void* slot,
                            int32_t* mismatches, void* stream) {
     const char* fn = "moe_verify_slot";

@@ -33,6 +33,10 @@ hipError_t launch_combine(const void* out_routes, int out_dt, const float* w, co
 // off: the blob layout (5 entries, host)
 hipError_t launch_fill_slot(int fmt, const void* src, bool host_src, int H, int FF, const uint64_t* off, void* slot,
                             hipStream_t s);
+// n (<= FILL_MAX) canonical blobs back to back at src (device) -> slots[j] (host array of device pointers)
+constexpr int FILL_MAX = 64;
+hipError_t launch_fill_slots(int fmt, const void* src, int n, int H, int FF, const uint64_t* off, void* const* slots,
+                             hipStream_t s);
 // mismatches (device): 16-byte chunks of slot that differ from the canonical blob src
 hipError_t launch_verify_slot(int fmt, const void* src, int H, int FF, const uint64_t* off, const void* slot,
                               int32_t* mismatches, hipStream_t s);

@@ -115,6 +115,17 @@ __global__ __launch_bounds__(256) void fill_slot_kernel(const u32x4* __restrict_
     if (i < m.nchunks) dst[slot_chunk(m, i)] = src[i];
 }
 
+// several experts at once: blockIdx.y picks the expert, its canonical blob at
+// src + y * blob bytes and its slot at dst.p[y]
+struct SlotPtrs {
+    u32x4* p[FILL_MAX];
+};
+
+__global__ __launch_bounds__(256) void fill_slots_kernel(const u32x4* __restrict__ src, SlotPtrs dst, SlotMap m) {
+    const uint32_t i = blockIdx.x * 256 + threadIdx.x;
+    if (i < m.nchunks) dst.p[blockIdx.y][slot_chunk(m, i)] = src[static_cast<uint64_t>(blockIdx.y) * m.nchunks + i];
+}
+
 // count of 16-byte chunks of the slot that differ from the canonical blob
 __global__ __launch_bounds__(256) void verify_slot_kernel(const u32x4* __restrict__ src,
                                                           const u32x4* __restrict__ slot, SlotMap m,
@@ -152,6 +163,16 @@ hipError_t launch_fill_slot(int fmt, const void* src, bool host_src, int H, int 
     const SlotMap m = slot_map(fmt, H, FF, off);
     hipLaunchKernelGGL(host_src ? fill_slot_kernel<true> : fill_slot_kernel<false>, dim3((m.nchunks + 255) / 256),
                        dim3(256), 0, s, static_cast<const u32x4*>(src), static_cast<u32x4*>(slot), m);
+    return hipGetLastError();
+}
+
+hipError_t launch_fill_slots(int fmt, const void* src, int n, int H, int FF, const uint64_t* off, void* const* slots,
+                             hipStream_t s) {
+    const SlotMap m = slot_map(fmt, H, FF, off);
+    SlotPtrs d{};
+    for (int j = 0; j < n; ++j) d.p[j] = static_cast<u32x4*>(slots[j]);
+    hipLaunchKernelGGL(fill_slots_kernel, dim3((m.nchunks + 255) / 256, n), dim3(256), 0, s,
+                       static_cast<const u32x4*>(src), d, m);
     return hipGetLastError();
 }
 

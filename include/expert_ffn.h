@@ -350,6 +350,18 @@ moe_status moe_fill_slot(int32_t wfmt, const void* src, int32_t src_on_host, int
                          void* staging, void* slot, void* stream);
 
 /*
+ * n experts at once (0 <= n <= 64), as moe_fill_slot with src_on_host = 1 for
+ * each: srcs (host array of n host pointers, pinned for asynchronous copies)
+ * are copied back to back into staging (device, n * moe_expert_bytes() bytes,
+ * 16-byte aligned), then one kernel unpacks all n into slots (host array of n
+ * device pointers, 16-byte aligned, none overlapping staging).  The copy
+ * engine runs the n copies without a hand-off to the compute queue between
+ * them.  Same formats, layout rules and errors as moe_fill_slot.
+ */
+moe_status moe_fill_slots(int32_t wfmt, int32_t n, const void* const* srcs, int32_t H, int32_t FF, void* staging,
+                          void* const* slots, void* stream);
+
+/*
  * Check a filled slot against the canonical blob src (both device, 16-byte
  * aligned): *mismatches (device int32, overwritten) receives the number of
  * 16-byte chunks of the slot that differ from what moe_fill_slot writes.

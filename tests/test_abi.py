@@ -96,6 +96,12 @@ def test_host_validation_errors(L):
     assert rc == 1 and "aligned" in msg
     rc, msg = _call(L, "moe_verify_slot", 2, fake, 2816, 704, fake, None, None)
     assert rc == 1
+    rc, msg = _call(L, "moe_fill_slots", 2, 65, fake, 2816, 704, fake, fake, None)
+    assert rc == 2 and "n=65" in msg
+    rc, msg = _call(L, "moe_fill_slots", 2, 0, None, 2816, 704, None, None, None)
+    assert rc == 0                                       # nothing to do, nothing enqueued
+    rc, msg = _call(L, "moe_fill_slots", 2, 2, None, 2816, 704, fake, fake, None)
+    assert rc == 1 and "null" in msg
     rc, msg = _call(L, "moe_min_weight", fake, fake, 4, 8, 128, fake, ctypes.c_float(float("nan")), fake, fake,
                     fake, None)
     assert rc == 1 and "NaN" in msg

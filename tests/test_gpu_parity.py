@@ -558,6 +558,33 @@ def test_min_weight_share_zero_without_residents_empties_the_layer(L):
     assert not to_np(ml.y[:T]).any()
 
 
+@pytest.mark.parametrize("fmt", [1, 2])
+def test_fill_slots_batch_bit_exact(L, fmt):
+    # five experts' canonical blobs from pinned host memory in one call, into
+    # scattered slots of a pool: each slot equals the oracle's packed blob,
+    # the slots in between stay untouched; a slot inside staging is refused
+    import oracle as ora
+    H, FF = 256, 128
+    sb = L.expert_bytes(fmt, H, FF)
+    pool = torch.full((12 * sb,), 0x5A, dtype=torch.uint8, device="cuda")
+    targets = [7, 1, 10, 4, 2]
+    canon, want = [], []
+    for e in range(5):
+        w13, w2 = synth.expert_weights(41, 0, e, H, FF)
+        canon.append(torch.from_numpy(ora.pack_expert_canonical(fmt, w13, w2, H, FF)).pin_memory())
+        want.append(ora.pack_expert(fmt, w13, w2, H, FF))
+    staging = torch.empty(5 * sb, dtype=torch.uint8, device="cuda")
+    L.fill_slots(fmt, canon, H, FF, [pool[t * sb:(t + 1) * sb] for t in targets], staging)
+    torch.cuda.synchronize()
+    got = to_np(pool).reshape(12, sb)
+    for e, t in enumerate(targets):
+        assert np.array_equal(got[t], want[e]), (e, t)
+    for t in set(range(12)) - set(targets):
+        assert (got[t] == 0x5A).all()
+    with pytest.raises(L.MoeError, match="overlaps"):
+        L.fill_slots(fmt, canon[:2], H, FF, [pool[:sb], staging[sb:2 * sb]], staging)
+
+
 @pytest.mark.parametrize("fmt", [0, 1, 2])
 def test_fill_slot_smallest_expert_and_errors(L, fmt):
     # H = FF = 64 (one 64-group per row, one 32-row tile per w2 block), then
