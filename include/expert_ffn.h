@@ -16,8 +16,10 @@
  * Conventions for every entry point:
  *   - Pointers marked "device" are device memory owned by the caller; the
  *     library keeps no pointer after a call returns and never allocates or
- *     frees device memory in the compute calls.  "host" pointers are host
- *     memory.
+ *     frees device memory in any call.  "host" pointers are host memory:
+ *     the layout query, the slot bookkeeping (moe_slot_admit) and the
+ *     sources of the slot fills (pinned memory, read by the copy engine or
+ *     the unpack kernel until the stream reaches them).
  *   - stream is a hipStream_t (NULL = the legacy default stream).  Every call
  *     only enqueues work on that stream and returns; nothing synchronises.
  *   - Arguments are checked on the host before anything is enqueued.  A call
