@@ -211,6 +211,104 @@ __global__ __launch_bounds__(PERM_THREADS) void permute_kernel(
     permute_steps<8>(S, wpre, ids, id0, res, R, E, offsets, sorted_route, route_pos, n_dropped);
 }
 
+// The same grouping for R > 1024 by ceil(R / 1024) workgroups with no
+// exchange between them: workgroup b histograms all R routes (kept routes
+// per expert, and those before its block of 1024), so every workgroup forms
+// the same offsets, and its block's routes start at offset[e] + the count of
+// earlier routes to e; inside the block the positions come from the wave
+// ballots above.  Workgroup 0 writes offsets and n_dropped; each writes the
+// -1 tail positions of its own range.  The positions equal the
+// single-workgroup ones.
+__global__ __launch_bounds__(PERM_THREADS) void permute_multi_kernel(
+    const int* __restrict__ ids, int R, int E, const int* __restrict__ slot_of,
+    int* __restrict__ offsets, int* __restrict__ sorted_route, int* __restrict__ route_pos,
+    int* __restrict__ n_dropped) {
+    constexpr int IB = 8;
+    __shared__ int cnt_all[PERM_MAX_E], cnt_before[PERM_MAX_E], base[PERM_MAX_E], res_s[PERM_MAX_E];
+    __shared__ int wcnt[PERM_WAVES][PERM_MAX_E];
+    __shared__ int drop, total;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int blk0 = blockIdx.x * PERM_THREADS;
+    const int res = tid < E ? (slot_of[tid] >= 0) : 0;
+    const int own = blk0 + tid < R ? ids[blk0 + tid] : -1;   // this thread's route of the block
+    if (tid < E) {
+        cnt_all[tid] = 0;
+        cnt_before[tid] = 0;
+        res_s[tid] = res;
+        for (int v = 0; v < PERM_WAVES; ++v) wcnt[v][tid] = 0;
+    }
+    if (tid == 0) drop = 0;
+    __syncthreads();
+    // 1. histograms of the kept routes: all, and those before this block
+    for (int b0 = 0; b0 < R; b0 += IB * PERM_THREADS) {
+        int raw[IB];
+#pragma unroll
+        for (int j = 0; j < IB; ++j) {
+            const int i = b0 + j * PERM_THREADS + tid;
+            raw[j] = i < R ? ids[i] : -1;
+        }
+        int nd = 0;
+#pragma unroll
+        for (int j = 0; j < IB; ++j) {
+            const int i = b0 + j * PERM_THREADS + tid, v = raw[j];
+            const int e = (v >= 0 && v < E && res_s[v]) ? v : -1;
+            if (e >= 0) {
+                atomicAdd(&cnt_all[e], 1);
+                if (i < blk0) atomicAdd(&cnt_before[e], 1);
+            }
+            nd += __popcll(__ballot(i < R && e < 0));
+        }
+        if (lane == 0 && nd) atomicAdd(&drop, nd);
+    }
+    __syncthreads();
+    // 2. offsets (wave 0, 64 experts per step); this block starts past the earlier routes
+    if (wave == 0) {
+        int carry = 0;
+        for (int e0 = 0; e0 < E; e0 += 64) {
+            const int e = e0 + lane;
+            const int c = e < E ? cnt_all[e] : 0;
+            const int incl = wave_incl_scan(c);
+            if (e < E) {
+                base[e] = carry + incl - c + cnt_before[e];
+                if (blockIdx.x == 0) offsets[e] = carry + incl - c;
+            }
+            carry += __builtin_amdgcn_readlane(incl, 63);
+        }
+        if (lane == 0) {
+            total = carry;
+            if (blockIdx.x == 0) {
+                offsets[E] = carry;
+                *n_dropped = drop;
+            }
+        }
+    }
+    __syncthreads();
+    // 3. positions of this block's routes
+    const int i = blk0 + tid;
+    const int e = (own >= 0 && own < E && res_s[own]) ? own : -1;
+    const int nbits = E > 1 ? 32 - __clz(E - 1) : 0;
+    uint64_t peers = __ballot(e >= 0);
+    for (int bit = 0; bit < nbits; ++bit) {
+        const bool mine = (e >> bit) & 1;
+        const uint64_t bb = __ballot(mine);
+        peers &= mine ? bb : ~bb;
+    }
+    const int rank = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(peers >> 32),
+                                               __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(peers), 0));
+    if (e >= 0 && rank == 0) wcnt[wave][e] = __popcll(peers);
+    __syncthreads();
+    if (e >= 0) {
+        int pos = base[e] + rank;
+        for (int v = 0; v < wave; ++v) pos += wcnt[v][e];
+        sorted_route[pos] = i;
+        route_pos[i] = pos;
+    } else if (i < R) {
+        route_pos[i] = -1;
+    }
+    // 4. positions past the kept routes, in this block's range
+    if (i < R && i >= total) sorted_route[i] = -1;
+}
+
 // Router top-k and grouping in one workgroup, for R = T k <= 1024: wave w
 // routes tokens w, w + 16, ...; the ids also go to LDS, and the grouping reads
 // them there, so the two steps cost one launch and no round trip through
@@ -256,8 +354,12 @@ hipError_t launch_route_permute(const float* logits, int T, int E, int k, int re
 
 hipError_t launch_permute(const int* ids, int R, int E, const int* slot_of, int* offsets,
                           int* sorted_route, int* route_pos, int* n_dropped, hipStream_t s) {
-    hipLaunchKernelGGL(permute_kernel, dim3(1), dim3(PERM_THREADS), 0, s, ids, R, E, slot_of,
-                       offsets, sorted_route, route_pos, n_dropped);
+    if (R > PERM_THREADS)
+        hipLaunchKernelGGL(permute_multi_kernel, dim3((R + PERM_THREADS - 1) / PERM_THREADS), dim3(PERM_THREADS), 0,
+                           s, ids, R, E, slot_of, offsets, sorted_route, route_pos, n_dropped);
+    else
+        hipLaunchKernelGGL(permute_kernel, dim3(1), dim3(PERM_THREADS), 0, s, ids, R, E, slot_of,
+                           offsets, sorted_route, route_pos, n_dropped);
     return hipGetLastError();
 }
 
