@@ -1,4 +1,6 @@
-// Stable grouping of routes by expert in one workgroup of 1024 threads.
+// Stable grouping of routes by expert: one workgroup of 1024 threads for up
+// to 1024 routes (below), one per block of 1024 routes above that
+// (permute_multi_kernel).
 //
 // Winery-Strata's RemoteExperts::begin lists, per expert group, its routes in
 // route order; rlx_runtime/expert_pool.rs count_hits is the per-expert
