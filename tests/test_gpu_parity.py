@@ -657,3 +657,47 @@ def test_residency_refresh_bit_exact(L, case):
     assert np.array_equal(got["promote_slot"][:np_], want["promote_slot"])
     assert np.array_equal(got["demote"][:nd], want["demote"])
     assert np.array_equal(got["slot_of"], want["slot_of"])
+
+
+def test_slot_cache_admit_fill_verify_then_layer(L):
+    # the slot-cache sequence (admit on the host, fill from pinned memory,
+    # verify) builds a pool for a layer whose table starts empty; the layer
+    # then matches the oracle, and a corrupted slot is caught by verify
+    from expert_ffn_amd.layer import MoeLayer
+    import oracle as ora
+    E, k, H, FF, T, S = 8, 2, 128, 64, 12, 5
+    f = L.W_INT4_G64
+    sb = L.expert_bytes(f, H, FF)
+    pool = torch.zeros(S * sb, dtype=torch.uint8, device="cuda")
+    slot_of = torch.full((E,), -1, dtype=torch.int32)
+    owner = torch.full((S,), -1, dtype=torch.int32)
+    staging = torch.empty(sb, dtype=torch.uint8, device="cuda")
+    bad = torch.empty(1, dtype=torch.int32, device="cuda")
+    W = {}
+    for e in (6, 1, 3, 0, 4):                               # admitted in this order: slots 0..4
+        j = L.slot_admit(slot_of, owner, e)
+        W[e] = synth.expert_weights(51, 0, e, H, FF)
+        canon = torch.from_numpy(ora.pack_expert_canonical(f, W[e][0], W[e][1], H, FF)).pin_memory()
+        L.fill_slot(f, canon, H, FF, pool[j * sb:(j + 1) * sb], staging=staging)
+        L.verify_slot(f, canon.cuda(), H, FF, pool[j * sb:(j + 1) * sb], bad)
+        torch.cuda.synchronize()
+        assert int(bad.item()) == 0
+    assert slot_of.tolist() == [3, 1, -1, 2, 4, -1, 0, -1]
+    with pytest.raises(L.MoeError, match="no free slot"):
+        L.slot_admit(slot_of, owner, 7)
+    logits = synth.logits(51, 0, T, E, None)
+    x_d, x_f32 = _x(51, 0, T, H, "bf16")
+    ml = MoeLayer(E, k, H, FF, f, T, out_dtype=torch.float32)
+    ml.bind(pool, sb, slot_of.cuda())
+    y = ml.run(torch.from_numpy(logits).cuda(), x_d)
+    torch.cuda.synchronize()
+    tokens = np.arange(T, dtype=np.int32)
+    ref = oracle_layer(51, 0, E, k, H, FF, f, 0, logits, x_f32, slot_of.numpy(), tokens)
+    err, _ = row_rel_err(to_np(y), ref["y"])
+    assert err <= TOL[f]
+    assert int(to_np(ml.n_dropped)[0]) == ref["n_dropped"] > 0
+    pool[2 * sb + 100] ^= 0x10                              # one code byte of expert 3's slot
+    canon3 = torch.from_numpy(ora.pack_expert_canonical(f, W[3][0], W[3][1], H, FF)).cuda()
+    L.verify_slot(f, canon3, H, FF, pool[2 * sb:3 * sb], bad)
+    torch.cuda.synchronize()
+    assert int(bad.item()) == 1
