@@ -438,10 +438,10 @@ def measure_router(lib, dev, seed, reps=200):
         logits = torch.empty((T, E), dtype=torch.float32, device=dev)
         ids = torch.empty((T, k), dtype=torch.int32, device=dev)
         w = torch.empty((T, k), dtype=torch.float32, device=dev)
-        cnt = torch.empty(lib.router_ws_bytes(T, H, E), dtype=torch.uint8, device=dev)
+        ws = torch.empty(lib.router_ws_bytes(T, H, E), dtype=torch.uint8, device=dev)
 
         def fused(i):
-            lib.router_topk(xs[i % copies], wr, k, logits, cnt, ids, w, stream=stream)
+            lib.router_topk(xs[i % copies], wr, k, logits, ws, ids, w, stream=stream)
 
         def split(i):
             torch.mm(xs[i % copies].float(), wr.t(), out=logits)

@@ -484,14 +484,14 @@ def test_router_topk(L, T, E, k, H, xdt):
         x_h = synth.x_f32(9, 0, T, H)
         x_d = torch.from_numpy(x_h).cuda()
     wr_d = torch.from_numpy(wr).cuda()
-    cnt = torch.full((L.router_ws_bytes(T, H, E),), 0x7F, dtype=torch.uint8, device="cuda")
+    ws = torch.full((L.router_ws_bytes(T, H, E),), 0x7F, dtype=torch.uint8, device="cuda")
     logits = torch.empty((T, E), dtype=torch.float32, device="cuda")
     ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
     w = torch.empty((T, k), dtype=torch.float32, device="cuda")
-    L.router_topk(x_d, wr_d, k, logits, cnt, ids, w)
+    L.router_topk(x_d, wr_d, k, logits, ws, ids, w)
     torch.cuda.synchronize()
     got_l, got_i, got_w = to_np(logits), to_np(ids), to_np(w)
-    L.router_topk(x_d, wr_d, k, logits, cnt, ids, w)
+    L.router_topk(x_d, wr_d, k, logits, ws, ids, w)
     torch.cuda.synchronize()
     assert np.array_equal(to_np(logits).view(np.uint32), got_l.view(np.uint32))
     assert np.array_equal(to_np(ids), got_i) and np.array_equal(to_np(w), got_w)
