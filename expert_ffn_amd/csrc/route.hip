@@ -12,6 +12,8 @@
 
 namespace moe {
 
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+
 template <int NPL>
 __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict__ logits, int T,
                                                          int E, int k, int renorm,
@@ -143,11 +145,13 @@ __global__ __launch_bounds__(256) void router_part_kernel(const void* __restrict
 }
 
 // Larger tiles for T > 64: workgroup (b, s, c) takes experts 64b .. 64b+63,
-// the 128-element slice s of H and tokens 64c .. 64c+63; lane l computes the
-// 4 x 4 partial logits of tokens l / 16 + 16 i and experts l % 16 + 16 j
-// (i, j < 4) over the whole slice: 8 LDS reads per 64 products, and the 16
-// lanes reading one row set hit consecutive rows (132-word stride: distinct
-// banks).  No cross-wave sum.
+// the 128-element slice s of H and tokens 64c .. 64c+63, staged in LDS as
+// fp32.  Wave w computes the 32 x 32 block of tokens 32 (w / 2) .. and experts
+// 32 (w % 2) .. with fp32 MFMA (v_mfma_f32_32x32x2f32: lane l gives row l % 32
+// of A, a token, and column l % 32 of B, an expert, at k = l / 32).  Per 8
+// elements of K, lane half h reads elements 4h .. 4h + 3 of both rows (one
+// 16-byte LDS read each) and feeds them to 4 MFMAs: MFMA j's k = 0, 1 are
+// elements j and 4 + j.  No cross-wave sum.
 constexpr int RL_TB = 64, RL_EB = 64, RL_HL = 128;
 
 template <bool XF32>
@@ -218,32 +222,23 @@ __global__ __launch_bounds__(256) void router_part_large_kernel(const void* __re
         *reinterpret_cast<f32x4*>(&ws[q >> 5][(q & 31) * 4]) = wv[i];
     }
     __syncthreads();
-    const int tp = tid >> 4, ep = tid & 15;
-    float a[4][4];
+    const int wave = tid >> 6, lane = tid & 63, h = lane >> 5;
+    const int tr = 32 * (wave >> 1) + (lane & 31), er = 32 * (wave & 1) + (lane & 31);
+    f32x16 acc = {};
+    for (int k8 = 0; k8 < hl; k8 += 8) {
+        const f32x4 xv = *reinterpret_cast<const f32x4*>(&xs[tr][k8 + 4 * h]);
+        const f32x4 wv = *reinterpret_cast<const f32x4*>(&ws[er][k8 + 4 * h]);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) a[i][j] = 0.0f;
-    for (int j = 0; j < hl; j += 4) {
-        f32x4 xv[4], wv[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            xv[i] = *reinterpret_cast<const f32x4*>(&xs[tp + 16 * i][j]);
-            wv[i] = *reinterpret_cast<const f32x4*>(&ws[ep + 16 * i][j]);
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int c = 0; c < 4; ++c)
-                a[i][c] += xv[i][0] * wv[c][0] + xv[i][1] * wv[c][1] + xv[i][2] * wv[c][2] + xv[i][3] * wv[c][3];
+        for (int j = 0; j < 4; ++j) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(xv[j], wv[j], acc, 0, 0, 0);
     }
+    // lane: expert column er, token rows 8 (v / 4) + 4 h + (v % 4) of the wave's 32
+    const int ecol = e0 + er;
+    if (ecol < E) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        if (tp + 16 * i >= nT) break;
-        float* pp = part + (static_cast<int64_t>(blockIdx.y) * T + t0 + tp + 16 * i) * E + e0 + ep;
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-            if (e0 + ep + 16 * c < E) pp[16 * c] = a[i][c];
+        for (int v = 0; v < 16; ++v) {
+            const int t = 32 * (wave >> 1) + 8 * (v >> 2) + 4 * h + (v & 3);
+            if (t < nT) part[(static_cast<int64_t>(blockIdx.y) * T + t0 + t) * E + ecol] = acc[v];
+        }
     }
 }
 
