@@ -79,12 +79,13 @@ def layer_inputs(seed, L, T, E, H, device, zipf=None):
     return logits, xs
 
 
-def _no_call():
-    return 0
-
-
 class StackRunner:
-    """Raw C calls with every argument prepared once (no per-call marshalling)."""
+    """Raw C calls with every argument prepared once (no per-call marshalling).
+
+    Each layer keeps its own routing results (ids, weights, offsets, sorted
+    routes, route positions, dropped count) and its own output y, as the
+    layers of a model would; the per-route outputs and the workspace are
+    shared, since each layer is done with them before the next starts."""
 
     def __init__(self, lib, pool, sb, slots, T, E, k, H, FF, fmt, logits, xs, stream):
         import ctypes
@@ -92,57 +93,78 @@ class StackRunner:
         from expert_ffn_amd.layer import MoeLayer
         self.L = len(logits)
         self.T = T
+        dev = pool.device
         # per-route outputs in bf16: half the bytes of the down write and the combine read
-        self.ml = MoeLayer(E, k, H, FF, fmt, T, device=pool.device, out_dtype=torch.bfloat16)
+        self.ml = MoeLayer(E, k, H, FF, fmt, T, device=dev, out_dtype=torch.bfloat16)
         ml = self.ml
-        self.slot_d = [torch.from_numpy(slots[l].copy()).to(pool.device) for l in range(self.L)]
+        self.slot_d = [torch.from_numpy(slots[l].copy()).to(dev) for l in range(self.L)]
+        i32 = torch.int32
+        self.rt = [dict(ids=torch.empty((T, k), dtype=i32, device=dev),
+                        w=torch.empty((T, k), dtype=torch.float32, device=dev),
+                        offsets=torch.empty(E + 1, dtype=i32, device=dev),
+                        sorted_route=torch.empty(T * k, dtype=i32, device=dev),
+                        route_pos=torch.empty(T * k, dtype=i32, device=dev),
+                        n_dropped=torch.empty(1, dtype=i32, device=dev),
+                        y=torch.empty((T, H), dtype=torch.bfloat16, device=dev))
+                   for _ in range(self.L)]
         c = lib.lib()
         P = lambda t: ctypes.c_void_p(t.data_ptr())
         s = ctypes.c_void_p(stream.cuda_stream)
-        R = T * k
         ws = ml.ws.numel()
         self.calls = []
         for l in range(self.L):
-            slot = P(self.slot_d[l])
+            slot, r = P(self.slot_d[l]), self.rt[l]
             # router top-k and grouping in one call (one launch for T k <= 1024)
-            route = (c.moe_route_permute, (P(logits[l]), T, E, k, 1, slot, P(ml.topk_ids), P(ml.topk_w),
-                                           P(ml.offsets), P(ml.sorted_route), P(ml.route_pos),
-                                           P(ml.n_dropped), s))
-            perm = (_no_call, ())
-            ffn_args = (P(pool), sb, slot, E, H, FF, fmt, 0, P(xs[l]), 1, T, k, P(ml.offsets),
-                        P(ml.sorted_route), P(ml.out_routes), 1, P(ml.ws), ws, s)
+            route = (c.moe_route_permute, (P(logits[l]), T, E, k, 1, slot, P(r["ids"]), P(r["w"]),
+                                           P(r["offsets"]), P(r["sorted_route"]), P(r["route_pos"]),
+                                           P(r["n_dropped"]), s))
+            ffn_args = (P(pool), sb, slot, E, H, FF, fmt, 0, P(xs[l]), 1, T, k, P(r["offsets"]),
+                        P(r["sorted_route"]), P(ml.out_routes), 1, P(ml.ws), ws, s)
             gu = (c.moe_ffn_gate_up, ffn_args)
             dn = (c.moe_ffn_down, ffn_args)
-            comb = (c.moe_combine, (P(ml.out_routes), 1, P(ml.topk_w), P(ml.route_pos), T, k, H,
-                                    P(ml.y), 1, s))
-            self.calls.append((route, perm, gu, dn, comb))
-        del R
+            comb = (c.moe_combine, (P(ml.out_routes), 1, P(r["w"]), P(r["route_pos"]), T, k, H,
+                                    P(r["y"]), 1, s))
+            self.calls.append((route, gu, dn, comb))
+
+    @staticmethod
+    def _call(fa):
+        if fa[0](*fa[1]):
+            raise RuntimeError("launch failed")
 
     def step(self, events=None):
-        for l, (route, perm, gu, dn, comb) in enumerate(self.calls):
-            for f, a in (route, perm):
-                if f(*a):
-                    raise RuntimeError("launch failed")
+        for l, (route, gu, dn, comb) in enumerate(self.calls):
+            self._call(route)
             if events is not None:
                 events[l][0].record()
-            if gu[0](*gu[1]):
-                raise RuntimeError("launch failed")
+            self._call(gu)
             if events is not None:
                 events[l][1].record()
-            for f, a in (dn, comb):
-                if f(*a):
-                    raise RuntimeError("launch failed")
+            self._call(dn)
+            self._call(comb)
+
+    def gate_up_only(self):
+        """The gate/up half of every layer, back to back, on the routing the
+        last step left (for timing that kernel alone)."""
+        for _, gu, _, _ in self.calls:
+            self._call(gu)
+
+    def capture(self, stream, body=None):
+        """A HIP graph of one step (or of body()), captured on stream."""
+        import torch
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            (body or self.step)()
+        return graph
 
 
 def realised_routing(lib, runner, logits):
     """Distinct experts and routes per layer (read once, outside any timing)."""
     import torch
     out = []
-    for l, (route, perm, _, _, _) in enumerate(runner.calls):
-        route[0](*route[1])
-        perm[0](*perm[1])
+    for l, (route, _, _, _) in enumerate(runner.calls):
+        runner._call(route)
         torch.cuda.synchronize()
-        off = runner.ml.offsets.cpu().numpy()
+        off = runner.rt[l]["offsets"].cpu().numpy()
         counts = np.diff(off)
         out.append((int((counts > 0).sum()), int(off[-1])))
     return out

@@ -51,7 +51,6 @@ def lib():
         L.moe_combine.argtypes = [P, i32, P, P, i32, i32, i32, P, i32, P]
         L.moe_quantize.argtypes = [i32, P, i32, i32, P, P, P]
         L.moe_pack_expert.argtypes = [i32, P, P, i32, i32, P, P]
-        L.moe_set_ffn_path.argtypes = [i32]
         L.moe_router_ws_bytes.argtypes = [i32, i32, i32]
         L.moe_router_ws_bytes.restype = sz
         L.moe_router_topk.argtypes = [P, i32, i32, i32, P, i32, i32, i32, P, P, sz, P, P, P]
@@ -67,7 +66,7 @@ def lib():
         L.moe_slot_admit.argtypes = [P, i32, P, i32, i32]
         for name in ("moe_blob_layout", "moe_route_topk", "moe_permute", "moe_route_permute", "moe_expert_ffn",
                      "moe_ffn_gate_up", "moe_ffn_down", "moe_combine", "moe_quantize",
-                     "moe_pack_expert", "moe_set_ffn_path", "moe_router_topk", "moe_residency_refresh", "moe_min_weight", "moe_fill_slot", "moe_fill_slots", "moe_verify_slot",
+                     "moe_pack_expert", "moe_router_topk", "moe_residency_refresh", "moe_min_weight", "moe_fill_slot", "moe_fill_slots", "moe_verify_slot",
                      "moe_slot_admit"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -111,10 +110,6 @@ def blob_layout(fmt: int, H: int, FF: int):
 
 def workspace_bytes(T: int, k: int, E: int, H: int, FF: int, fmt: int) -> int:
     return int(lib().moe_workspace_bytes(T, k, E, H, FF, fmt))
-
-
-def set_ffn_path(path: int):
-    _check(lib().moe_set_ffn_path(path))
 
 
 # ------------------------------------------------------------- the steps --

@@ -13,7 +13,6 @@
 namespace {
 
 thread_local std::string g_last_error;
-int g_ffn_path = 0;
 
 moe_status fail(moe_status st, const char* fn, const char* fmt, ...) {
     char buf[512];
@@ -108,12 +107,6 @@ size_t moe_workspace_bytes(int32_t T, int32_t k, int32_t E, int32_t H, int32_t F
     (void)wfmt;
     if (T < 0 || k < 1 || H < 1 || FF < 1) return 0;
     return moe::ffn_workspace(T, k, H, FF).bytes;
-}
-
-moe_status moe_set_ffn_path(int32_t path) {
-    if (path < 0 || path > 2) return fail(MOE_E_ARG, "moe_set_ffn_path", "path=%d not in {0,1,2}", path);
-    g_ffn_path = path;
-    return MOE_OK;
 }
 
 moe_status moe_route_topk(const float* logits, int32_t T, int32_t E, int32_t k, int32_t renorm,
@@ -276,12 +269,14 @@ static moe_status ffn_entry(const char* fn, int phases, const void* pool, uint64
     P.xq_out = reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(ws) + wl.xq_off);
     P.xsum = nullptr;
     P.xsum_out = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + wl.xsum_off);
+    P.xqg_out = reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(ws) + wl.xqg_off);
+    P.xsumg_out = reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(ws) + wl.xsumg_off);
     P.h = reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(ws) + wl.h_off);
     P.hsum = reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(ws) + wl.hsum_off);
     P.out = out_routes;
     P.out_dt = out_dtype;
     P.o13 = off[0]; P.os13 = off[1]; P.o2 = off[2]; P.os2 = off[3];
-    return hip_status(fn, moe::launch_ffn(P, phases, g_ffn_path, static_cast<hipStream_t>(stream)));
+    return hip_status(fn, moe::launch_ffn(P, phases, static_cast<hipStream_t>(stream)));
 }
 
 #define FFN_ARGS pool, slot_bytes, slot_of, E, H, FF, wfmt, act, x, x_dtype, T, k, expert_offsets, \

@@ -27,6 +27,8 @@
 // K range, no LDS for operands; the first half splits K over the workgroup's
 // waves and reduces the partial sums in LDS.  Expert groups with no routes
 // leave their workgroups idle at once.
+#include <climits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -594,8 +596,8 @@ __global__ __launch_bounds__(128 * KH) void gate_up_int4_kernel(FfnParams P) {
     extern __shared__ float smem[];
     const int ntile = P.FF >> 4;
     const int e = blockIdx.x / ntile, u = blockIdx.x - e * ntile;
-    const int beg = P.offsets[e] + 16 * static_cast<int>(blockIdx.y), end = P.offsets[e + 1];
-    if (beg >= end) return;
+    const int b0 = P.offsets[e], end = P.offsets[e + 1], beg = b0 + 16 * static_cast<int>(blockIdx.y);
+    if (beg >= end || end - b0 > P.gmin) return;   // no routes here, or the group is the GEMM's
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, r = lane & 15, q = lane >> 4;
     const int t = wave / KH, hp = wave - t * KH;
     const uint8_t* blob = P.pool + static_cast<uint64_t>(P.slot_of[e]) * P.slot_bytes;
@@ -649,8 +651,8 @@ __global__ __launch_bounds__(256) void down_int4_kernel(FfnParams P) {
     extern __shared__ float smem[];
     const int nblk = P.H >> 6;
     const int e = blockIdx.x / nblk, blk = blockIdx.x - e * nblk;
-    const int beg = P.offsets[e] + 16 * static_cast<int>(blockIdx.y), end = P.offsets[e + 1];
-    if (beg >= end) return;
+    const int b0 = P.offsets[e], end = P.offsets[e + 1], beg = b0 + 16 * static_cast<int>(blockIdx.y);
+    if (beg >= end || end - b0 > P.gmin) return;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, r = lane & 15, q = lane >> 4;
     const uint8_t* blob = P.pool + static_cast<uint64_t>(P.slot_of[e]) * P.slot_bytes;
     const int m0 = blk * 64 + wave * 16;
@@ -721,7 +723,7 @@ __global__ __launch_bounds__(256) void gate_up_int4_dec_kernel(FfnParams P) {
     const int nwt = (P.FF >> 4) / GUD_TPW;   // workgroups per expert
     const int e = blockIdx.x / nwt, u0 = (blockIdx.x - e * nwt) * GUD_TPW;
     const int beg = P.offsets[e], end = P.offsets[e + 1];
-    if (beg >= end) return;
+    if (beg >= end || end - beg > P.gmin) return;   // no routes, or the group is the GEMM's
     const int H = P.H, G = H / 64, GS = (G + 39) & ~7;
     const GudLds L = gud_lds(H);
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r = lane & 15, q = lane >> 4;
@@ -941,7 +943,7 @@ __global__ __launch_bounds__(256) void down_int4_dec_kernel(FfnParams P) {
     const int nblk = P.H / (64 * TPW);
     const int e = blockIdx.x / nblk, blk = blockIdx.x - e * nblk;
     const int beg = P.offsets[e], end = P.offsets[e + 1];
-    if (beg >= end) return;
+    if (beg >= end || end - beg > P.gmin) return;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r = lane & 15, q = lane >> 4;
     const uint8_t* blob = P.pool + static_cast<uint64_t>(P.slot_of[e]) * P.slot_bytes;   // scalar, first
     const int m0 = (blk * 4 + wave) * 16 * TPW;   // first row of the wave; tile tt is rows m0 + 16 tt
@@ -1157,7 +1159,11 @@ FfnWorkspace ffn_workspace(int T, int k, int H, int FF) {
     // group sums: bf16 hi + lo per (row, 64-group), rows padded to 16 groups
     const size_t gx = static_cast<size_t>((H / 64 + 15) & ~15), gh = static_cast<size_t>((FF / 64 + 15) & ~15);
     w.xsum_off = up(static_cast<size_t>(T) * H * 2);
-    w.h_off = w.xsum_off + up(static_cast<size_t>(T) * gx * 4);
+    w.xqg_off = w.xsum_off + up(static_cast<size_t>(T) * gx * 4);
+    // the grouped GEMM's own x copy and sums, only when that family can run
+    const size_t tg = T > GEMM_T_MIN ? static_cast<size_t>(T) : 0;
+    w.xsumg_off = w.xqg_off + up(tg * H * 2);
+    w.h_off = w.xsumg_off + up(tg * gx * 4);
     w.hsum_off = w.h_off + up(static_cast<size_t>(T) * k * FF * 2);
     w.bytes = w.hsum_off + up(static_cast<size_t>(T) * k * gh * 4);
     return w;
@@ -1222,12 +1228,16 @@ static void launch_phases(const FfnParams& P, int phases, hipStream_t s) {
     }
 }
 
-hipError_t launch_ffn(const FfnParams& P0, int phases, int path, hipStream_t s) {
+hipError_t launch_ffn(const FfnParams& P0, int phases, hipStream_t s) {
     FfnParams P = P0;
-    // int4, large token groups: LDS-staged grouped GEMM (both halves, so that
-    // split calls with the same T agree on the layout of h)
-    if (int4_gemm_eligible(P) && (path == 2 || (path == 0 && P.T >= 256))) return launch_int4_gemm(P, phases, s);
-    if ((phases & 1) && path != 2 && P.fmt == W_INT4 && P.H == 2816 && P.FF % (16 * GUD_TPW) == 0) {
+    P.gmin = INT_MAX;
+    if (P.fmt == W_INT4 && P.T > GEMM_T_MIN && int4_gemm_eligible(P)) {
+        // per expert group: more than GEMM_GROUP_MIN routes -> grouped GEMM
+        P.gmin = GEMM_GROUP_MIN;
+        const hipError_t err = launch_int4_gemm(P, phases, s);
+        if (err != hipSuccess) return err;
+    }
+    if ((phases & 1) && P.fmt == W_INT4 && P.H == 2816 && P.FF % (16 * GUD_TPW) == 0) {
         const GudLds L = gud_lds(P.H);
         const dim3 grid(P.E * (P.FF / 16 / GUD_TPW));
         if (P.x_dt == F32) {

@@ -29,6 +29,8 @@
 // groups ahead into a ring of three stages, whole cache lines per copy, XOR
 // swizzled in LDS; each wave keeps the weights of the next 2*DC groups in flight
 // in registers, one 1 KB load per group and 32 rows from the blob's tiled codes.
+#include <atomic>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -176,7 +178,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void ffn_int4_gemm_kernel(FfnParam
         for (int e0 = 0; e0 < E; e0 += 64) {
             const int e = e0 + lane;
             const int me = e < E ? P.offsets[e + 1] - P.offsets[e] : 0;
-            const int cnt = me == 0 ? 0 : (me <= GEMM_WIDE_MAX ? (me + 63) / 64 * NTW : (me + GM_ROWS - 1) / GM_ROWS * NT);
+            // groups of at most gmin routes are the streaming kernels'
+            const int cnt = me <= P.gmin ? 0 : (me <= GEMM_WIDE_MAX ? (me + 63) / 64 * NTW : (me + GM_ROWS - 1) / GM_ROWS * NT);
             int incl = cnt;
 #pragma unroll
             for (int d = 1; d < 64; d <<= 1) {
@@ -559,39 +562,55 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void ffn_int4_gemm_kernel(FfnParam
     }
 }
 
-// true if the int4 GEMM path takes this call
-bool int4_gemm_eligible(const FfnParams& P) {
-    // the tiles handle any H, FF that are multiples of 64 (ragged last N tile,
-    // odd group counts); E bounds the prefix table in LDS
-    return P.fmt == W_INT4 && P.H % 64 == 0 && P.FF % 64 == 0 && P.E <= 4096;
-}
-
 #ifndef GEMM_NW
 #define GEMM_NW 4
 #endif
+
+// LDS the device allows a workgroup, per device (queried once)
+static int max_lds_bytes() {
+    static std::atomic<int> cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    int v = cached[dev].load(std::memory_order_relaxed);
+    if (v == 0) {
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess) return 0;
+        cached[dev].store(v, std::memory_order_relaxed);
+    }
+    return v;
+}
+
+// true if the int4 GEMM can take this call's large groups: the tiles handle
+// any H, FF that are multiples of 64 (ragged last N tile, odd group counts);
+// E bounds the prefix table, and both halves' LDS must fit (checked here, so
+// that nothing is launched when it does not)
+bool int4_gemm_eligible(const FfnParams& P) {
+    if (P.fmt != W_INT4 || P.H % 64 || P.FF % 64 || P.E > 4096) return false;
+    const size_t lim = static_cast<size_t>(max_lds_bytes());
+    return gemm_lds_bytes(P.E, P.H / 64, GEMM_NW) <= lim && gemm_lds_bytes(P.E, P.FF / 64, GEMM_NW) <= lim;
+}
+
 hipError_t launch_int4_gemm(const FfnParams& P0, int phases, hipStream_t s) {
     FfnParams P = P0;
-    int dev = 0, cus = 0, maxlds = 0;
+    int dev = 0, cus = 0;
     hipError_t err = hipGetDevice(&dev);
     if (err != hipSuccess) return err;
     if ((err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return err;
-    if ((err = hipDeviceGetAttribute(&maxlds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev)) != hipSuccess) return err;
+    const int maxlds = max_lds_bytes();
     constexpr int DC0 = 2, DC1 = 3, NW = GEMM_NW;   // weight prefetch depth (2 DC groups) per half
     // persistent: 8 waves per CU, as one workgroup of 8 or two of 4 (which then
     // run out of step with each other)
     const dim3 grid(static_cast<uint32_t>(cus * (8 / NW))), block(64 * NW);
     if (phases & 1) {
         const int64_t nblk = static_cast<int64_t>(P.T) * P.H / 8;
-        P.xq = P.xq_out;
-        P.xsum = P.xsum_out;
+        P.xq = P.xqg_out;
+        P.xsum = reinterpret_cast<float*>(P.xsumg_out);
         if (P.x_dt == F32)
             hipLaunchKernelGGL((prep_x_m32_kernel<F32>), dim3(static_cast<uint32_t>((nblk + 255) / 256)), dim3(256), 0, s,
-                               P.x, P.T, P.H, P.xq_out, reinterpret_cast<uint16_t*>(P.xsum_out));
+                               P.x, P.T, P.H, P.xqg_out, P.xsumg_out);
         else
             hipLaunchKernelGGL((prep_x_m32_kernel<BF16>), dim3(static_cast<uint32_t>((nblk + 255) / 256)), dim3(256), 0, s,
-                               P.x, P.T, P.H, P.xq_out, reinterpret_cast<uint16_t*>(P.xsum_out));
+                               P.x, P.T, P.H, P.xqg_out, P.xsumg_out);
         const size_t lds = gemm_lds_bytes(P.E, P.H / 64, NW);
-        if (static_cast<int>(lds) > maxlds) return hipErrorInvalidConfiguration;
         static bool attr = false;
         if (!attr)
             attr = hipFuncSetAttribute(reinterpret_cast<const void*>(ffn_int4_gemm_kernel<0, DC0, NW>),
@@ -600,7 +619,6 @@ hipError_t launch_int4_gemm(const FfnParams& P0, int phases, hipStream_t s) {
     }
     if (phases & 2) {
         const size_t lds = gemm_lds_bytes(P.E, P.FF / 64, NW);
-        if (static_cast<int>(lds) > maxlds) return hipErrorInvalidConfiguration;
         static bool attr = false;
         if (!attr)
             attr = hipFuncSetAttribute(reinterpret_cast<const void*>(ffn_int4_gemm_kernel<1, DC1, NW>),

@@ -58,25 +58,36 @@ struct FfnParams {
     uint16_t* xq_out;         // where the preparation kernel writes xq (workspace)
     float* xsum;              // group sums of xq per (token, 64-group) as bf16 hi [T, H/64] then lo; int4 fast gate/up
     float* xsum_out;          // where the preparation kernel may write them (workspace)
+    uint16_t* xqg_out;        // the grouped GEMM's copy of x (M32 operand order) and its group
+    uint16_t* xsumg_out;      //   sums (workspace; both kernel families can run in one call)
     uint16_t* h;              // [T*k, FF] bf16 in the w2 operand order (workspace)
     uint16_t* hsum;           // group sums of h per (route, 64-group of FF), bf16 hi then lo (int4 GEMM path)
     void* out;                // [T*k, H] fp32 or bf16 (out_dt)
     int out_dt;
     uint64_t o13, os13, o2, os2;  // blob sub-block offsets
+    int gmin;                 // int4: groups of more than gmin routes belong to the grouped GEMM,
+                              // the others to the streaming kernels (INT_MAX: no GEMM)
 };
 
 // Workspace layout of the expert FFN.
 struct FfnWorkspace {
-    size_t xq_off, xsum_off, h_off, hsum_off, bytes;
+    size_t xq_off, xsum_off, xqg_off, xsumg_off, h_off, hsum_off, bytes;
 };
 FfnWorkspace ffn_workspace(int T, int k, int H, int FF);
 
-// int4 grouped-GEMM path (large token groups)
+// Kernel family per expert group (int4): a group of m_e routes takes the
+// grouped GEMM when m_e > GEMM_GROUP_MIN, else the streaming kernels (which
+// take the routes a few at a time against weights held in registers).  The
+// GEMM family is launched only when T > GEMM_T_MIN (m_e <= T, and at decode
+// sizes its launches would find no work).
+constexpr int GEMM_GROUP_MIN = 16;
+constexpr int GEMM_T_MIN = 64;
+
+// int4 grouped-GEMM path (large token groups): shape and LDS fit, checked
+// before anything is launched
 bool int4_gemm_eligible(const FfnParams& p);
 hipError_t launch_int4_gemm(const FfnParams& p, int phases, hipStream_t s);
 
-// 0 = choose by token count, 1 = streaming kernels, 2 = LDS-tiled kernels
-hipError_t launch_ffn(const FfnParams& p, int phases /*1 gate_up, 2 down, 3 both*/, int path,
-                      hipStream_t s);
+hipError_t launch_ffn(const FfnParams& p, int phases /*1 gate_up, 2 down, 3 both*/, hipStream_t s);
 
 }  // namespace moe

@@ -381,14 +381,6 @@ moe_status moe_verify_slot(int32_t wfmt, const void* src, int32_t H, int32_t FF,
  */
 int32_t moe_slot_admit(int32_t* slot_of, int32_t E, int32_t* owner, int32_t S, int32_t expert);
 
-/*
- * Kernel family moe_expert_ffn uses: 0 = by token count (default), 1 = the
- * streaming kernels for small per-expert groups, 2 = the LDS-tiled kernels for
- * large groups.  Process-wide setting for tests and measurement; not
- * synchronised with concurrent calls.  Returns MOE_E_ARG for other values.
- */
-moe_status moe_set_ffn_path(int32_t path);
-
 #ifdef __cplusplus
 }
 #endif

@@ -10,7 +10,9 @@ tensor id, layer, expert])):
   router logits   fp32 N(0, 1), optionally plus ln p_e for a Zipf(s) expert
                   popularity p_e = rank_e^-s / sum, ranks a seeded permutation
                   of 1..E
-  activations x   fp32 N(0, 1); bf16 by rounding
+  activations x   fp32 N(0, 1); bf16 by rounding.  A heavy-tailed variant
+                  for edge cases: Student-t with 2 degrees of freedom, and in
+                  each row 4 elements at random positions multiplied by 100
   expert weights  fp32 N(0, 0.02) -> bf16, w13 [2FF, H] and w2 [H, FF]
   slot table      a seeded permutation of the L*E slots of a pool, [L, E]
   router weight   fp32 N(0, 1/H) [E, H], so that x . Wr has unit spread like
@@ -24,7 +26,7 @@ from __future__ import annotations
 
 import numpy as np
 
-T_LOGITS, T_X, T_W13, T_W2, T_SLOTS, T_ZIPF, T_ROUTER = 1, 2, 3, 4, 5, 6, 7
+T_LOGITS, T_X, T_W13, T_W2, T_SLOTS, T_ZIPF, T_ROUTER, T_XHEAVY = 1, 2, 3, 4, 5, 6, 7, 8
 WEIGHT_STD = 0.02
 
 GEMMA = dict(E=128, k=8, H=2816, FF=704)
@@ -62,6 +64,21 @@ def x_f32(seed: int, layer: int, T: int, H: int) -> np.ndarray:
 
 def x_bf16(seed: int, layer: int, T: int, H: int) -> np.ndarray:
     return to_bf16_bits(x_f32(seed, layer, T, H))
+
+
+def x_heavy_f32(seed: int, layer: int, T: int, H: int, outliers: int = 4, gain: float = 100.0) -> np.ndarray:
+    """Heavy-tailed activations: Student-t(2) draws, with `outliers` elements
+    per row (at seeded positions) multiplied by `gain`."""
+    r = rng(seed, T_XHEAVY, layer)
+    x = r.standard_t(2.0, size=(T, H)).astype(np.float32)
+    for t in range(T):
+        pos = r.choice(H, size=min(outliers, H), replace=False)
+        x[t, pos] *= np.float32(gain)
+    return x
+
+
+def x_heavy_bf16(seed: int, layer: int, T: int, H: int) -> np.ndarray:
+    return to_bf16_bits(x_heavy_f32(seed, layer, T, H))
 
 
 def router_weight(seed: int, layer: int, E: int, H: int) -> np.ndarray:

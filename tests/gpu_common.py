@@ -42,22 +42,27 @@ def build_pool(seed, layer, E, H, FF, fmt, slot_of, n_slots=None, device="cuda")
     return pool, sb
 
 
-def oracle_layer(seed, layer, E, k, H, FF, fmt, act, logits, x_f32, slot_of, tokens, routes_in=None):
+def oracle_layer(seed, layer, E, k, H, FF, fmt, act, logits, x_f32, slot_of, tokens, routes_in=None,
+                 weights=None):
     """Oracle route + permute for all tokens, FFN and combine for the sampled
     tokens, with blobs the oracle packs itself (only the experts those tokens
-    need).  routes_in = (ids, w) replaces the oracle's own top-k."""
+    need).  routes_in = (ids, w) replaces the oracle's own top-k; weights (a
+    function e -> (w13, w2) bf16 bit patterns) replaces the host generator."""
     T = logits.shape[0]
     ids, w = ora.route_topk(logits, k) if routes_in is None else routes_in
     offsets, sorted_route, route_pos, nd = ora.permute(ids, E, slot_of)
     tokens = np.asarray(tokens, dtype=np.int32)
     need = sorted({int(e) for e in ids[tokens].reshape(-1) if slot_of[e] >= 0})
     sb = ora.expert_bytes(fmt, H, FF)
-    W = host_weights(seed, layer, E, H, FF)
+    if weights is None:
+        W = host_weights(seed, layer, E, H, FF)
+        weights = lambda e: W[e]
     cpool = np.zeros(max(len(need), 1) * sb, np.uint8)
     cslot = np.full(E, -1, np.int32)
     blobs = {}
     for j, e in enumerate(need):
-        blobs[e] = ora.pack_expert(fmt, W[e][0], W[e][1], H, FF)
+        w13, w2 = weights(e)
+        blobs[e] = ora.pack_expert(fmt, w13, w2, H, FF)
         cpool[j * sb:(j + 1) * sb] = blobs[e]
         cslot[e] = j
     routes = (tokens[:, None] * k + np.arange(k, dtype=np.int32)[None, :]).reshape(-1)

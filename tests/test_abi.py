@@ -84,8 +84,6 @@ def test_host_validation_errors(L):
     assert rc == 2
     rc, msg = _call(L, "moe_combine", fake, 0, fake, fake, 4, 2, 60, fake, 0, None)
     assert rc == 2 and "H=60" in msg
-    rc, msg = _call(L, "moe_set_ffn_path", 3)
-    assert rc == 1
     rc, msg = _call(L, "moe_fill_slot", 2, fake, 1, 2816, 704, None, fake, None)
     assert rc == 1 and "staging" in msg
     rc, msg = _call(L, "moe_fill_slot", 2, fake, 0, 2816, 704, None, fake, None)

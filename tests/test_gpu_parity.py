@@ -26,17 +26,18 @@ def L():
 
 
 def _x(seed, layer, T, H, kind):
+    """Device x and its fp32 values: "f32" (N(0,1) kept fp32), "bf16" (N(0,1)
+    rounded), "heavy" (Student-t(2) with 100x outliers, rounded)."""
+    import oracle as ora
     if kind == "f32":
         xh = synth.x_f32(seed, layer, T, H)
-        import oracle as ora
         return torch.from_numpy(xh).cuda(), xh
-    bits = synth.x_bf16(seed, layer, T, H)
-    import oracle as ora
+    bits = synth.x_heavy_bf16(seed, layer, T, H) if kind == "heavy" else synth.x_bf16(seed, layer, T, H)
     return torch.from_numpy(bits.view(np.int16)).cuda().view(torch.bfloat16), ora.bf16_to_f32(bits)
 
 
 def run_case(L, name, *, E, k, H, FF, fmt, T, act=0, x_kind="bf16", y_dtype=torch.bfloat16,
-             zipf=None, slot_of=None, n_sample=16, seed=0, layer=0, out_dtype=torch.float32, path=0):
+             zipf=None, slot_of=None, n_sample=None, seed=0, layer=0, out_dtype=torch.float32, gemm=None):
     from expert_ffn_amd.layer import MoeLayer
     log(f"[case] {name}: E={E} k={k} H={H} FF={FF} fmt={fmt} T={T} act={act} zipf={zipf}")
     f = FMT[fmt]
@@ -47,16 +48,12 @@ def run_case(L, name, *, E, k, H, FF, fmt, T, act=0, x_kind="bf16", y_dtype=torc
     x_d, x_f32 = _x(seed, layer, T, H, x_kind)
     pool, sb = build_pool(seed, layer, E, H, FF, f, slot_of)
     slot_d = torch.from_numpy(slot_of).cuda()
-    L.set_ffn_path(path)
-    try:
-        ml = MoeLayer(E, k, H, FF, f, max(T, 1), act=act, y_dtype=y_dtype, out_dtype=out_dtype)
-        ml.bind(pool, sb, slot_d)
-        y = ml.run(torch.from_numpy(logits).cuda(), x_d)
-        torch.cuda.synchronize()
-    finally:
-        L.set_ffn_path(0)
+    ml = MoeLayer(E, k, H, FF, f, max(T, 1), act=act, y_dtype=y_dtype, out_dtype=out_dtype)
+    ml.bind(pool, sb, slot_d)
+    y = ml.run(torch.from_numpy(logits).cuda(), x_d)
+    torch.cuda.synchronize()
     v = ml.views(T)
-    tokens = sample_tokens(T, n_sample)
+    tokens = sample_tokens(T, T if n_sample is None else n_sample)
     ref = oracle_layer(seed, layer, E, k, H, FF, f, act, logits, x_f32, slot_of, tokens)
     assert np.array_equal(to_np(v["topk_ids"]), ref["ids"]), "topk ids differ"
     assert np.max(np.abs(to_np(v["topk_w"]) - ref["w"])) <= 1e-5, "router weights differ"
@@ -64,6 +61,15 @@ def run_case(L, name, *, E, k, H, FF, fmt, T, act=0, x_kind="bf16", y_dtype=torc
     assert np.array_equal(to_np(v["sorted_route"]), ref["sorted_route"]), "sorted routes differ"
     assert np.array_equal(to_np(v["route_pos"]), ref["route_pos"]), "route positions differ"
     assert int(to_np(v["n_dropped"])[0]) == ref["n_dropped"]
+    # int4 kernel family per expert group: more than GEMM_GROUP_MIN routes (when
+    # T > GEMM_T_MIN) -> grouped GEMM, else streaming; gemm = (some GEMM groups,
+    # some streaming groups) the case is meant to cover
+    m = np.diff(ref["offsets"])
+    n_gemm = int(((m > GEMM_GROUP_MIN) & (T > GEMM_T_MIN)).sum()) if f == 2 else 0
+    n_stream = int((m > 0).sum()) - n_gemm
+    log(f"    groups: {n_gemm} grouped-GEMM, {n_stream} streaming, largest {int(m.max()) if m.size else 0}")
+    if gemm is not None:
+        assert (n_gemm > 0, n_stream > 0) == gemm, f"{name}: families used {(n_gemm > 0, n_stream > 0)}"
     for e, blob in ref["blobs"].items():
         got = to_np(pool[slot_of[e] * sb:slot_of[e] * sb + blob.size])
         assert np.array_equal(got, blob), f"packed bytes of expert {e} differ"
@@ -112,12 +118,12 @@ def test_all_dropped(L):
 
 # -------------------------------------------------- Gemma-shaped layers ----
 G = synth.GEMMA
+GEMM_GROUP_MIN, GEMM_T_MIN = 16, 64     # the library's dispatch thresholds (csrc/kernels.h)
 
 
 @pytest.mark.parametrize("T", [1, 4, 16, 64])
 def test_gemma_bf16_decode(L, T):
-    run_case(L, f"gemma-bf16-T{T}", E=G["E"], k=G["k"], H=G["H"], FF=G["FF"], fmt="bf16", T=T,
-             n_sample=16)
+    run_case(L, f"gemma-bf16-T{T}", E=G["E"], k=G["k"], H=G["H"], FF=G["FF"], fmt="bf16", T=T)
 
 
 def test_gemma_bf16_silu(L):
@@ -150,30 +156,57 @@ def test_gemma_int4_decode_f32_x(L):
 @pytest.mark.parametrize("zipf", [None, 1.1])
 def test_gemma_int4_prefill(L, zipf):
     run_case(L, f"gemma-int4-T1024-zipf{zipf}", E=G["E"], k=G["k"], H=G["H"], FF=G["FF"], fmt="int4",
-             T=1024, zipf=zipf, n_sample=12)
+             T=1024, zipf=zipf)
 
 
-# The int4 grouped-GEMM path (prefill-sized groups), forced on small shapes:
-# partial and multiple 128-route tiles, odd group counts, ragged N tiles.
+# The int4 grouped-GEMM path (groups of more than 16 routes) on small shapes:
+# partial and multiple 128-route tiles, wide 64-route tiles, odd group counts,
+# ragged N tiles, and calls where both kernel families take groups.
 GEMM_CASES = [
     dict(name="gemm-E8-H256-FF128-T100", E=8, k=2, H=256, FF=128, T=100),
     dict(name="gemm-E2-H384-FF384-T300-zipf", E=2, k=1, H=384, FF=384, T=300, zipf=1.1),
     dict(name="gemm-E4-H640-FF640-T150-silu-f32x", E=4, k=2, H=640, FF=640, T=150, act=1, x_kind="f32",
          out_dtype=torch.bfloat16),
     dict(name="gemm-E4-H192-FF192-T90", E=4, k=2, H=192, FF=192, T=90),
-    dict(name="gemm-E16-H128-FF256-T40-dropped", E=16, k=4, H=128, FF=256, T=40,
+    dict(name="gemm-E16-H128-FF256-T100-dropped", E=16, k=4, H=128, FF=256, T=100,
          slot_of=np.array([0, -1, 2, 3, -1, 5, 6, 7, 8, 9, -1, 11, 12, 13, 14, 15], np.int32)),
+    dict(name="mixed-E32-H256-FF192-T80-zipf", E=32, k=2, H=256, FF=192, T=80, zipf=1.1, gemm=(True, True)),
+    dict(name="mixed-E24-H384-FF128-T70-zipf-f32x", E=24, k=3, H=384, FF=128, T=70, zipf=1.1, x_kind="f32",
+         gemm=(True, True)),
 ]
 
 
 @pytest.mark.parametrize("case", GEMM_CASES, ids=[c["name"] for c in GEMM_CASES])
 def test_int4_gemm_path(L, case):
     c = dict(case)
-    run_case(L, c.pop("name"), fmt="int4", path=2, seed=3, **c)
+    c.setdefault("gemm", (True, False) if c["name"].startswith("gemm") else None)
+    if c["name"].startswith("gemm-E16"):
+        c["gemm"] = None      # a few small groups may remain with the streaming kernels
+    run_case(L, c.pop("name"), fmt="int4", seed=3, **c)
 
 
 def test_gemma_int4_gemm_T256(L):
-    run_case(L, "gemma-int4-T256", E=G["E"], k=G["k"], H=G["H"], FF=G["FF"], fmt="int4", T=256, n_sample=12)
+    run_case(L, "gemma-int4-T256", E=G["E"], k=G["k"], H=G["H"], FF=G["FF"], fmt="int4", T=256)
+
+
+# Mid-sized batches, where one expert's group can be large while the others
+# stay small (the kernel family is chosen per expert group): every format at
+# T = 128 with Zipf(1.1) routing and T = 256 with uniform routing.
+@pytest.mark.parametrize("fmt", ["bf16", "int8", "int4"])
+@pytest.mark.parametrize("T,zipf", [(128, 1.1), (256, None)])
+def test_gemma_mid_batches(L, fmt, T, zipf):
+    run_case(L, f"gemma-{fmt}-T{T}-zipf{zipf}", E=G["E"], k=G["k"], H=G["H"], FF=G["FF"], fmt=fmt, T=T,
+             zipf=zipf, seed=4)
+
+
+# Heavy-tailed activations (Student-t(2), 4 elements per row at 100x): the
+# int4 kernels remove the code offset through per-group activation sums kept
+# as bf16 hi + lo, whose cancellation is worst with such inputs.
+@pytest.mark.parametrize("fmt,T,zipf", [("int4", 16, None), ("int4", 256, None), ("int4", 128, 1.1),
+                                        ("int8", 16, None), ("bf16", 16, None)])
+def test_gemma_heavy_tailed_x(L, fmt, T, zipf):
+    run_case(L, f"gemma-{fmt}-T{T}-heavy-zipf{zipf}", E=G["E"], k=G["k"], H=G["H"], FF=G["FF"], fmt=fmt, T=T,
+             zipf=zipf, x_kind="heavy", seed=5)
 
 
 # ------------------------------------------------------------ invariants ----
