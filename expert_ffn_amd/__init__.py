@@ -48,6 +48,7 @@ def lib():
         ffn = [P, u64, P, i32, i32, i32, i32, i32, P, i32, i32, i32, P, P, P, i32, P, sz, P]
         for name in ("moe_expert_ffn", "moe_ffn_gate_up", "moe_ffn_down"):
             getattr(L, name).argtypes = ffn
+        L.moe_expert_ffn_noalloc.argtypes = ffn[:16] + [P]
         L.moe_combine.argtypes = [P, i32, P, P, i32, i32, i32, P, i32, P]
         L.moe_quantize.argtypes = [i32, P, i32, i32, P, P, P]
         L.moe_pack_expert.argtypes = [i32, P, P, i32, i32, P, P]
@@ -65,7 +66,7 @@ def lib():
         L.moe_verify_slot.argtypes = [i32, P, i32, i32, P, P, P]
         L.moe_slot_admit.argtypes = [P, i32, P, i32, i32]
         for name in ("moe_blob_layout", "moe_route_topk", "moe_permute", "moe_route_permute", "moe_expert_ffn",
-                     "moe_ffn_gate_up", "moe_ffn_down", "moe_combine", "moe_quantize",
+                     "moe_ffn_gate_up", "moe_ffn_down", "moe_expert_ffn_noalloc", "moe_combine", "moe_quantize",
                      "moe_pack_expert", "moe_router_topk", "moe_residency_refresh", "moe_min_weight", "moe_fill_slot", "moe_fill_slots", "moe_verify_slot",
                      "moe_slot_admit"):
             getattr(L, name).restype = ctypes.c_int
@@ -148,6 +149,17 @@ def expert_ffn(pool, slot_bytes, slot_of, E, H, FF, fmt, act, x, k, expert_offse
                out_routes, ws, stream=None):
     _ffn("moe_expert_ffn", pool, slot_bytes, slot_of, E, H, FF, fmt, act, x, x.shape[0], k,
          expert_offsets, sorted_route, out_routes, ws, stream)
+
+
+def expert_ffn_noalloc(pool, slot_bytes, slot_of, E, H, FF, fmt, act, x, k, expert_offsets, sorted_route,
+                       out_routes, stream=None):
+    """moe_expert_ffn_noalloc: the library's static scratch array is the workspace."""
+    _check(lib().moe_expert_ffn_noalloc(_ptr(pool), slot_bytes, _ptr(slot_of), E, H, FF, fmt, act, _ptr(x),
+                                        _dt(x), x.shape[0], k, _ptr(expert_offsets), _ptr(sorted_route),
+                                        _ptr(out_routes), _dt(out_routes), _stream(stream)))
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20
 
 
 def ffn_gate_up(pool, slot_bytes, slot_of, E, H, FF, fmt, act, x, k, expert_offsets,

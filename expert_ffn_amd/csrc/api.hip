@@ -3,6 +3,7 @@
 // a check fails; the reason is kept per thread for moe_last_error().
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "../../include/expert_ffn.h"
@@ -289,6 +290,57 @@ static moe_status ffn_entry(const char* fn, int phases, const void* pool, uint64
 moe_status moe_expert_ffn(FFN_PARAMS) { return ffn_entry("moe_expert_ffn", 3, FFN_ARGS); }
 moe_status moe_ffn_gate_up(FFN_PARAMS) { return ffn_entry("moe_ffn_gate_up", 1, FFN_ARGS); }
 moe_status moe_ffn_down(FFN_PARAMS) { return ffn_entry("moe_ffn_down", 2, FFN_ARGS); }
+
+}  // extern "C"
+
+// Workspace of moe_expert_ffn_noalloc: one array per device, allocated when the
+// library's code object is loaded on it and held until the process ends.
+static __device__ __align__(256) uint8_t scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+// Device address of this device's scratch array, looked up once per device
+// (the array's name is a host-side stand-in; kernels get this address).
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+hipError_t scratch_address(void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return hipSuccess;
+}
+}  // namespace
+
+extern "C" {
+
+moe_status moe_expert_ffn_noalloc(const void* pool, uint64_t slot_bytes, const int32_t* slot_of, int32_t E,
+                                  int32_t H, int32_t FF, int32_t wfmt, int32_t act, const void* x,
+                                  int32_t x_dtype, int32_t T, int32_t k, const int32_t* expert_offsets,
+                                  const int32_t* sorted_route, void* out_routes, int32_t out_dtype,
+                                  void* stream) {
+    const char* fn = "moe_expert_ffn_noalloc";
+    moe_status st = check_ffn_shape(fn, E, H, FF, wfmt, T, k);
+    if (st != MOE_OK) return st;
+    const size_t need = moe::ffn_workspace(T, k, H, FF).bytes;
+    if (need > MOE_NOALLOC_SCRATCH_BYTES)
+        return fail(MOE_E_WORKSPACE, fn, "T=%d k=%d H=%d FF=%d needs %zu workspace bytes > the %u-byte scratch array",
+                    T, k, H, FF, need, static_cast<unsigned>(MOE_NOALLOC_SCRATCH_BYTES));
+    void* ws = nullptr;
+    const hipError_t e = scratch_address(&ws);
+    if (e != hipSuccess) return hip_status(fn, e);
+    return ffn_entry(fn, 3, pool, slot_bytes, slot_of, E, H, FF, wfmt, act, x, x_dtype, T, k, expert_offsets,
+                     sorted_route, out_routes, out_dtype, ws, MOE_NOALLOC_SCRATCH_BYTES, stream);
+}
 
 moe_status moe_combine(const void* out_routes, int32_t out_dtype, const float* topk_w,
                        const int32_t* route_pos, int32_t T, int32_t k, int32_t H, void* y,

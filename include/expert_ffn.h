@@ -279,6 +279,28 @@ moe_status moe_ffn_down(const void* pool, uint64_t slot_bytes, const int32_t* sl
                         void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * moe_expert_ffn without a workspace argument, for callers that cannot
+ * allocate device memory around the call: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation.  Same arguments (minus ws
+ * and ws_bytes), results and errors as moe_expert_ffn.  The workspace is a
+ * static device array of MOE_NOALLOC_SCRATCH_BYTES (32 MiB) inside the
+ * library, one per GPU, held from the first call on that GPU until the
+ * process ends; its address is looked up once per device.  Calls whose
+ * moe_workspace_bytes(T, k, E, H, FF, wfmt) exceeds the array return
+ * MOE_E_WORKSPACE and enqueue nothing (at the Gemma-4-26B-A4B shape, up to
+ * T = 1024 with top-8 fits).  The call allocates nothing.  Every call on one
+ * GPU shares that GPU's array and nothing in it needs to start zeroed: calls
+ * that overlap on one GPU (other streams, other threads) race and must be
+ * ordered by the caller.
+ */
+#define MOE_NOALLOC_SCRATCH_BYTES (32u << 20)
+moe_status moe_expert_ffn_noalloc(const void* pool, uint64_t slot_bytes, const int32_t* slot_of, int32_t E,
+                                  int32_t H, int32_t FF, int32_t wfmt, int32_t act, const void* x,
+                                  int32_t x_dtype, int32_t T, int32_t k, const int32_t* expert_offsets,
+                                  const int32_t* sorted_route, void* out_routes, int32_t out_dtype,
+                                  void* stream);
+
+/*
  * Weighted scatter-combine back to token order (Winery-Strata
  * RemoteExperts::finish scatters each computed row back to its route; prain
  * README, "Trading quality for speed": a token's result is its routes weighted

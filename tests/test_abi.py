@@ -84,6 +84,13 @@ def test_host_validation_errors(L):
     assert rc == 2
     rc, msg = _call(L, "moe_combine", fake, 0, fake, fake, 4, 2, 60, fake, 0, None)
     assert rc == 2 and "H=60" in msg
+    # no-alloc FFN: a workspace larger than the static scratch array is refused on the host
+    rc, msg = _call(L, "moe_expert_ffn_noalloc", fake, ctypes.c_uint64(3159552), fake, 128, 2816, 704, 2, 0, fake, 1,
+                    4096, 8, fake, fake, fake, 0, None)
+    assert rc == 4 and "scratch" in msg
+    rc, msg = _call(L, "moe_expert_ffn_noalloc", fake, ctypes.c_uint64(3159552), fake, 128, 2816, 700, 2, 0, fake, 1,
+                    16, 8, fake, fake, fake, 0, None)
+    assert rc == 2 and "FF=700" in msg
     rc, msg = _call(L, "moe_fill_slot", 2, fake, 1, 2816, 704, None, fake, None)
     assert rc == 1 and "staging" in msg
     rc, msg = _call(L, "moe_fill_slot", 2, fake, 0, 2816, 704, None, fake, None)
