@@ -93,6 +93,7 @@ class StackRunner:
         from expert_ffn_amd.layer import MoeLayer
         self.L = len(logits)
         self.T = T
+        self.sb = sb
         dev = pool.device
         # per-route outputs in bf16: half the bytes of the down write and the combine read
         self.ml = MoeLayer(E, k, H, FF, fmt, T, device=dev, out_dtype=torch.bfloat16)
@@ -155,6 +156,99 @@ class StackRunner:
         with torch.cuda.graph(graph, stream=stream):
             (body or self.step)()
         return graph
+
+
+def call_times(run, stream, reps, graphs=True):
+    """Microseconds per launch of each call of the step -- route_permute,
+    gate_up, down, combine -- from a HIP graph of that call for every layer
+    (on the routing the last step left; eager calls with graphs=False),
+    replayed `reps` times between two HIP events recorded on the stream the
+    calls run on."""
+    import torch
+    out = {}
+    for name, idx in (("route_permute", 0), ("gate_up", 1), ("down", 2), ("combine", 3)):
+        body = lambda idx=idx: [run._call(c[idx]) for c in run.calls]
+        g = run.capture(stream, body=body) if graphs else None
+        fn = g.replay if graphs else body
+        fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        e1.synchronize()
+        out[name] = round(e0.elapsed_time(e1) * 1e3 / (reps * run.L), 2)
+        del g
+    return out
+
+
+def trace_avg_us(kernel, summary=os.path.join(ROOT, "profiles", "kernels_int4_stack_decode_T16_prefill_T1024.md")):
+    """Average duration of a kernel in the committed rocprofv3 trace summary
+    (None if absent)."""
+    try:
+        with open(summary) as f:
+            for line in f:
+                if line.startswith(f"| `moe::{kernel}"):
+                    return float(line.split("|")[4])
+    except OSError:
+        pass
+    return None
+
+
+def measure_peaks(lib, dev, pool, run, stream, reps=5):
+    """Achieved peaks on this GPU (the measurement library's kernels):
+    streaming read of 8 GiB of the slot pool (best over grid sizes), the decode
+    gate/up kernel's weight loads alone over the stack's layers, and
+    back-to-back bf16 MFMA 32x32x16."""
+    import ctypes
+
+    import torch
+    from expert_ffn_amd import _build
+    P = ctypes.c_void_p
+    pk = ctypes.CDLL(_build.PEAKS_LIB)
+    pk.peak_stream_read.argtypes = [P, ctypes.c_uint64, ctypes.c_int, P, P]
+    pk.peak_tile_loads.argtypes = [P, ctypes.c_uint64, P, P, ctypes.c_int, ctypes.c_int, ctypes.c_int, P, P]
+    pk.peak_mfma_bf16.argtypes = [ctypes.c_int, ctypes.c_int, P, P]
+    sink = torch.zeros(1024, dtype=torch.int32, device=dev)
+    s = P(stream.cuda_stream)
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+
+    def timed(fn, n):
+        fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(n):
+            fn()
+        e1.record(stream)
+        e1.synchronize()
+        return e0.elapsed_time(e1) * 1e-3 / n   # s per call
+
+    out = {}
+    nbytes = min(pool.numel(), 8 << 30)
+    best = (0.0, 0)
+    for blocks in (cus * 4, cus * 8, cus * 16, cus * 32):
+        t = timed(lambda: pk.peak_stream_read(P(pool.data_ptr()), nbytes, blocks, P(sink.data_ptr()), s), reps)
+        best = max(best, (nbytes / t / 1e9, blocks))
+    out["hbm_stream_read_gbs"] = round(best[0], 1)
+    out["hbm_stream_read_blocks"] = best[1]
+    E, H, FF = G["E"], G["H"], G["FF"]
+    w13_codes = 2 * FF * H // 2
+    dist = [int((np.diff(r["offsets"].cpu().numpy()) > 0).sum()) for r in run.rt]
+
+    def tiles():
+        for l in range(run.L):
+            pk.peak_tile_loads(P(pool.data_ptr()), run.sb, P(run.slot_d[l].data_ptr()),
+                               P(run.rt[l]["offsets"].data_ptr()), E, H, FF, P(sink.data_ptr()), s)
+    t = timed(tiles, reps)
+    out["decode_tile_loads_gbs"] = round(sum(dist) * w13_codes / t / 1e9, 1)
+    iters, blocks = 4000, cus * 2
+    fsink = sink.view(torch.float32)
+    t = timed(lambda: pk.peak_mfma_bf16(blocks, iters, P(fsink.data_ptr()), s), reps)
+    out["mfma_bf16_tflops"] = round(blocks * 4 * iters * 4 * 32768 / t / 1e12, 1)
+    out["note"] = ("stream read: 16-byte loads, 8 in flight per thread, over 8 GiB; tile loads: the "
+                   "decode gate/up kernel's weight fragments only (w13 codes of the routed experts, "
+                   "no compute); mfma: 4 independent 32x32x16 bf16 chains per wave, 8 waves per CU")
+    return out
 
 
 def realised_routing(lib, runner, logits):
@@ -246,6 +340,30 @@ def summarize_pmc(fetch_dir, write_dir, commands):
     print(json.dumps(out, indent=1))
 
 
+def summarize_counters(dirs, dest, command, kernels):
+    """Per kernel (names containing one of `kernels`), the mean per dispatch of
+    every counter collected by the rocprofv3 --pmc runs under dirs, as a
+    markdown table (derived ratios below it)."""
+    table = {}
+    for d in dirs:
+        for kname, cname, v in _counter_rows(d):
+            base = kname.split("(")[0].replace("void ", "")
+            for kk in kernels:
+                if kk in base:
+                    table.setdefault(base, {}).setdefault(cname, []).append(v)
+    cols = sorted({c for v in table.values() for c in v})
+    lines = ["# rocprofv3 counters per dispatch", "", "Commands (from the repository root):", "", "```",
+             command, "```", "", "| kernel | dispatches | " + " | ".join(cols) + " |",
+             "|---|---|" + "---|" * len(cols)]
+    for name, cv in sorted(table.items()):
+        n = max(len(v) for v in cv.values())
+        vals = [f"{np.mean(cv[c]):.4g}" if c in cv else "" for c in cols]
+        lines.append(f"| `{name[:60]}` | {n} | " + " | ".join(vals) + " |")
+    with open(dest, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def summarize_trace(trace_dir, dest, command):
     """Per-kernel count / average / median duration from a rocprofv3
     --kernel-trace --stats run written with -f csv, as a markdown table."""
@@ -281,39 +399,83 @@ def summarize_trace(trace_dir, dest, command):
     print("\n".join(lines[:40]))
 
 
-def cpu_baseline(seed, T, budget_s=20.0):
-    """The oracle on one layer of the same stack (layer 0, decode T tokens),
-    repeated until about budget_s of CPU work; scaled to the 30-layer step."""
+def _oracle_layer_setup(seed_w, seed_x, layer, T):
+    """Inputs of one stack layer for the oracle: logits, fp32 x, and a pool
+    with the experts those logits route to, packed by the oracle from the
+    layer's bf16 weights (drawn as the stack draws them).  Not timed."""
     import torch
 
     import oracle as ora
     E, k, H, FF = G["E"], G["k"], G["H"], G["FF"]
-    logits = synth.logits(seed, 0, T, E)
-    x = ora.bf16_to_f32(synth.x_bf16(seed, 0, T, H))
+    logits = synth.logits(seed_x, layer, T, E)
+    x = ora.bf16_to_f32(synth.x_bf16(seed_x, layer, T, H))
     ids, _ = ora.route_topk(logits, k)
     need = sorted(set(int(e) for e in ids.reshape(-1)))
-    w13, w2 = synth.layer_weights_cuda(seed, 0, E, H, FF, "cuda")
+    w13, w2 = synth.layer_weights_cuda(seed_w, layer, E, H, FF, "cuda")
     w13 = w13.view(torch.int16).cpu().numpy().view(np.uint16)
     w2 = w2.view(torch.int16).cpu().numpy().view(np.uint16)
     sb = ora.expert_bytes(2, H, FF)
     pool = np.zeros(E * sb, np.uint8)
-    for e in need:                       # packing is not timed
+    for e in need:
         pool[e * sb:(e + 1) * sb] = ora.pack_expert(2, w13[e], w2[e], H, FF)
-    slot_of = np.arange(E, dtype=np.int32)    # expert e in slot e (only routed ones packed)
-    reps, t0 = 0, time.perf_counter()
-    while True:
-        ora.moe_layer(logits, x, pool, sb, slot_of, H, FF, 2, 0, k)
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s or reps >= 50:
-            break
-    per_layer = el / reps
-    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
-    return dict(value=round(T / (per_layer * L_LAYERS), 3), unit="tokens/s", cores=cores,
-                kind="oracle",
-                sample=f"layer 0 of 30 at T={T} (int4, {len(need)} distinct experts), {reps} runs "
-                       f"of route+permute+FFN+combine, {per_layer * 1e3:.1f} ms per layer, "
-                       f"scaled x30 to the stack step")
+    del w13, w2
+    return logits, x, pool, sb, np.arange(E, dtype=np.int32), len(need)
+
+
+def cpu_baseline(seed, T, layers=L_LAYERS):
+    """The oracle as it stands (plain C, fp64 accumulation, OpenMP over routes)
+    on bounded samples of the benchmark's own inputs, route + permute + FFN +
+    combine per layer (packing and input generation not timed):
+      decode  layer 0 at T tokens, all host threads (median of 3 runs) and one
+              thread (one run), scaled to the step of `layers` layers;
+      prefill layers 0 and 15 at T = 1024 (one run each, all threads), the
+              mean extrapolated to the chunk of `layers` layers.
+    value = the all-thread decode rate, in the headline's unit."""
+    import oracle as ora
+    E, k, H, FF = G["E"], G["k"], G["H"], G["FF"]
+    threads = ora.set_threads(0)
+    legs = []
+
+    def run(setup, reps):
+        logits, x, pool, sb, slot_of, _ = setup
+        ts = []
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            ora.moe_layer(logits, x, pool, sb, slot_of, H, FF, 2, 0, k)
+            ts.append(time.perf_counter() - t0)
+        return float(np.median(ts))
+
+    dec = _oracle_layer_setup(seed, seed, 0, T)
+    t_all = run(dec, 3)
+    legs.append(dict(leg="decode", T=T, threads=threads, s_per_layer=round(t_all, 4),
+                     tokens_per_s=round(T / (t_all * layers), 3)))
+    ora.set_threads(1)
+    t_one = run(dec, 1)
+    ora.set_threads(threads)
+    legs.append(dict(leg="decode", T=T, threads=1, s_per_layer=round(t_one, 4),
+                     tokens_per_s=round(T / (t_one * layers), 4)))
+    del dec
+    tp = []
+    for l in (0, 15):
+        pre = _oracle_layer_setup(seed, seed + 1, l, 1024)
+        tp.append(run(pre, 1))
+        del pre
+    t_pre = float(np.mean(tp))
+    legs.append(dict(leg="prefill", T=1024, threads=threads, layers_sampled=[0, 15],
+                     s_per_layer=[round(v, 3) for v in tp],
+                     tokens_per_s=round(1024 / (t_pre * layers), 3),
+                     note=f"extrapolated from 2 sampled layers to {layers}"))
+    return dict(value=legs[0]["tokens_per_s"], unit="tokens/s", cores=threads, kind="oracle",
+                sample=f"decode: layer 0 of {layers} at T={T} ({dec_need_note(seed, T)}), median of 3 runs of "
+                       f"route+permute+FFN+combine on {threads} threads, {t_all * 1e3:.1f} ms per layer, "
+                       f"scaled x{layers} to the stack step; also 1 thread and a T=1024 prefill leg (legs)",
+                legs=legs)
+
+
+def dec_need_note(seed, T):
+    import oracle as ora
+    ids, _ = ora.route_topk(synth.logits(seed, 0, T, G["E"]), G["k"])
+    return f"int4, {len(set(ids.reshape(-1).tolist()))} distinct experts"
 
 
 def measure_configs(lib, dev, seed, copies=4, reps=20):
@@ -353,6 +515,7 @@ def measure_configs(lib, dev, seed, copies=4, reps=20):
                 graph.replay()
             torch.cuda.synchronize()
             us = (time.perf_counter() - t0) / (reps * copies) * 1e6
+            calls = call_times(run, stream, max(3, reps // 4))
             del graph, run
         distinct = float(np.mean([d for d, _ in routing]))
         kept = float(np.mean([r for _, r in routing]))
@@ -363,7 +526,8 @@ def measure_configs(lib, dev, seed, copies=4, reps=20):
                         distinct_experts=round(distinct, 1), hbm_gbs=round(byts / (us * 1e-6) / 1e9, 1),
                         hbm_frac=round(byts / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
                         mfma_tflops=round(flops / (us * 1e-6) / 1e12, 1),
-                        mfma_frac=round(flops / (us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)))
+                        mfma_frac=round(flops / (us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                        calls_us=calls))
         log(json.dumps(out[-1]))
     return out
 
@@ -797,6 +961,11 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--tokens", type=int, default=16)
     ap.add_argument("--prefill-steps", type=int, default=5)
+    ap.add_argument("--layers", type=int, default=L_LAYERS, help="stack depth (30; fewer for profiling runs)")
+    ap.add_argument("--no-peaks", dest="peaks", action="store_false",
+                    help="skip the achieved-peak microbenchmarks")
+    ap.add_argument("--no-configs", dest="configs_summary", action="store_false",
+                    help="skip the single-layer figures of the other workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--calib-copy", action="store_true",
@@ -806,6 +975,11 @@ def main():
     ap.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_DIR", "DEST"),
                     help="write a kernel-trace summary from a rocprofv3 run (no GPU)")
     ap.add_argument("--command", default="", help="the profiled command, recorded in summaries")
+    ap.add_argument("--summarize-counters", nargs="+", metavar="DIR",
+                    help="counter table of --kernels from rocprofv3 --pmc runs, written to --dest")
+    ap.add_argument("--kernels", nargs="+", default=["ffn_int4_gemm_kernel", "gate_up_int4_dec_kernel",
+                                                     "down_int4_dec_kernel"])
+    ap.add_argument("--dest", default="")
     ap.add_argument("--configs", action="store_true",
                     help="instead of the stack step: single-layer timings of the other workloads "
                          "(one JSON object per line)")
@@ -827,6 +1001,9 @@ def main():
         return
     if args.summarize_trace:
         summarize_trace(*args.summarize_trace, command=args.command)
+        return
+    if args.summarize_counters:
+        summarize_counters(args.summarize_counters, args.dest, args.command, args.kernels)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the expert FFN here runs on one GPU and has no "
@@ -860,16 +1037,17 @@ def main():
     E, k, H, FF = G["E"], G["k"], G["H"], G["FF"]
     fmt = lib.W_INT4_G64
     T = args.tokens
+    Ls = args.layers
 
     t0 = time.time()
-    log(f"building the {L_LAYERS}-layer int4 stack ...")
-    pool, sb, slots = build_stack(lib, args.seed, L_LAYERS, E, H, FF, fmt, dev)
+    log(f"building the {Ls}-layer int4 stack ...")
+    pool, sb, slots = build_stack(lib, args.seed, Ls, E, H, FF, fmt, dev)
     log(f"  pool {pool.numel() / 2**30:.2f} GiB, slot {sb} B, built in {time.time() - t0:.1f} s")
 
     if args.calib_copy:
         calibration_copies(dev)
     stream = torch.cuda.Stream()
-    logits, xs = layer_inputs(args.seed, L_LAYERS, T, E, H, dev)
+    logits, xs = layer_inputs(args.seed, Ls, T, E, H, dev)
     with torch.cuda.stream(stream):
         run = StackRunner(lib, pool, sb, slots, T, E, k, H, FF, fmt, logits, xs, stream)
         routing = realised_routing(lib, run, logits)
@@ -877,10 +1055,9 @@ def main():
             run.step()
         torch.cuda.synchronize()
         graph = None
-        if not args.no_graph:
-            graph = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(graph, stream=stream):
-                run.step()
+        use_graph = not args.no_graph
+        if use_graph:
+            graph = run.capture(stream)
             for _ in range(3):
                 graph.replay()
         torch.cuda.synchronize()
@@ -890,64 +1067,99 @@ def main():
             graph.replay() if graph is not None else run.step()
         torch.cuda.synchronize()
         elapsed = time.perf_counter() - t_start
-        # instrumented pass (same steps, eager): per-launch gate/up durations
-        ev = [[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
-              for _ in range(L_LAYERS)]
-        gu_ms = []
-        for _ in range(max(3, min(args.steps, 20))):
-            run.step(events=ev)
-            torch.cuda.synchronize()
-            gu_ms.append([ev[l][0].elapsed_time(ev[l][1]) for l in range(L_LAYERS)])
+        # per-call times (HIP events around graphs of one call kind)
+        calls = call_times(run, stream, max(5, min(args.steps, 20)), graphs=graph is not None)
         t_e = time.perf_counter()
         for _ in range(args.steps):
             run.step()
         torch.cuda.synchronize()
         eager_ms = (time.perf_counter() - t_e) / args.steps * 1e3
+        peaks = measure_peaks(lib, dev, pool, run, stream) if args.peaks else None
     ms_per_step = elapsed / args.steps * 1e3
     tok_s = T * args.steps / elapsed
 
     # algorithmic bytes: each distinct expert's packed bytes once, plus x, y, logits and the route indices
     off = lib.blob_layout(fmt, H, FF)
-    w13_bytes = off[2]                    # w13 codes + scales (+ alignment, none at this shape)
+    w13_bytes, w2_bytes = off[2], sb - off[2]   # w13 codes + scales; w2 codes + scales
     per_layer_io = T * H * 2 * 2 + T * E * 4 + T * k * 4 * 4 + (E + 1) * 4
     step_bytes = sum(d * sb + per_layer_io for d, _ in routing)
     step_gbs = step_bytes / (ms_per_step * 1e-3) / 1e9
-    gu = np.array(gu_ms)                  # [reps, L] ms
-    gu_bytes = np.array([d * w13_bytes + T * H * 2 for d, _ in routing], np.float64)
-    achieved = float(gu_bytes.sum() / (gu.mean(0).sum() * 1e-3) / 1e9)
+    dist = float(np.mean([d for d, _ in routing]))
+    gu_bytes = dist * w13_bytes + T * H * 2
+    dn_bytes = dist * w2_bytes + T * k * FF * 2 + T * k * H * 2
+    achieved = gu_bytes / (calls["gate_up"] * 1e-6) / 1e9
     khash = kernel_source_hash()
     traffic = measured_traffic(khash)
+    tr_us = trace_avg_us(GATE_UP_KERNEL)
     roofline = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                     frac=round(achieved / HBM_PEAK_GBS, 4), traffic=traffic,
                     kernel=GATE_UP_KERNEL + " (moe_ffn_gate_up)",
-                    avg_launch_us=round(float(gu.mean()) * 1e3, 2),
-                    bytes_per_launch=round(float(gu_bytes.mean())))
+                    avg_launch_us=calls["gate_up"], bytes_per_launch=round(gu_bytes),
+                    trace_avg_us=tr_us,
+                    trace_frac=round(gu_bytes / (tr_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4) if tr_us else None)
+    if peaks:
+        roofline["frac_of_measured_stream"] = round(achieved / peaks["hbm_stream_read_gbs"], 4)
+    kernels = {name: dict(us=us) for name, us in calls.items()}
+    for name, b in (("gate_up", gu_bytes), ("down", dn_bytes)):
+        kernels[name]["gbs"] = round(b / (calls[name] * 1e-6) / 1e9, 1)
+        kernels[name]["hbm_frac"] = round(b / (calls[name] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
+    ffn_us = calls["gate_up"] + calls["down"]
+    kernels["expert_ffn_hbm_frac"] = round((gu_bytes + dn_bytes) / (ffn_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
 
     # prefill chunk through the same stack
     prefill = None
     if args.prefill_steps > 0:
         Tp = 1024
-        lp, xp = layer_inputs(args.seed + 1, L_LAYERS, Tp, E, H, dev)
+        lp, xp = layer_inputs(args.seed + 1, Ls, Tp, E, H, dev)
         with torch.cuda.stream(stream):
             runp = StackRunner(lib, pool, sb, slots, Tp, E, k, H, FF, fmt, lp, xp, stream)
             rp = realised_routing(lib, runp, lp)
             runp.step()
+            gp = runp.capture(stream) if use_graph else None
+            stepp = gp.replay if gp is not None else runp.step
+            stepp()
             torch.cuda.synchronize()
             tp = time.perf_counter()
             for _ in range(args.prefill_steps):
-                runp.step()
+                stepp()
             torch.cuda.synchronize()
             pms = (time.perf_counter() - tp) / args.prefill_steps * 1e3
-        flops = sum(r for _, r in rp) * 6.0 * H * FF
+            callp = call_times(runp, stream, 3, graphs=gp is not None)
+            del gp, stepp
+        kept = sum(r for _, r in rp)
+        flops = kept * 6.0 * H * FF
+        pbytes = sum(d * sb for d, _ in rp) + Ls * (Tp * H * 2 * 2 + Tp * E * 4 + Tp * k * 16)
+        gu_fl, dn_fl = kept / Ls * 4.0 * H * FF, kept / Ls * 2.0 * H * FF
+        tf = lambda fl, us: fl / (us * 1e-6) / 1e12
         prefill = dict(T=Tp, ms_per_chunk=round(pms, 3), tokens_per_s=round(Tp / (pms * 1e-3), 1),
                        mfma_tflops=round(flops / (pms * 1e-3) / 1e12, 1),
-                       mfma_frac=round(flops / (pms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4))
+                       mfma_frac=round(flops / (pms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                       hbm_gbs=round(pbytes / (pms * 1e-3) / 1e9, 1),
+                       calls_us=callp,
+                       roofline=dict(bound="mfma", kernel="ffn_int4_gemm_kernel (moe_ffn_gate_up: prep + GEMM)",
+                                     achieved=round(tf(gu_fl, callp["gate_up"]), 1), peak=MFMA_BF16_PEAK_TFLOPS,
+                                     unit="TFLOP/s",
+                                     frac=round(tf(gu_fl, callp["gate_up"]) / MFMA_BF16_PEAK_TFLOPS, 4),
+                                     down_tflops=round(tf(dn_fl, callp["down"]), 1),
+                                     down_frac=round(tf(dn_fl, callp["down"]) / MFMA_BF16_PEAK_TFLOPS, 4)))
+        if peaks:
+            prefill["mfma_frac_of_measured"] = round(prefill["mfma_tflops"] / peaks["mfma_bf16_tflops"], 4)
         del runp
+
+    configs = None
+    if args.configs_summary:
+        log("single-layer timings of the other workloads ...")
+        del graph, run
+        torch.cuda.empty_cache()
+        configs = [{k2: r[k2] for k2 in ("config", "T", "us_per_layer", "tokens_per_s", "hbm_frac", "mfma_frac", "calls_us")}
+                   for r in measure_configs(lib, dev, args.seed)]
 
     cpu = None
     if not args.no_cpu_baseline:
-        log("timing the CPU oracle on a sample ...")
-        cpu = cpu_baseline(args.seed, T)
+        log("timing the CPU oracle on samples ...")
+        tc = time.time()
+        cpu = cpu_baseline(args.seed, T, Ls)
+        log(f"  oracle legs took {time.time() - tc:.1f} s")
 
     out = {
         "metric": "expert-FFN tokens/s + HBM GB/s (int4 decode T=16) and MFMA util (T=1024 prefill)",
@@ -956,16 +1168,19 @@ def main():
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) logits and activations, N(0,0.02) weights; "
                 "random-init Gemma-4-26B-A4B expert shapes)",
-        "config": {"workload": "int4_stack_decode: 30 MoE layers x 128 int4 experts (w4a16, bf16 scale "
+        "config": {"workload": f"int4_stack_decode: {Ls} MoE layers x 128 int4 experts (w4a16, bf16 scale "
                                "per 64, MSE clip), H=2816, FF=704, top-8 renormalised, T=16 decode, "
                                "shuffled per-layer slot tables, 11.3 GiB resident",
-                   "layers": L_LAYERS, "experts": E, "top_k": k, "hidden": H, "ffn": FF,
-                   "tokens": T, "weights": "int4_g64", "graph": graph is not None},
+                   "layers": Ls, "experts": E, "top_k": k, "hidden": H, "ffn": FF,
+                   "tokens": T, "weights": "int4_g64", "graph": use_graph},
         "hbm_gbs": round(step_gbs, 1), "hbm_frac": round(step_gbs / HBM_PEAK_GBS, 4),
         "eager_ms_per_step": round(eager_ms, 4),
-        "distinct_experts_per_layer": round(float(np.mean([d for d, _ in routing])), 2),
+        "distinct_experts_per_layer": round(dist, 2),
         "roofline": roofline,
+        "kernels": kernels,
         "prefill": prefill,
+        "peaks": peaks,
+        "configs": configs,
         "cpu_baseline": cpu,
         "kernel_hash": khash,
     }

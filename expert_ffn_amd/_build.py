@@ -10,6 +10,9 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(HERE, "_obj")
 LIB = os.path.join(HERE, "libexpert_ffn.so")
+# measurement kernels of the benchmark (achieved peaks): a library of their own
+PEAKS_SRC = os.path.join(HERE, "measure", "peaks.hip")
+PEAKS_LIB = os.path.join(HERE, "libpeaks.so")
 ARCH = os.environ.get("EXPERT_FFN_ARCH", "gfx950")
 
 HIPCC = "/opt/rocm/bin/hipcc" if os.path.exists("/opt/rocm/bin/hipcc") else "hipcc"
@@ -52,7 +55,17 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"link failed:\n{r.stderr}")
     os.replace(tmp, LIB)
     del deps
+    build_peaks()
     return LIB
+
+
+def build_peaks() -> str:
+    tmp = PEAKS_LIB + ".tmp%d" % os.getpid()
+    r = subprocess.run([HIPCC, *FLAGS, "-shared", PEAKS_SRC, "-o", tmp], capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {PEAKS_SRC}:\n{r.stderr}")
+    os.replace(tmp, PEAKS_LIB)
+    return PEAKS_LIB
 
 
 if __name__ == "__main__":

@@ -262,6 +262,7 @@ static moe_status ffn_entry(const char* fn, int phases, const void* pool, uint64
     P.slot_bytes = slot_bytes;
     P.slot_of = slot_of;
     P.E = E; P.H = H; P.FF = FF; P.fmt = wfmt; P.act = act; P.T = T; P.k = k;
+    P.kmul = moe::token_multiplier(k);
     P.offsets = expert_offsets;
     P.sorted_route = sorted_route;
     P.x = x;

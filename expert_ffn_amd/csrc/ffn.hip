@@ -720,10 +720,14 @@ __global__ __launch_bounds__(256) void gate_up_int4_dec_kernel(FfnParams P) {
     constexpr int NGW = 2 * NDW;
     static_assert(NGW <= 32, "the bias MFMA takes 32 groups");
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-    const int nwt = (P.FF >> 4) / GUD_TPW;   // workgroups per expert
-    const int e = blockIdx.x / nwt, u0 = (blockIdx.x - e * nwt) * GUD_TPW;
+    // grid (tile, expert).  The group bounds and the expert's slot are
+    // requested together (one round trip), before the exit test.
+    const int e = blockIdx.y, u0 = blockIdx.x * GUD_TPW;
     const int beg = P.offsets[e], end = P.offsets[e + 1];
-    if (beg >= end || end - beg > P.gmin) return;   // no routes, or the group is the GEMM's
+    const int slot = P.slot_of[e];
+    // no routes, or the group is the GEMM's (a resident expert has slot >= 0;
+    // the test on it makes the slot load part of the same round trip)
+    if ((beg >= end) | (end - beg > P.gmin) | (slot < 0)) return;
     const int H = P.H, G = H / 64, GS = (G + 39) & ~7;
     const GudLds L = gud_lds(H);
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r = lane & 15, q = lane >> 4;
@@ -744,11 +748,16 @@ __global__ __launch_bounds__(256) void gate_up_int4_dec_kernel(FfnParams P) {
     // preparation kernel (xq and its group sums).
     constexpr int NSB = (GUD_RT * NDT * 16 + 255) / 256;
     static_assert(GUD_RT == 4, "four route tokens");
-    const uint8_t* blob = P.pool + static_cast<uint64_t>(P.slot_of[e]) * P.slot_bytes;
+    const uint8_t* blob = P.pool + static_cast<uint64_t>(slot) * P.slot_bytes;
     constexpr int HC = 128 * NDT;   // H of this instantiation
     constexpr int nb = HC / 8;      // blocks per row, a multiple of 16
-    int tk0 = P.sorted_route[beg] / P.k, tk1 = P.sorted_route[beg + min(1, end - beg - 1)] / P.k;
-    int tk2 = P.sorted_route[beg + min(2, end - beg - 1)] / P.k, tk3 = P.sorted_route[beg + min(3, end - beg - 1)] / P.k;
+    // the first tile's 4 route indices, requested together, then their tokens
+    int tk0 = P.sorted_route[beg], tk1 = P.sorted_route[beg + min(1, end - beg - 1)];
+    int tk2 = P.sorted_route[beg + min(2, end - beg - 1)], tk3 = P.sorted_route[beg + min(3, end - beg - 1)];
+    tk0 = route_token(tk0, P.kmul, P.k);
+    tk1 = route_token(tk1, P.kmul, P.k);
+    tk2 = route_token(tk2, P.kmul, P.k);
+    tk3 = route_token(tk3, P.kmul, P.k);
     u32x4 xr[NSB];
     // Blocks past the tile's rows are neither read nor converted (nr * nb is
     // uniform, so the skips are scalar branches).
@@ -906,10 +915,14 @@ __global__ __launch_bounds__(256) void gate_up_int4_dec_kernel(FfnParams P) {
     // further route tiles (groups of more than 4 routes)
     for (int rt = beg + GUD_RT; rt < end; rt += GUD_RT) {
         const int nr = min(GUD_RT, end - rt);
-        tk0 = P.sorted_route[rt] / P.k;
-        tk1 = P.sorted_route[rt + min(1, nr - 1)] / P.k;
-        tk2 = P.sorted_route[rt + min(2, nr - 1)] / P.k;
-        tk3 = P.sorted_route[rt + min(3, nr - 1)] / P.k;
+        tk0 = P.sorted_route[rt];
+        tk1 = P.sorted_route[rt + min(1, nr - 1)];
+        tk2 = P.sorted_route[rt + min(2, nr - 1)];
+        tk3 = P.sorted_route[rt + min(3, nr - 1)];
+        tk0 = route_token(tk0, P.kmul, P.k);
+        tk1 = route_token(tk1, P.kmul, P.k);
+        tk2 = route_token(tk2, P.kmul, P.k);
+        tk3 = route_token(tk3, P.kmul, P.k);
         __syncthreads();   // the previous tile's readers of xs, xsum and s_red are done
         load_x(nr);
         store_x(nr);
@@ -940,12 +953,13 @@ __global__ __launch_bounds__(256) void down_int4_dec_kernel(FfnParams P) {
     __shared__ __attribute__((aligned(16))) uint16_t hs[RT * 128 * (NDS + 1)];
     __shared__ float s_scs[4][TPW][NG * 16];
     const int FF = P.FF;
-    const int nblk = P.H / (64 * TPW);
-    const int e = blockIdx.x / nblk, blk = blockIdx.x - e * nblk;
+    // grid (64 TPW-row block of H, expert); group bounds and slot in one round trip
+    const int e = blockIdx.y, blk = blockIdx.x;
     const int beg = P.offsets[e], end = P.offsets[e + 1];
-    if (beg >= end || end - beg > P.gmin) return;
+    const int slot = P.slot_of[e];
+    if ((beg >= end) | (end - beg > P.gmin) | (slot < 0)) return;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r = lane & 15, q = lane >> 4;
-    const uint8_t* blob = P.pool + static_cast<uint64_t>(P.slot_of[e]) * P.slot_bytes;   // scalar, first
+    const uint8_t* blob = P.pool + static_cast<uint64_t>(slot) * P.slot_bytes;
     const int m0 = (blk * 4 + wave) * 16 * TPW;   // first row of the wave; tile tt is rows m0 + 16 tt
     constexpr int NHB = (RT * 128 * (NDS + 1) / 8 + 255) / 256;   // blocks of 8 per thread (upper bound)
     const int nbr = FF / 8;                                         // blocks per h row
@@ -1139,9 +1153,9 @@ static void launch_int4(const FfnParams& P, int phases, hipStream_t s) {
         const size_t smem = 4 * 16 * (P.FF / 64) * sizeof(float);
         if (P.FF == 704) {   // decode: 5 double steps and a tail group
             if (P.H % (64 * DND_TPW) == 0)
-                hipLaunchKernelGGL((down_int4_dec_kernel<5, true, DND_TPW>), dim3(P.E * (P.H / (64 * DND_TPW))), dim3(256), 0, s, P);
+                hipLaunchKernelGGL((down_int4_dec_kernel<5, true, DND_TPW>), dim3(P.H / (64 * DND_TPW), P.E), dim3(256), 0, s, P);
             else
-                hipLaunchKernelGGL((down_int4_dec_kernel<5, true, 1>), dim3(P.E * (P.H / 64)), dim3(256), 0, s, P);
+                hipLaunchKernelGGL((down_int4_dec_kernel<5, true, 1>), dim3(P.H / 64, P.E), dim3(256), 0, s, P);
             return;
         }
         if (P.FF <= 704)   // <= 5 double steps and a tail, <= 11 groups
@@ -1239,7 +1253,7 @@ hipError_t launch_ffn(const FfnParams& P0, int phases, hipStream_t s) {
     }
     if ((phases & 1) && P.fmt == W_INT4 && P.H == 2816 && P.FF % (16 * GUD_TPW) == 0) {
         const GudLds L = gud_lds(P.H);
-        const dim3 grid(P.E * (P.FF / 16 / GUD_TPW));
+        const dim3 grid(P.FF / 16 / GUD_TPW, P.E);
         if (P.x_dt == F32) {
             const int64_t nblk = static_cast<int64_t>(P.T) * P.H / 8;
             P.xq = P.xq_out;

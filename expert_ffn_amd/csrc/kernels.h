@@ -65,9 +65,19 @@ struct FfnParams {
     void* out;                // [T*k, H] fp32 or bf16 (out_dt)
     int out_dt;
     uint64_t o13, os13, o2, os2;  // blob sub-block offsets
+    uint64_t kmul;            // ceil(2^32 / k): route -> token by a multiply (route_token)
     int gmin;                 // int4: groups of more than gmin routes belong to the grouped GEMM,
                               // the others to the streaming kernels (INT_MAX: no GEMM)
 };
+
+// token of route i = t * k + j (i < 2^30, k <= 32): q = (i * ceil(2^32 / k)) >> 32
+// is t or t + 1 (the error i * (ceil - 2^32 / k) / 2^32 stays below 1/4), so one
+// comparison corrects it; scalar multiplies instead of an integer division
+__host__ __device__ __forceinline__ int route_token(int i, uint64_t kmul, int k) {
+    const int q = static_cast<int>((static_cast<uint64_t>(static_cast<uint32_t>(i)) * kmul) >> 32);
+    return q * k > i ? q - 1 : q;
+}
+inline uint64_t token_multiplier(int k) { return ((1ull << 32) + static_cast<uint64_t>(k) - 1) / static_cast<uint64_t>(k); }
 
 // Workspace layout of the expert FFN.
 struct FfnWorkspace {

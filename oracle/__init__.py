@@ -51,6 +51,8 @@ def lib():
 def _declare(L):
     P = ctypes.c_void_p
     i32, i64, u64 = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64
+    L.oracle_set_threads.argtypes = [i32]
+    L.oracle_set_threads.restype = ctypes.c_int
     L.oracle_f32_to_bf16.argtypes = [P, P, i64]
     L.oracle_bf16_to_f32.argtypes = [P, P, i64]
     L.oracle_route_topk.argtypes = [P, i32, i32, i32, i32, P, P]
@@ -284,6 +286,11 @@ def combine(o_rows, route_row, w, tokens):
     _check(lib().oracle_combine(_p(o_rows), _p(route_row), _p(w), k, H, _p(tokens), tokens.size,
                                 _p(y)), "combine")
     return y
+
+
+def set_threads(n: int) -> int:
+    """Threads of the oracle's parallel loops (n <= 0 leaves them); returns the count in use."""
+    return int(lib().oracle_set_threads(n))
 
 
 def moe_layer(logits, x_f32, pool, slot_bytes: int, slot_of, H: int, FF: int, fmt: int,

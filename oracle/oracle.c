@@ -28,6 +28,7 @@
  * No routine is "parity unpinned".
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -668,4 +669,13 @@ int oracle_combine(const double* o_rows, const int32_t* route_row, const float* 
         }
     }
     return ORA_OK;
+}
+
+/* ------------------------------------------------------------- threads --
+ * Worker threads of the parallel loops above (for timing the oracle at a
+ * chosen thread count); returns the count that later loops will use. */
+int oracle_set_threads(int32_t n)
+{
+    if (n > 0) omp_set_num_threads(n);
+    return omp_get_max_threads();
 }
