@@ -51,6 +51,8 @@ def lib():
 def _declare(L):
     P = ctypes.c_void_p
     i32, i64, u64 = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64
+    L.oracle_int4_candidates.argtypes = [P, P, P]
+    L.oracle_int4_candidates.restype = None
     L.oracle_set_threads.argtypes = [i32]
     L.oracle_set_threads.restype = ctypes.c_int
     L.oracle_f32_to_bf16.argtypes = [P, P, i64]
@@ -151,6 +153,15 @@ def quantize_int4(w_bf16):
     s = np.empty((N, K // 64), dtype=np.uint16)
     lib().oracle_quantize_int4(_p(w), N, K, _p(q), _p(s))
     return q, s
+
+
+def int4_candidates(group_bf16):
+    """All ten clip candidates of one 64-element group: (bf16 scale bits [10], squared errors [10])."""
+    g = np.ascontiguousarray(group_bf16, dtype=np.uint16).reshape(64)
+    sc = np.zeros(10, np.uint16)
+    er = np.zeros(10, np.float64)
+    lib().oracle_int4_candidates(_p(g), _p(sc), _p(er))
+    return sc, er
 
 
 def blob_layout(fmt: int, H: int, FF: int):

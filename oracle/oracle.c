@@ -379,6 +379,42 @@ static void int4_codes(const float* v, float sc, int32_t* code)
     }
 }
 
+/* Clip candidate i of a 64-element group v with absmax a: its bf16 scale and
+ * its squared error summed in element order (fp64, no FMA). */
+static double int4_candidate(const float* v, float a, int i, uint16_t* sb_out, int32_t* code)
+{
+    const uint16_t sb = f32_to_bf16_bits((a * (float)(20 - i)) / 140.0f);
+    const float sc = bf16_bits_to_f32(sb);
+    int4_codes(v, sc, code);
+    double err = 0.0;
+    for (int c = 0; c < 64; ++c) {
+        double d = (double)v[c] - (double)sc * (double)code[c];
+        err = err + d * d;
+    }
+    *sb_out = sb;
+    return err;
+}
+
+static float group_absmax(const uint16_t* grp, float* v)
+{
+    float a = 0.0f;
+    for (int c = 0; c < 64; ++c) {
+        v[c] = bf16_bits_to_f32(grp[c]);
+        if (fabsf(v[c]) > a) a = fabsf(v[c]);
+    }
+    return a;
+}
+
+/* Every clip candidate of one 64-element group (bf16 bits): scale bits and
+ * squared error of each i = 0..9 (for pinning the candidates that never win). */
+void oracle_int4_candidates(const uint16_t* grp, uint16_t* scales, double* errs)
+{
+    float v[64];
+    int32_t code[64];
+    const float a = group_absmax(grp, v);
+    for (int i = 0; i < 10; ++i) errs[i] = int4_candidate(v, a, i, &scales[i], code);
+}
+
 void oracle_quantize_int4(const uint16_t* w, int32_t N, int32_t K, uint8_t* q, uint16_t* s)
 {
     const int32_t G = K / 64;
@@ -388,22 +424,12 @@ void oracle_quantize_int4(const uint16_t* w, int32_t N, int32_t K, uint8_t* q, u
         int32_t code[64], best_code[64];
         for (int32_t g = 0; g < G; ++g) {
             const uint16_t* grp = w + (int64_t)r * K + (int64_t)g * 64;
-            float a = 0.0f;
-            for (int c = 0; c < 64; ++c) {
-                v[c] = bf16_bits_to_f32(grp[c]);
-                if (fabsf(v[c]) > a) a = fabsf(v[c]);
-            }
+            const float a = group_absmax(grp, v);
             double best_err = 0.0;
             uint16_t best_s = 0;
             for (int i = 0; i < 10; ++i) {
-                uint16_t sb = f32_to_bf16_bits((a * (float)(20 - i)) / 140.0f);
-                float sc = bf16_bits_to_f32(sb);
-                int4_codes(v, sc, code);
-                double err = 0.0;
-                for (int c = 0; c < 64; ++c) {
-                    double d = (double)v[c] - (double)sc * (double)code[c];
-                    err = err + d * d;
-                }
+                uint16_t sb;
+                const double err = int4_candidate(v, a, i, &sb, code);
                 if (i == 0 || err < best_err) {
                     best_err = err;
                     best_s = sb;

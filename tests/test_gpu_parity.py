@@ -354,6 +354,8 @@ def test_quantize_bit_exact_specials(L):
     w[1, :64] = 1e-39                           # subnormal group
     w[2] *= 1e4                                 # large values
     w[3, 5] = 7.0                               # one outlier
+    from test_oracle_quant_ffn import CLIP_065_GROUP
+    w[4, :64] = ora.bf16_to_f32(CLIP_065_GROUP)   # a group whose best clip is alpha = 0.65
     bits = synth.to_bf16_bits(w)
     wd = torch.from_numpy(bits.view(np.int16)).cuda()
     for fmt in (1, 2):
