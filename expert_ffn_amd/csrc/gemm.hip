@@ -165,7 +165,11 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void ffn_int4_gemm_kernel(FfnParam
     uint8_t* xbuf = lds;                                                   // [NSTG][XBUF]
     uint16_t* ssc = reinterpret_cast<uint16_t*>(lds + NSTG * XBUF);        // [NTH][G] bf16 scales of the tile
     int* pre = reinterpret_cast<int*>(lds + NSTG * XBUF + ((NTH * G * 2 + 15) & ~15));   // [E+1]
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, c32 = lane & 31, hh = lane >> 5;
+    // the wave index as a scalar: the LDS DMA copies take wave-derived offsets
+    // in SGPRs and M0, which the compiler must know to be uniform (else each
+    // copy becomes a loop over the lanes' values)
+    const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, c32 = lane & 31,
+              hh = lane >> 5;
     const int mh = wave / NQ, nq = wave % NQ;
 
     // Items per expert -> prefix sums (wave 0).  An expert with at most 64
