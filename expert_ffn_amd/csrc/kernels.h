@@ -87,11 +87,20 @@ FfnWorkspace ffn_workspace(int T, int k, int H, int FF);
 
 // Kernel family per expert group (int4): a group of m_e routes takes the
 // grouped GEMM when m_e > GEMM_GROUP_MIN, else the streaming kernels (which
-// take the routes a few at a time against weights held in registers).  The
-// GEMM family is launched only when T > GEMM_T_MIN (m_e <= T, and at decode
-// sizes its launches would find no work).
-constexpr int GEMM_GROUP_MIN = 16;
-constexpr int GEMM_T_MIN = 64;
+// take the routes 4 at a time against weights held in registers).  The GEMM
+// family is launched only when T > GEMM_T_MIN (m_e <= T, and at decode sizes
+// its launches would find no work).  Measured at the Gemma shape, T = 64 to
+// 1024: thresholds of 32 to 128 routes per group were slower at every size
+// from T = 256 on, and launching the GEMM from T > 32 on took a T = 64 layer
+// with Zipf routing from 179 to 140 us.
+#ifndef GEMM_GROUP_MIN_DEF
+#define GEMM_GROUP_MIN_DEF 16
+#endif
+constexpr int GEMM_GROUP_MIN = GEMM_GROUP_MIN_DEF;
+#ifndef GEMM_T_MIN_DEF
+#define GEMM_T_MIN_DEF 32
+#endif
+constexpr int GEMM_T_MIN = GEMM_GROUP_MIN > GEMM_T_MIN_DEF ? GEMM_GROUP_MIN : GEMM_T_MIN_DEF;
 
 // int4 grouped-GEMM path (large token groups): shape and LDS fit, checked
 // before anything is launched

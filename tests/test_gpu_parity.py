@@ -118,7 +118,7 @@ def test_all_dropped(L):
 
 # -------------------------------------------------- Gemma-shaped layers ----
 G = synth.GEMMA
-GEMM_GROUP_MIN, GEMM_T_MIN = 16, 64     # the library's dispatch thresholds (csrc/kernels.h)
+GEMM_GROUP_MIN, GEMM_T_MIN = 16, 32     # the library's dispatch thresholds (csrc/kernels.h)
 
 
 @pytest.mark.parametrize("T", [1, 4, 16, 64])
