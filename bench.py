@@ -344,23 +344,69 @@ def summarize_pmc(fetch_dir, write_dir, commands):
 
 def summarize_counters(dirs, dest, command, kernels):
     """Per kernel (names containing one of `kernels`), the mean per dispatch of
-    every counter collected by the rocprofv3 --pmc runs under dirs, as a
-    markdown table (derived ratios below it)."""
-    table = {}
+    every counter collected by the rocprofv3 --pmc runs under dirs, and the
+    ratios derived from them, as markdown.  Dispatches shorter than a quarter
+    of the kernel's 90th-percentile duration (launches that found no work)
+    are left out."""
+    import csv
+    import glob
+    disp = {}   # (kernel, run dir, dispatch id) -> {counter: value, "_us": duration}
     for d in dirs:
-        for kname, cname, v in _counter_rows(d):
-            base = kname.split("(")[0].replace("void ", "")
-            for kk in kernels:
-                if kk in base:
-                    table.setdefault(base, {}).setdefault(cname, []).append(v)
-    cols = sorted({c for v in table.values() for c in v})
+        for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            with open(path, newline="") as f:
+                for r in csv.DictReader(f):
+                    base = r["Kernel_Name"].split("(")[0].replace("void ", "")
+                    if not any(kk in base for kk in kernels):
+                        continue
+                    rec = disp.setdefault((base, d, r["Dispatch_Id"]), {})
+                    rec[r["Counter_Name"]] = float(r["Counter_Value"])
+                    rec["_us"] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+    table = {}
+    for (base, _, _), rec in disp.items():
+        table.setdefault(base, []).append(rec)
+    for base, recs in table.items():
+        p90 = np.percentile([r["_us"] for r in recs], 90)
+        table[base] = [r for r in recs if r["_us"] >= 0.25 * p90]
+
+    def mean(recs, c):
+        v = [r[c] for r in recs if c in r]
+        return float(np.mean(v)) if v else float("nan")
+
+    cols = sorted({c for recs in table.values() for r in recs for c in r if c != "_us"})
     lines = ["# rocprofv3 counters per dispatch", "", "Commands (from the repository root):", "", "```",
-             command, "```", "", "| kernel | dispatches | " + " | ".join(cols) + " |",
-             "|---|---|" + "---|" * len(cols)]
-    for name, cv in sorted(table.items()):
-        n = max(len(v) for v in cv.values())
-        vals = [f"{np.mean(cv[c]):.4g}" if c in cv else "" for c in cols]
-        lines.append(f"| `{name[:60]}` | {n} | " + " | ".join(vals) + " |")
+             command, "```", "",
+             "Raw means per dispatch (launches that found no work left out):", "",
+             "| kernel | dispatches | avg us | " + " | ".join(cols) + " |",
+             "|---|---|---|" + "---|" * len(cols)]
+    for name, recs in sorted(table.items()):
+        vals = [f"{mean(recs, c):.4g}" for c in cols]
+        lines.append(f"| `{name[:60]}` | {len(recs)} | {mean(recs, '_us'):.2f} | " + " | ".join(vals) + " |")
+    lines += ["", "Derived (per dispatch; MI355X has 8 XCDs, 256 CUs, 1024 SIMDs):", "",
+              "- cycles = the smaller of GRBM_GUI_ACTIVE / 8 (it counts on every XCD, over a window a few us",
+              "  longer than a short kernel) and duration x 2.4 GHz; window GHz = GRBM_GUI_ACTIVE / 8 / duration;",
+              "- MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x cycles);",
+              "- VALU issue = 4 x SQ_ACTIVE_INST_VALU (quad-cycles, MFMA issue included) / (1024 x cycles);",
+              "- waves/SIMD = 4 x SQ_WAVE_CYCLES (quad-cycles) / (1024 x cycles), the mean resident waves;",
+              "- s_waitcnt share = SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES, wave time spent waiting on a counter;",
+              "- issued TFLOP/s = 512 x SQ_INSTS_VALU_MFMA_MOPS_BF16 / duration (padding included);",
+              "- VALU/MFMA = non-MFMA VALU instructions per MFMA instruction;",
+              "- LDS conflict = SQ_LDS_BANK_CONFLICT / SQ_ACTIVE_INST_LDS.", "",
+              "| kernel | window GHz | MFMA busy | VALU issue | waves/SIMD | s_waitcnt share | issued TFLOP/s | "
+              "VALU/MFMA | LDS conflict |", "|---|---|---|---|---|---|---|---|---|"]
+    for name, recs in sorted(table.items()):
+        us = mean(recs, "_us")
+        win = mean(recs, "GRBM_GUI_ACTIVE") / 8
+        cyc = min(win, us * 2.4e3)
+        simd = 1024 * cyc
+        mf = mean(recs, "SQ_INSTS_MFMA")
+        row = [win / (us * 1e3), mean(recs, "SQ_VALU_MFMA_BUSY_CYCLES") / simd,
+               4 * mean(recs, "SQ_ACTIVE_INST_VALU") / simd, 4 * mean(recs, "SQ_WAVE_CYCLES") / simd,
+               mean(recs, "SQ_WAIT_INST_ANY") / mean(recs, "SQ_WAVE_CYCLES"),
+               512 * mean(recs, "SQ_INSTS_VALU_MFMA_MOPS_BF16") / (us * 1e6),
+               (mean(recs, "SQ_INSTS_VALU") - mf) / mf if mf else float("nan"),
+               mean(recs, "SQ_LDS_BANK_CONFLICT") / mean(recs, "SQ_ACTIVE_INST_LDS")
+               if mean(recs, "SQ_ACTIVE_INST_LDS") else float("nan")]
+        lines.append(f"| `{name[:60]}` | " + " | ".join(f"{v:.3g}" for v in row) + " |")
     with open(dest, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
