@@ -1196,6 +1196,7 @@ def main():
                        mfma_tflops=round(flops / (pms * 1e-3) / 1e12, 1),
                        mfma_frac=round(flops / (pms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
                        hbm_gbs=round(pbytes / (pms * 1e-3) / 1e9, 1),
+                       hbm_frac=round(pbytes / (pms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                        calls_us=callp,
                        roofline=dict(bound="mfma", kernel="ffn_int4_gemm_kernel (moe_ffn_gate_up: prep + GEMM)",
                                      achieved=round(tf(gu_fl, callp["gate_up"]), 1), peak=MFMA_BF16_PEAK_TFLOPS,
