@@ -22,14 +22,20 @@
 // -136 * sum_g s[n][g] * X[m][g].
 //
 // Work items are (expert, route tile, N tile); two workgroups of 4 waves per
-// CU walk the items (one of 8 waves is a build option).  Wave (mh, nq): routes
-// 64 mh .. 64 mh + 63 of the tile (two 32-route blocks) times 64 weight rows
-// (two 32-row blocks).  The K loop runs over 64-groups: a group's activations
+// CU walk the items (one of 8 waves is a build option).  A group of up to 96
+// routes is one route tile, each wave taking all of it (MB = 1 to 3 blocks of
+// 32 routes) times its own 64 weight rows (two 32-row blocks); a larger group
+// takes 128-route tiles, wave (mh, nq) taking routes 64 mh .. 64 mh + 63 times
+// 64 rows.  Each (route block, row block) pair is a chain of 4 MFMAs per
+// 64-group whose partial sum is scaled into the accumulator; with three route
+// blocks this happens block by block, so that only two partial tiles are
+// live.  The K loop runs over 64-groups: a group's activations
 // (a 128-byte piece of each route row of the tile) are copied by LDS DMA two
 // groups ahead into a ring of three stages, whole cache lines per copy, XOR
 // swizzled in LDS; each wave keeps the weights of the next 2*DC groups in flight
 // in registers, one 1 KB load per group and 32 rows from the blob's tiled codes.
 #include <atomic>
+#include <type_traits>
 
 #include "common.h"
 #include "kernels.h"
@@ -50,12 +56,14 @@ __host__ __device__ __forceinline__ int m32_pos(int f) {
 }
 
 constexpr int GM_ROWS = 128;   // routes per narrow tile
-// Groups of at most GEMM_WIDE_MAX routes take wide tiles (64 routes, an N
-// tile twice as wide: half the activation traffic per weight byte); larger
-// ones take 128-route narrow tiles.
+// Groups of at most GEMM_WIDE_MAX routes take one wide tile (all the group's
+// routes, up to three 32-route blocks per wave, and an N tile twice as wide:
+// less activation traffic per weight byte); larger ones take 128-route
+// narrow tiles.
 #ifndef GEMM_WIDE_MAX
 #define GEMM_WIDE_MAX 96
 #endif
+static_assert(GEMM_WIDE_MAX > 64 && GEMM_WIDE_MAX <= 96, "a wide tile holds at most three 32-route blocks per wave");
 constexpr int GM_GBUF = 16384; // one group of a stage: [4 K steps][4 route blocks] x 1 KB
 // A workgroup of NW waves (4 or 8): wave (mh, nq), NQ = NW / 2 column blocks
 // per narrow tile; a stage holds NW / 4 groups.
@@ -146,7 +154,7 @@ __host__ __device__ constexpr int gemm_nstage(int NW) { return NW == 4 ? 3 : 2; 
 
 __host__ __device__ inline size_t gemm_lds_bytes(int E, int G, int NW) {
     return gemm_nstage(NW) * static_cast<size_t>(NW / 4) * GM_GBUF + static_cast<size_t>(64 * NW) * G * 2 + 16 +
-           static_cast<size_t>(E + 1) * 4;
+           static_cast<size_t>(E + 1) * 8;
 }
 
 template <int MODE, int DC, int NW>
@@ -164,7 +172,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void ffn_int4_gemm_kernel(FfnParam
     const int E = P.E, G = S.G, GP = S.GP, NC = S.NC, NT = S.NT;
     uint8_t* xbuf = lds;                                                   // [NSTG][XBUF]
     uint16_t* ssc = reinterpret_cast<uint16_t*>(lds + NSTG * XBUF);        // [NTH][G] bf16 scales of the tile
-    int* pre = reinterpret_cast<int*>(lds + NSTG * XBUF + ((NTH * G * 2 + 15) & ~15));   // [E+1]
+    int* pre = reinterpret_cast<int*>(lds + NSTG * XBUF + ((NTH * G * 2 + 15) & ~15));   // [2][E+1]
     // the wave index as a scalar: the LDS DMA copies take wave-derived offsets
     // in SGPRs and M0, which the compiler must know to be uniform (else each
     // copy becomes a loop over the lanes' values)
@@ -172,31 +180,74 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void ffn_int4_gemm_kernel(FfnParam
               hh = lane >> 5;
     const int mh = wave / NQ, nq = wave % NQ;
 
-    // Items per expert -> prefix sums (wave 0).  An expert with at most 64
-    // routes is one "wide" row tile: the two wave halves take different
-    // columns (an N tile twice as wide), so that both waves of each SIMD work.
-    // Larger groups take 128-route tiles, the halves splitting the routes.
+    // Items: (expert, row tile, N tile).  A group of at most GEMM_WIDE_MAX
+    // routes takes "wide" row tiles of up to 64 routes: every wave takes all
+    // the tile's routes (MB = 1 or 2 blocks of 32), and the four waves take
+    // different columns (an N tile twice as wide as a narrow one).  Larger
+    // groups take 128-route narrow tiles, the two wave halves splitting the
+    // routes (two blocks each).  When those items outnumber the workgroups, a
+    // group of 65 to 96 routes takes one three-block tile instead of two
+    // ("class A": one item of about 1.35 times the time of the others, in
+    // place of two); with fewer items the two tiles run side by side and the
+    // split is faster.  Class-A items are listed first: pre / preB are
+    // per-expert prefix sums of the two classes' item counts (wave 0).
+    // Measured per layer at T = 1024 (gate/up + down): 146 + 87 -> 131 + 79 us
+    // under uniform routing; Zipf routing (few such groups) and T = 128 to 512
+    // unchanged within 3 us.
     const int NTW = MODE == 0 ? (P.FF + 32 * NW - 1) / (32 * NW) : (P.H + 64 * NW - 1) / (64 * NW);
+    int* preB = pre + (E + 1);
+    // items of a group of me routes with 64-route wide tiles (groups of at
+    // most gmin routes are the streaming kernels')
+    auto split_items = [&](int me) {
+        return me <= P.gmin ? 0 : (me <= GEMM_WIDE_MAX ? (me + 63) / 64 * NTW : (me + GM_ROWS - 1) / GM_ROWS * NT);
+    };
     if (wave == 0) {
-        int run = 0;
+        // one round of global loads: the group sizes wait in pre[] for the
+        // second pass, which overwrites each entry after reading it
+        int tot = 0, elig = 0;
         for (int e0 = 0; e0 < E; e0 += 64) {
             const int e = e0 + lane;
             const int me = e < E ? P.offsets[e + 1] - P.offsets[e] : 0;
-            // groups of at most gmin routes are the streaming kernels'
-            const int cnt = me <= P.gmin ? 0 : (me <= GEMM_WIDE_MAX ? (me + 63) / 64 * NTW : (me + GM_ROWS - 1) / GM_ROWS * NT);
-            int incl = cnt;
+            if (e < E) pre[e + 1] = me;
+            int c = split_items(me), ce = me > 64 && me <= GEMM_WIDE_MAX ? c : 0;
 #pragma unroll
             for (int d = 1; d < 64; d <<= 1) {
-                const int o = __shfl_up(incl, d, 64);
-                if (lane >= d) incl += o;
+                c += __shfl_xor(c, d, 64);
+                ce += __shfl_xor(ce, d, 64);
             }
-            if (e < E) pre[e + 1] = run + incl;
-            run += __shfl(incl, 63, 64);
+            tot += c;
+            elig += ce;
         }
-        if (lane == 0) pre[0] = 0;
+        // merge when the split items outnumber the workgroups and the groups
+        // of 65-96 routes hold at least a quarter of them (a few three-block
+        // items among many others lengthen the rounds they fall in)
+        const bool merge = tot > static_cast<int>(gridDim.x) && 4 * elig >= tot;
+        int runA = 0, runB = 0;
+        for (int e0 = 0; e0 < E; e0 += 64) {
+            const int e = e0 + lane;
+            const int me = e < E ? pre[e + 1] : 0;
+            const bool three = merge && me > 64 && me <= GEMM_WIDE_MAX;
+            const int cnt = three ? NTW : split_items(me);
+            int ia = three ? cnt : 0, ib = three ? 0 : cnt;
+#pragma unroll
+            for (int d = 1; d < 64; d <<= 1) {
+                const int oa = __shfl_up(ia, d, 64), ob = __shfl_up(ib, d, 64);
+                if (lane >= d) {
+                    ia += oa;
+                    ib += ob;
+                }
+            }
+            if (e < E) {
+                pre[e + 1] = runA + ia;
+                preB[e + 1] = runB + ib;
+            }
+            runA += __shfl(ia, 63, 64);
+            runB += __shfl(ib, 63, 64);
+        }
+        if (lane == 0) pre[0] = preB[0] = 0;
     }
     __syncthreads();
-    const int nitems = pre[E];
+    const int nA = pre[E], nB = preB[E];
 
     const uint64_t o_codes = MODE == 0 ? P.o13 : P.o2, o_scales = MODE == 0 ? P.os13 : P.os2;
     const int arow_stride = MODE == 0 ? P.H : P.FF;                 // elements per A row
@@ -205,32 +256,54 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void ffn_int4_gemm_kernel(FfnParam
     const int asum_rows = MODE == 0 ? P.T : P.T * P.k;
 
     // XCD-aware order: workgroups are dealt to the 8 XCDs round robin, so the
-    // workgroups of one XCD (blockIdx % 8) take one contiguous eighth of the
-    // item list.  An expert's N tiles then run on one XCD and its activation
-    // rows are fetched into that XCD's L2 once.  (A mapping that differs only
-    // costs locality, not correctness: every item is still taken once.)
+    // workgroups of one XCD (blockIdx % 8) take one contiguous eighth of each
+    // class's item list, class A first.  An expert's N tiles then mostly run
+    // on one XCD and its activation rows are fetched into that XCD's L2 once.
+    // Inside an XCD workgroup j takes position r W + j in round r; for gate/up
+    // with class-A items the odd rounds run backwards (r W + W - 1 - j), so
+    // that the workgroups which started with a class-A item take their next
+    // item last (measured: 133 -> 126 us per gate/up layer at T = 1024; down,
+    // with 11 N tiles per expert and nearly 3 items per workgroup, is 2.5 us
+    // faster without it, and so is gate/up without class-A items).
+    // (A mapping of workgroups to XCDs that differs only costs locality: every
+    // item is still taken once.)
     const int nxcd = gridDim.x % 8 == 0 ? 8 : 1;
     const int xcd = blockIdx.x % nxcd, wpx = gridDim.x / nxcd, wj = blockIdx.x / nxcd;
-    const int ibeg = static_cast<int>(static_cast<int64_t>(nitems) * xcd / nxcd);
-    const int iend = static_cast<int>(static_cast<int64_t>(nitems) * (xcd + 1) / nxcd);
-    for (int item = ibeg + wj; item < iend; item += wpx) {
-        int lo = 0, hi = E;   // largest e with pre[e] <= item
+    const int a0i = static_cast<int>(static_cast<int64_t>(nA) * xcd / nxcd);
+    const int na = static_cast<int>(static_cast<int64_t>(nA) * (xcd + 1) / nxcd) - a0i;
+    const int b0i = static_cast<int>(static_cast<int64_t>(nB) * xcd / nxcd);
+    const int nmine = na + static_cast<int>(static_cast<int64_t>(nB) * (xcd + 1) / nxcd) - b0i;
+    const bool snake = MODE == 0 && nA > 0;
+    // One item at list position pos.  MBC = the route blocks its K loop
+    // computes: 3 for class A; 2 for class B, where a group of at most 32
+    // routes computes a second block of zero rows.  The two classes are two
+    // inlined copies of the whole item, run one after the other, so that
+    // no large state is live across a branch between K loops (with the
+    // choice made per item, the register allocator spilled).
+    auto do_item = [&](auto mbc, int pos) {
+        constexpr int MBC = decltype(mbc)::value;
+        constexpr bool inA = MBC == 3;
+        const int item = inA ? a0i + pos : b0i + pos - na;
+        const int* pc = inA ? pre : preB;
+        int lo = 0, hi = E;   // largest e with pc[e] <= item
         while (hi - lo > 1) {
             const int mid = (lo + hi) >> 1;
-            if (pre[mid] <= item) lo = mid; else hi = mid;
+            if (pc[mid] <= item) lo = mid; else hi = mid;
         }
-        const int e = lo, li = item - pre[e];
-        const bool wide = P.offsets[e + 1] - P.offsets[e] <= GEMM_WIDE_MAX;
+        const int e = lo, li = item - pc[e];
+        const int me = P.offsets[e + 1] - P.offsets[e];
+        const bool wide = me <= GEMM_WIDE_MAX;
         const int nw = wide ? 2 : 1;                        // N tile width in narrow tiles
-        const int ntl = wide ? NTW : NT, rows = wide ? 64 : GM_ROWS;
+        const int ntl = wide ? NTW : NT;
         const int mt = li / ntl, nt = li - mt * ntl;
+        const int rows = wide ? (inA ? 96 : 64) : GM_ROWS;  // route rows of the tile
         const int beg = P.offsets[e] + rows * mt;
         const int end = min(P.offsets[e + 1], beg + rows);
+        const int MB = inA ? 3 : (wide ? (end - beg + 31) / 32 : 2);   // route blocks of each wave (uniform)
         const uint8_t* blob = P.pool + static_cast<uint64_t>(P.slot_of[e]) * P.slot_bytes;
         const int n0 = (MODE == 0 ? 32 * NQ : 64 * NQ) * nw * nt;
         const int nsub = wide ? wave : nq;                  // this wave's column block of the tile
         const int mbase = wide ? 0 : 64 * mh;               // this wave's first route row of the tile
-
         // ---- scales of the tile's 256 rows -> LDS (16-byte copies; rows past the matrix read as 0)
         {
             const uint8_t* sblk = blob + o_scales;
@@ -278,15 +351,15 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void ffn_int4_gemm_kernel(FfnParam
         const uint8_t* wp1 = blob + o_codes + int4_code_off(wrow[1], G, 16 * hh);
         // Register staging (8-wave workgroups): a stage is [group][K step s]
         // [route block] 1 KB fragment blocks; wave w copies (group gi, K step s) =
-        // (w >> 2, w & 3) of the 4 route blocks.  Rows past the tile (and blocks
-        // 2, 3 of a wide tile) read zeros without a memory access.
+        // (w >> 2, w & 3) of the 4 route blocks.  Rows past the group read zeros
+        // without a memory access.
         const int sgi = wave >> 2, ss = wave & 3;
         const rsrc_t ares = make_rsrc(abase, static_cast<uint32_t>(asum_rows) * arow_stride * 2);
         uint32_t aoff[4];
 #pragma unroll
         for (int mb4 = 0; mb4 < 4; ++mb4) {
             const int p = beg + 32 * mb4 + c32;
-            const bool ok = p < end && (!wide || mb4 < 2);
+            const bool ok = p < end;
             const int r = ok ? (MODE == 0 ? P.sorted_route[p] / P.k : p) : 0;
             aoff[mb4] = ok ? static_cast<uint32_t>((r * arow_stride + 16 * ss + 8 * hh) * 2) : NO_LANE;
         }
@@ -301,7 +374,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void ffn_int4_gemm_kernel(FfnParam
         for (int i = 0; i < 4; ++i) {
             const int R = 32 * (wave & 3) + 8 * i + (lane >> 3);
             const int p = beg + R;
-            const bool ok = p < end && (!wide || R < 64);
+            const bool ok = p < end;
             const int r = ok ? (MODE == 0 ? P.sorted_route[p] / P.k : p) : 0;
             const int j = (lane & 7) ^ ((lane >> 3) & 7) ^ i;
             adm[i] = ok ? static_cast<uint32_t>((r * arow_stride + 8 * j) * 2) : NO_LANE;
@@ -350,10 +423,13 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void ffn_int4_gemm_kernel(FfnParam
         __syncthreads();   // scales (and stage 0) in LDS
 
         // ---- bias of the expanded codes: acc = -136 * sum_g X[m][g] s[n][g]
-        f32x16 acc[2][2];
+        // (acc[mb][nb] for the wave's MB route blocks; the group sums of all
+        // MBC blocks are loaded from clamped rows, the MFMAs run for mb < MB)
+        f32x16 acc[MBC][2];
         {
             const f32x16 z = {};
-            f32x16 corr[2][2] = {{z, z}, {z, z}};
+#pragma unroll
+            for (int mb = 0; mb < MBC; ++mb) acc[mb][0] = acc[mb][1] = z;
             for (int t = 0; t < GP / 16; ++t) {
                 u32x4 bs[2];
 #pragma unroll
@@ -366,31 +442,38 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void ffn_int4_gemm_kernel(FfnParam
                         bs[nb][j] = a | (b << 16);
                     }
                 }
+                u32x4 ah[MBC], al[MBC];
 #pragma unroll
-                for (int mb = 0; mb < 2; ++mb) {
+                for (int mb = 0; mb < MBC; ++mb) {
                     const int p = min(beg + mbase + 32 * mb + c32, end - 1);
                     const int r = MODE == 0 ? P.sorted_route[p] / P.k : p;
                     const uint16_t* sh = asum + static_cast<int64_t>(r) * GP + 16 * t + 8 * hh;
                     const uint16_t* sl = sh + static_cast<int64_t>(asum_rows) * GP;
-                    u32x4 ah = *reinterpret_cast<const u32x4*>(sh), al = *reinterpret_cast<const u32x4*>(sl);
+                    ah[mb] = *reinterpret_cast<const u32x4*>(sh);
+                    al[mb] = *reinterpret_cast<const u32x4*>(sl);
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {   // groups past G: zero (the padding is not trusted)
                         const int g0 = 16 * t + 8 * hh + 2 * j;
                         const uint32_t m = g0 >= G ? 0u : (g0 + 1 >= G ? 0x0000FFFFu : 0xFFFFFFFFu);
-                        ah[j] &= m;
-                        al[j] &= m;
+                        ah[mb][j] &= m;
+                        al[mb][j] &= m;
                     }
+                }
 #pragma unroll
-                    for (int nb = 0; nb < 2; ++nb) {
-                        corr[mb][nb] = mfma32(ah, bs[nb], corr[mb][nb]);
-                        corr[mb][nb] = mfma32(al, bs[nb], corr[mb][nb]);
+                for (int mb = 0; mb < MBC; ++mb) {
+                    if (mb < MB) {
+#pragma unroll
+                        for (int nb = 0; nb < 2; ++nb) {
+                            acc[mb][nb] = mfma32(ah[mb], bs[nb], acc[mb][nb]);
+                            acc[mb][nb] = mfma32(al[mb], bs[nb], acc[mb][nb]);
+                        }
                     }
                 }
             }
 #pragma unroll
-            for (int mb = 0; mb < 2; ++mb)
+            for (int mb = 0; mb < MBC; ++mb)
 #pragma unroll
-                for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = corr[mb][nb] * -136.0f;
+                for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = acc[mb][nb] * -136.0f;
         }
         if (XD) {
             // stage 0, weight group D - 2, stage 1, weight group D - 1: the
@@ -409,95 +492,131 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void ffn_int4_gemm_kernel(FfnParam
             fill(D - 1);
         }
 
-        // ---- K loop: U chunks per unrolled body
-        const int ncu = (NC + U - 1) / U * U;
+        // ---- K loop, U chunks per unrolled body, for MBC route blocks
         int bcur = 0;   // LDS DMA ring: the buffer of stage c is c % 3
-        for (int c0 = 0; c0 < ncu; c0 += U) {
+        auto kloop = [&](auto) {
+            const int ncu = (NC + U - 1) / U * U;
+            for (int c0 = 0; c0 < ncu; c0 += U) {
 #pragma unroll
-            for (int cu = 0; cu < U; ++cu) {
-                const int c = c0 + cu;
-                const uint8_t* xb = xbuf + (XD ? bcur : (cu & 1)) * XBUF;
-                if (XD) {
-                    // Stage c was requested two chunks ago; after it this wave
-                    // issued 8 vector-memory operations (the 2 weight loads of
-                    // that chunk, stage c + 1's 4 copies, the next 2 weight
-                    // loads; likewise in the prologue), so vmcnt <= 8 means its
-                    // copies have landed.  The barrier makes that true for every
-                    // wave, and also ends the reads of stage c - 1, whose buffer
-                    // stage c + 2 now takes.  (The compiler does not track LDS DMA
-                    // completion itself.)
-                    __builtin_amdgcn_s_waitcnt(0x0F78);   // vmcnt(8), lgkm/exp not waited
-                    __builtin_amdgcn_s_barrier();
-                    dma_stage(min(c + 2, NC - 1), bcur == 0 ? 2 : bcur - 1);
-                } else {
-                    // stage c + 1 (loaded one chunk ago) into the other buffer, whose
-                    // readers finished at the last barrier; then start stage c + 2,
-                    // ahead of this chunk's weight loads so that the in-order load
-                    // counter never makes a wait cover weights needed later
-                    store_stage((cu + 1) & 1, xr);
-                    load_stage(min(c + 2, NC - 1), xr);
-                }
-                __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                for (int gi = 0; gi < SG; ++gi) {
-                    const int g = SG * c + gi;
-                    const int slot = (SG * cu + gi) % D;
-                    if (nact && mact && g < G) {
-                        // K steps software-pipelined: the next step's activation
-                        // fragments are read and its weights expanded while this
-                        // step's MFMAs run
-                        const int mblk = wide ? 0 : 2 * mh;
-                        const uint8_t* xa = XD ? xb + mblk * 4096 : xb + (gi * 16 + mblk) * 1024 + lane * 16;
-                        const float sc0 = bf16_to_f32(ssc[lrow[0] * G + g]), sc1 = bf16_to_f32(ssc[lrow[1] * G + g]);
-                        f32x16 part[2][2];
-                        u32x4 a0 = *reinterpret_cast<const u32x4*>(xa + (XD ? aro[0] : 0));
-                        u32x4 a1 = *reinterpret_cast<const u32x4*>(xa + (XD ? aro[0] + 4096 : 1024));
-                        u32x4 b0 = deq_int4(wr[slot][0][0]), b1 = deq_int4(wr[slot][1][0]);
-#pragma unroll
-                        for (int s = 0; s < 4; ++s) {
-                            u32x4 na0, na1, nb0, nb1;
-                            if (s < 3) {
-                                na0 = *reinterpret_cast<const u32x4*>(xa + (XD ? aro[s + 1] : (s + 1) * 4096));
-                                na1 = *reinterpret_cast<const u32x4*>(xa + (XD ? aro[s + 1] + 4096 : (s + 1) * 4096 + 1024));
-                            }
-                            if (s == 0) {
-                                const f32x16 z = {};
-                                part[0][0] = mfma32(a0, b0, z);
-                                part[0][1] = mfma32(a0, b1, z);
-                                part[1][0] = mfma32(a1, b0, z);
-                                part[1][1] = mfma32(a1, b1, z);
-                            } else {
-                                part[0][0] = mfma32(a0, b0, part[0][0]);
-                                part[0][1] = mfma32(a0, b1, part[0][1]);
-                                part[1][0] = mfma32(a1, b0, part[1][0]);
-                                part[1][1] = mfma32(a1, b1, part[1][1]);
-                            }
-                            if (s < 3) {
-                                nb0 = deq_int4(wr[slot][0][s + 1]);
-                                nb1 = deq_int4(wr[slot][1][s + 1]);
-                                a0 = na0;
-                                a1 = na1;
-                                b0 = nb0;
-                                b1 = nb1;
-                            }
-                        }
-#pragma unroll
-                        for (int mb = 0; mb < 2; ++mb) {
-                            acc[mb][0] += sc0 * part[mb][0];
-                            acc[mb][1] += sc1 * part[mb][1];
-                        }
+                for (int cu = 0; cu < U; ++cu) {
+                    const int c = c0 + cu;
+                    const uint8_t* xb = xbuf + (XD ? bcur : (cu & 1)) * XBUF;
+                    if (XD) {
+                        // Stage c was requested two chunks ago; after it this wave
+                        // issued 8 vector-memory operations (the 2 weight loads of
+                        // that chunk, stage c + 1's 4 copies, the next 2 weight
+                        // loads; likewise in the prologue), so vmcnt <= 8 means its
+                        // copies have landed.  The barrier makes that true for every
+                        // wave, and also ends the reads of stage c - 1, whose buffer
+                        // stage c + 2 now takes.  (The compiler does not track LDS DMA
+                        // completion itself.)
+                        __builtin_amdgcn_s_waitcnt(0x0F78);   // vmcnt(8), lgkm/exp not waited
+                        __builtin_amdgcn_s_barrier();
+                        dma_stage(min(c + 2, NC - 1), bcur == 0 ? 2 : bcur - 1);
+                    } else {
+                        // stage c + 1 (loaded one chunk ago) into the other buffer, whose
+                        // readers finished at the last barrier; then start stage c + 2,
+                        // ahead of this chunk's weight loads so that the in-order load
+                        // counter never makes a wait cover weights needed later
+                        store_stage((cu + 1) & 1, xr);
+                        load_stage(min(c + 2, NC - 1), xr);
                     }
-                    // refill the slot with group g + D (past the end: the last group again)
-                    const int gn = min(g + D, G - 1);
-                    wr[slot][0] = *reinterpret_cast<const u32x4*>(wp0 + 1024 * gn);
-                    wr[slot][1] = *reinterpret_cast<const u32x4*>(wp1 + 1024 * gn);
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int gi = 0; gi < SG; ++gi) {
+                        const int g = SG * c + gi;
+                        const int slot = (SG * cu + gi) % D;
+                        if (nact && mact && g < G) {
+                            const int mblk = wide ? 0 : 2 * mh;
+                            const uint8_t* xa = XD ? xb + mblk * 4096 : xb + (gi * 16 + mblk) * 1024 + lane * 16;
+                            const float sc0 = bf16_to_f32(ssc[lrow[0] * G + g]), sc1 = bf16_to_f32(ssc[lrow[1] * G + g]);
+                            if constexpr (MBC == 2) {
+                                // two route blocks: all four chains per K step, the next
+                                // step's activation fragments read and its weights
+                                // expanded while this step's MFMAs run; then the scaling
+                                f32x16 part[2][2];
+                                u32x4 a0 = *reinterpret_cast<const u32x4*>(xa + (XD ? aro[0] : 0));
+                                u32x4 a1 = *reinterpret_cast<const u32x4*>(xa + (XD ? aro[0] + 4096 : 1024));
+                                u32x4 b0 = deq_int4(wr[slot][0][0]), b1 = deq_int4(wr[slot][1][0]);
+#pragma unroll
+                                for (int s = 0; s < 4; ++s) {
+                                    u32x4 na0, na1, nb0, nb1;
+                                    if (s < 3) {
+                                        na0 = *reinterpret_cast<const u32x4*>(xa + (XD ? aro[s + 1] : (s + 1) * 4096));
+                                        na1 = *reinterpret_cast<const u32x4*>(xa + (XD ? aro[s + 1] + 4096 : (s + 1) * 4096 + 1024));
+                                    }
+                                    if (s == 0) {
+                                        const f32x16 z = {};
+                                        part[0][0] = mfma32(a0, b0, z);
+                                        part[0][1] = mfma32(a0, b1, z);
+                                        part[1][0] = mfma32(a1, b0, z);
+                                        part[1][1] = mfma32(a1, b1, z);
+                                    } else {
+                                        part[0][0] = mfma32(a0, b0, part[0][0]);
+                                        part[0][1] = mfma32(a0, b1, part[0][1]);
+                                        part[1][0] = mfma32(a1, b0, part[1][0]);
+                                        part[1][1] = mfma32(a1, b1, part[1][1]);
+                                    }
+                                    if (s < 3) {
+                                        nb0 = deq_int4(wr[slot][0][s + 1]);
+                                        nb1 = deq_int4(wr[slot][1][s + 1]);
+                                        a0 = na0;
+                                        a1 = na1;
+                                        b0 = nb0;
+                                        b1 = nb1;
+                                    }
+                                }
+#pragma unroll
+                                for (int mb = 0; mb < 2; ++mb) {
+                                    acc[mb][0] += sc0 * part[mb][0];
+                                    acc[mb][1] += sc1 * part[mb][1];
+                                }
+                            } else {
+                                // three route blocks: the group's weights expanded once,
+                                // then per block two chains of 4 MFMAs scaled into the
+                                // accumulators as soon as they end
+                                u32x4 bq[2][4];
+    #pragma unroll
+                                for (int s = 0; s < 4; ++s) {
+                                    bq[0][s] = deq_int4(wr[slot][0][s]);
+                                    bq[1][s] = deq_int4(wr[slot][1][s]);
+                                }
+    #pragma unroll
+                                for (int mb = 0; mb < MBC; ++mb) {
+                                    // fragment (route block mb, K step s)
+                                    auto afrag = [&](int s) {
+                                        return *reinterpret_cast<const u32x4*>(
+                                            XD ? xa + mb * 4096 + aro[s] : xa + s * 4096 + mb * 1024);
+                                    };
+                                    u32x4 a = afrag(0);
+                                    const f32x16 z = {};
+                                    f32x16 p0 = z, p1 = z;
+    #pragma unroll
+                                    for (int s = 0; s < 4; ++s) {
+                                        u32x4 na;
+                                        if (s < 3) na = afrag(s + 1);
+                                        p0 = mfma32(a, bq[0][s], p0);
+                                        p1 = mfma32(a, bq[1][s], p1);
+                                        if (s < 3) a = na;
+                                    }
+                                    acc[mb][0] += sc0 * p0;
+                                    acc[mb][1] += sc1 * p1;
+                                }
+                            }
+                        }
+                        // refill the slot with group g + D (past the end: the last group again)
+                        const int gn = min(g + D, G - 1);
+                        wr[slot][0] = *reinterpret_cast<const u32x4*>(wp0 + 1024 * gn);
+                        wr[slot][1] = *reinterpret_cast<const u32x4*>(wp1 + 1024 * gn);
+                    }
+                    if (XD)
+                        bcur = bcur == 2 ? 0 : bcur + 1;
+                    else
+                        __syncthreads();
                 }
-                if (XD)
-                    bcur = bcur == 2 ? 0 : bcur + 1;
-                else
-                    __syncthreads();
             }
-        }
+        };
+        kloop(mbc);
         if (XD) {
             // every copy into the ring has landed before the epilogue reuses it
             __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
@@ -506,37 +625,46 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void ffn_int4_gemm_kernel(FfnParam
 
         // ---- epilogue
         if (MODE == 0) {
-            // [128 / nw routes][128 nw columns] bf16, M32 order inside each 64-group
+            // [tile rows][128 nw columns] bf16, M32 order inside each 64-group;
+            // tile rows: 32 MB (wide) or 128 (narrow)
             uint16_t* tile = reinterpret_cast<uint16_t*>(xbuf);
-            const int tw = 32 * NQ * nw;
+            const int tw = 32 * NQ * nw, trows = wide ? 32 * MB : GM_ROWS;
             if (nact && mact) {
 #pragma unroll
-                for (int mb = 0; mb < 2; ++mb)
+                for (int mb = 0; mb < MBC; ++mb) {
+                    if (mb < MB) {
 #pragma unroll
-                    for (int v = 0; v < 16; ++v) {
-                        const int r = mbase + 32 * mb + 8 * (v >> 2) + 4 * hh + (v & 3);
-                        const int col = 32 * nsub + c32;
-                        const float hv = act_fn(P.act, acc[mb][0][v]) * acc[mb][1][v];
-                        tile[r * tw + 64 * (col >> 6) + m32_pos(col & 63)] = f32_to_bf16(hv);
+                        for (int v = 0; v < 16; ++v) {
+                            const int r = mbase + 32 * mb + 8 * (v >> 2) + 4 * hh + (v & 3);
+                            const int col = 32 * nsub + c32;
+                            const float hv = act_fn(P.act, acc[mb][0][v]) * acc[mb][1][v];
+                            tile[r * tw + 64 * (col >> 6) + m32_pos(col & 63)] = f32_to_bf16(hv);
+                        }
                     }
+                }
             }
             __syncthreads();
             const int ncol = min(tw, P.FF - n0);
-            for (int i = tid; i < 512 * NQ; i += NTH) {   // (128 / nw rows) x (tw / 8 blocks)
-                const int r = i / (4 * NQ * nw), c8 = i - r * (4 * NQ * nw);
+            for (int i = tid; i < trows * (tw / 8); i += NTH) {   // trows x (tw / 8 blocks)
+                const int r = i / (tw / 8), c8 = i - r * (tw / 8);
                 if (beg + r < end && 8 * c8 < ncol)
                     *reinterpret_cast<u32x4*>(P.h + static_cast<int64_t>(beg + r) * P.FF + n0 + 8 * c8) =
                         *reinterpret_cast<const u32x4*>(tile + r * tw + 8 * c8);
             }
-            {
-                // group sums of the stored h: 2 threads per (route row, 64-group)
-                const int pr = tid >> 1, hf = tid & 1, r = pr / (NQ * nw / 2), gg = pr - r * (NQ * nw / 2);
+            // group sums of the stored h: 2 threads (adjacent lanes) per (route
+            // row, 64-group); trows * tw / 32 is a multiple of 64, so every
+            // wave runs the same number of passes
+            for (int i0 = 0; i0 < trows * (tw / 32); i0 += NTH) {
+                const int i = i0 + tid;
+                const int pr = i >> 1, hf = i & 1, r = pr / (tw / 64), gg = pr - r * (tw / 64);
                 float sum = 0.0f;
-                const uint16_t* src = tile + r * tw + 64 * gg + 32 * hf;
+                if (r < trows) {
+                    const uint16_t* src = tile + r * tw + 64 * gg + 32 * hf;
 #pragma unroll
-                for (int j = 0; j < 32; ++j) sum += bf16_to_f32(src[j]);
+                    for (int j = 0; j < 32; ++j) sum += bf16_to_f32(src[j]);
+                }
                 sum += __shfl_xor(sum, 1, 64);
-                if (hf == 0 && beg + r < end && 64 * gg < ncol) {
+                if (hf == 0 && r < trows && beg + r < end && 64 * gg < ncol) {
                     const int G2 = P.FF / 64, GP2 = (G2 + 15) & ~15, R = P.T * P.k;
                     const uint16_t shi = f32_to_bf16(sum);
                     const int gidx = n0 / 64 + gg;
@@ -546,23 +674,39 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void ffn_int4_gemm_kernel(FfnParam
             }
         } else if (nact && mact) {
 #pragma unroll
-            for (int mb = 0; mb < 2; ++mb)
+            for (int mb = 0; mb < MBC; ++mb) {
+                if (mb < MB) {
 #pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    const int p = beg + mbase + 32 * mb + 8 * (v >> 2) + 4 * hh + (v & 3);
-                    if (p < end) {
+                    for (int v = 0; v < 16; ++v) {
+                        const int p = beg + mbase + 32 * mb + 8 * (v >> 2) + 4 * hh + (v & 3);
+                        if (p < end) {
 #pragma unroll
-                        for (int nb = 0; nb < 2; ++nb) {
-                            const int64_t o = static_cast<int64_t>(p) * P.H + n0 + 64 * nsub + 32 * nb + c32;
-                            if (P.out_dt == F32)
-                                static_cast<float*>(P.out)[o] = acc[mb][nb][v];
-                            else
-                                static_cast<uint16_t*>(P.out)[o] = f32_to_bf16(acc[mb][nb][v]);
+                            for (int nb = 0; nb < 2; ++nb) {
+                                const int64_t o = static_cast<int64_t>(p) * P.H + n0 + 64 * nsub + 32 * nb + c32;
+                                if (P.out_dt == F32)
+                                    static_cast<float*>(P.out)[o] = acc[mb][nb][v];
+                                else
+                                    static_cast<uint16_t*>(P.out)[o] = f32_to_bf16(acc[mb][nb][v]);
+                            }
                         }
                     }
                 }
+            }
         }
         __syncthreads();   // LDS is rewritten by the next item
+    };
+    // class-A positions come first in every workgroup's sequence (a
+    // workgroup's positions grow with the round)
+    int rnd = 0;
+    for (;; ++rnd) {
+        const int pos = rnd * wpx + ((snake && (rnd & 1)) ? wpx - 1 - wj : wj);
+        if (pos >= na) break;
+        do_item(std::integral_constant<int, 3>{}, pos);
+    }
+    for (;; ++rnd) {
+        const int pos = rnd * wpx + ((snake && (rnd & 1)) ? wpx - 1 - wj : wj);
+        if (pos >= nmine) break;   // every later round's positions are larger
+        do_item(std::integral_constant<int, 2>{}, pos);
     }
 }
 
@@ -600,7 +744,7 @@ hipError_t launch_int4_gemm(const FfnParams& P0, int phases, hipStream_t s) {
     if (err != hipSuccess) return err;
     if ((err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return err;
     const int maxlds = max_lds_bytes();
-    constexpr int DC0 = 2, DC1 = 3, NW = GEMM_NW;   // weight prefetch depth (2 DC groups) per half
+    constexpr int DC0 = 2, DC1 = 2, NW = GEMM_NW;   // weight prefetch depth (2 DC groups) per half
     // persistent: 8 waves per CU, as one workgroup of 8 or two of 4 (which then
     // run out of step with each other)
     const dim3 grid(static_cast<uint32_t>(cus * (8 / NW))), block(64 * NW);
