@@ -830,7 +830,10 @@ __global__ __launch_bounds__(256) void gate_up_int4_dec_kernel(FfnParams P) {
         sa[tt] = *reinterpret_cast<const u32x4*>(srow + 4 * (8 * q < ng ? q : 0));
         const uint8_t* a_lane = blob + P.o13 + int4_code_off(row, G, k0 / 2 + 16 * q);   // tiled: double step i 2 KB further
 #pragma unroll
-        for (int i = 0; i < NDW; ++i) a[tt][i] = *reinterpret_cast<const u32x4*>(a_lane + 2048 * min(i, nds - 1));
+        for (int i = 0; i < NDW; ++i) {
+            a[tt][i] = *reinterpret_cast<const u32x4*>(a_lane + 2048 * min(i, nds - 1));
+            __builtin_amdgcn_sched_barrier(0);   // issue order = order of use
+        }
     }
 
     for (int i = tid; i < 2 * GUD_RT * GS; i += 256) xsum[i] = 0;
@@ -990,19 +993,11 @@ __global__ __launch_bounds__(256) void down_int4_dec_kernel(FfnParams P) {
     const int nr0 = min(RT, end - beg);
     load_h(beg, nr0);
 
-    // weights of the wave's TPW tiles of 16 rows, and their scales
+    // the scales of the wave's TPW tiles of 16 rows (needed in LDS before any
+    // MFMA), then the weights in the order of use, the tail group last
     u32x4 a[TPW][NDS];
     u32x2 at[TPW];
     float sv[TPW][SPL];
-#pragma unroll
-    for (int tt = 0; tt < TPW; ++tt) {
-        const int arow = m0 + 16 * tt + r;
-        const uint8_t* a_lane = blob + P.o2 + int4_code_off(arow, FF / 64, 16 * q);   // tiled: double step i 2 KB further
-#pragma unroll
-        for (int i = 0; i < NDS; ++i) a[tt][i] = *reinterpret_cast<const u32x4*>(a_lane + 2048 * i);
-        at[tt] = u32x2{0u, 0u};
-        if (TAIL) at[tt] = *reinterpret_cast<const u32x2*>(blob + P.o2 + int4_code_off(arow, FF / 64, 64 * NDS + 8 * q));
-    }
     {
         const uint16_t* sc = reinterpret_cast<const uint16_t*>(blob + P.os2);
 #pragma unroll
@@ -1013,6 +1008,19 @@ __global__ __launch_bounds__(256) void down_int4_dec_kernel(FfnParams P) {
                 const int i = idx / NG, g = idx - i * NG;
                 sv[tt][m] = bf16_to_f32(sc[static_cast<int64_t>(m0 + 16 * tt + i) * NG + g]);
             }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int tt = 0; tt < TPW; ++tt) {
+        const int arow = m0 + 16 * tt + r;
+        const uint8_t* a_lane = blob + P.o2 + int4_code_off(arow, FF / 64, 16 * q);   // tiled: double step i 2 KB further
+#pragma unroll
+        for (int i = 0; i < NDS; ++i) {
+            a[tt][i] = *reinterpret_cast<const u32x4*>(a_lane + 2048 * i);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        at[tt] = u32x2{0u, 0u};
+        if (TAIL) at[tt] = *reinterpret_cast<const u32x2*>(blob + P.o2 + int4_code_off(arow, FF / 64, 64 * NDS + 8 * q));
     }
 
     auto compute_tile = [&](int rt, int nr) {
