@@ -317,19 +317,41 @@ void gate_up_fast_kernel(FfnParams P) {
     const uint8_t* ag_row = blob + P.o13 + static_cast<int64_t>(n0 + r) * rs;
     const uint8_t* au_row = ag_row + static_cast<int64_t>(P.FF) * rs;
 
-    // 1. route of this lane's column (invalid columns read route beg: their D
-    //    column is computed from real data and never stored)
+    // The vector-memory counter retires loads in issue order, so the loads go
+    // out in the order they are needed: the activations (they sit in L2 and
+    // arrive long before the weights), then every weight fragment of the
+    // wave's K range in the order of use, then the int8 row scales.
+    // 1. the tile's 16 route indices by uniform (scalar) loads, read before
+    //    any store; column r is route beg + r (columns past the group repeat
+    //    the last route: computed from real data and never stored)
     const int p = beg + r;
     const bool valid = p < end;
-    const int route = P.sorted_route[valid ? p : beg];
-    // 2. every weight fragment of this wave's K range
+    int route;
+    {
+        int rt[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) rt[i] = P.sorted_route[min(beg + i, end - 1)];
+        route = rt[0];
+#pragma unroll
+        for (int i = 1; i < 16; ++i) route = r == i ? rt[i] : route;
+    }
+    // 2. activations, D steps ahead of the MFMAs
+    const uint16_t* xrow = P.xq + static_cast<int64_t>(route_token(route, P.kmul, P.k)) * P.H;
+    u32x4 b[D][MF];
+#pragma unroll
+    for (int g = 0; g < D; ++g)
+#pragma unroll
+        for (int m = 0; m < MF; ++m) b[g][m] = *reinterpret_cast<const u32x4*>(xrow + b_off<FMT>(s0 + g, q) + 8 * m);
+    __builtin_amdgcn_sched_barrier(0);
+    // 3. the weights
     AF ag[NG], au[NG];
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
         ag[g] = *reinterpret_cast<const AF*>(ag_row + a_off<FMT>(s0 + g, q));
         au[g] = *reinterpret_cast<const AF*>(au_row + a_off<FMT>(s0 + g, q));
+        __builtin_amdgcn_sched_barrier(0);
     }
-    // 3. int8 row scales
+    // 4. int8 row scales
     float* s_red = smem;   // [KSPLIT-1][8][64]
     f32x4 sg_row = {0, 0, 0, 0}, su_row = {0, 0, 0, 0};
     if constexpr (FMT == W_INT8) {
@@ -337,13 +359,6 @@ void gate_up_fast_kernel(FfnParams P) {
         sg_row = *reinterpret_cast<const f32x4*>(sc + n0 + 4 * q);
         su_row = *reinterpret_cast<const f32x4*>(sc + P.FF + n0 + 4 * q);
     }
-    // 4. activations, D steps ahead of the MFMAs
-    const uint16_t* xrow = P.xq + static_cast<int64_t>(route / P.k) * P.H;
-    u32x4 b[D][MF];
-#pragma unroll
-    for (int g = 0; g < D; ++g)
-#pragma unroll
-        for (int m = 0; m < MF; ++m) b[g][m] = *reinterpret_cast<const u32x4*>(xrow + b_off<FMT>(s0 + g, q) + 8 * m);
     __syncthreads();
 
     const f32x4 zero = {0, 0, 0, 0};
@@ -410,20 +425,26 @@ void down_fast_kernel(FfnParams P) {
 
     const int p = beg + r;
     const bool valid = p < end;
-    AF a[NG];
-#pragma unroll
-    for (int g = 0; g < NG; ++g) a[g] = *reinterpret_cast<const AF*>(a_row + a_off<FMT>(s0 + g, q));
-    float* s_red = smem;   // [3][4][64] when K is split
-    f32x4 s_row = {0, 0, 0, 0};
-    if constexpr (FMT == W_INT8) {
-        s_row = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(blob + P.os2) + m0 + 4 * q);
-    }
+    // loads in the order of need (the in-order vector-memory counter): the h
+    // rows (in L2), then the weights in the order of use, then the row scales
     const uint16_t* hrow = P.h + static_cast<int64_t>(valid ? p : beg) * P.FF;
     u32x4 b[D][MF];
 #pragma unroll
     for (int g = 0; g < D; ++g)
 #pragma unroll
         for (int m = 0; m < MF; ++m) b[g][m] = *reinterpret_cast<const u32x4*>(hrow + b_off<FMT>(s0 + g, q) + 8 * m);
+    __builtin_amdgcn_sched_barrier(0);
+    AF a[NG];
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+        a[g] = *reinterpret_cast<const AF*>(a_row + a_off<FMT>(s0 + g, q));
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    float* s_red = smem;   // [3][4][64] when K is split
+    f32x4 s_row = {0, 0, 0, 0};
+    if constexpr (FMT == W_INT8) {
+        s_row = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(blob + P.os2) + m0 + 4 * q);
+    }
     __syncthreads();
 
     const f32x4 zero = {0, 0, 0, 0};
