@@ -234,7 +234,7 @@ static moe_status ffn_entry(const char* fn, int phases, const void* pool, uint64
                             int32_t act, const void* x, int32_t x_dtype, int32_t T, int32_t k,
                             const int32_t* expert_offsets, const int32_t* sorted_route,
                             void* out_routes, int32_t out_dtype, void* ws, size_t ws_bytes,
-                            void* stream) {
+                            void* stream, bool fork = true) {
     moe_status st = check_ffn_shape(fn, E, H, FF, wfmt, T, k);
     if (st != MOE_OK) return st;
     if (!pool || !slot_of || !expert_offsets || !sorted_route || !ws)
@@ -278,7 +278,7 @@ static moe_status ffn_entry(const char* fn, int phases, const void* pool, uint64
     P.out = out_routes;
     P.out_dt = out_dtype;
     P.o13 = off[0]; P.os13 = off[1]; P.o2 = off[2]; P.os2 = off[3];
-    return hip_status(fn, moe::launch_ffn(P, phases, static_cast<hipStream_t>(stream)));
+    return hip_status(fn, moe::launch_ffn(P, phases, static_cast<hipStream_t>(stream), fork));
 }
 
 #define FFN_ARGS pool, slot_bytes, slot_of, E, H, FF, wfmt, act, x, x_dtype, T, k, expert_offsets, \
@@ -339,8 +339,9 @@ moe_status moe_expert_ffn_noalloc(const void* pool, uint64_t slot_bytes, const i
     void* ws = nullptr;
     const hipError_t e = scratch_address(&ws);
     if (e != hipSuccess) return hip_status(fn, e);
+    // one stream only: a second stream and its events would be created on the first call
     return ffn_entry(fn, 3, pool, slot_bytes, slot_of, E, H, FF, wfmt, act, x, x_dtype, T, k, expert_offsets,
-                     sorted_route, out_routes, out_dtype, ws, MOE_NOALLOC_SCRATCH_BYTES, stream);
+                     sorted_route, out_routes, out_dtype, ws, MOE_NOALLOC_SCRATCH_BYTES, stream, false);
 }
 
 moe_status moe_combine(const void* out_routes, int32_t out_dtype, const float* topk_w,

@@ -28,6 +28,7 @@
 // waves and reduces the partial sums in LDS.  Expert groups with no routes
 // leave their workgroups idle at once.
 #include <climits>
+#include <mutex>
 
 #include "common.h"
 #include "kernels.h"
@@ -1271,15 +1272,71 @@ static void launch_phases(const FfnParams& P, int phases, hipStream_t s) {
     }
 }
 
-hipError_t launch_ffn(const FfnParams& P0, int phases, hipStream_t s) {
+// A second stream per device for the grouped GEMM, with the two events that
+// fork it from and join it back into the caller's stream; created on first
+// use and kept until the process ends.  nullptr if creation failed (the call
+// then runs on one stream).
+namespace {
+struct SideStream {
+    hipStream_t s = nullptr;
+    hipEvent_t fork = nullptr, join = nullptr;
+};
+std::mutex g_side_mu;   // also orders the event records of concurrent calls
+SideStream* side_stream_locked() {
+    static SideStream side[64];
+    static bool tried[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+    if (!tried[dev]) {
+        tried[dev] = true;
+        SideStream t;
+        if (hipStreamCreateWithFlags(&t.s, hipStreamNonBlocking) == hipSuccess &&
+            hipEventCreateWithFlags(&t.fork, hipEventDisableTiming) == hipSuccess &&
+            hipEventCreateWithFlags(&t.join, hipEventDisableTiming) == hipSuccess)
+            side[dev] = t;
+        (void)hipGetLastError();
+    }
+    return side[dev].join ? &side[dev] : nullptr;
+}
+}  // namespace
+
+static hipError_t launch_streaming(FfnParams P, int phases, hipStream_t s);
+
+hipError_t launch_ffn(const FfnParams& P0, int phases, hipStream_t s, bool fork) {
     FfnParams P = P0;
     P.gmin = INT_MAX;
     if (P.fmt == W_INT4 && P.T > GEMM_T_MIN && int4_gemm_eligible(P)) {
-        // per expert group: more than GEMM_GROUP_MIN routes -> grouped GEMM
+        // per expert group: more than GEMM_GROUP_MIN routes -> grouped GEMM,
+        // the rest -> the streaming kernels.  The two families touch disjoint
+        // groups (and disjoint parts of the workspace), so the GEMM runs on a
+        // second stream, forked from s and joined back: at mid-size batches
+        // neither family fills the GPU alone.
         P.gmin = GEMM_GROUP_MIN;
-        const hipError_t err = launch_int4_gemm(P, phases, s);
-        if (err != hipSuccess) return err;
+        std::unique_lock<std::mutex> lk(g_side_mu, std::defer_lock);
+        SideStream* side = nullptr;
+        if (fork) {
+            lk.lock();
+            side = side_stream_locked();
+        }
+        hipError_t err = hipSuccess;
+        if (side) {
+            if ((err = hipEventRecord(side->fork, s)) != hipSuccess) return err;
+            if ((err = hipStreamWaitEvent(side->s, side->fork, 0)) != hipSuccess) return err;
+        }
+        if ((err = launch_int4_gemm(P, phases, side ? side->s : s)) != hipSuccess) return err;
+        err = launch_streaming(P, phases, s);
+        if (side) {
+            const hipError_t e1 = hipEventRecord(side->join, side->s);
+            const hipError_t e2 = hipStreamWaitEvent(s, side->join, 0);
+            if (err == hipSuccess) err = e1 != hipSuccess ? e1 : e2;
+        }
+        return err;
     }
+    return launch_streaming(P, phases, s);
+}
+
+// the streaming kernels of every group that P.gmin leaves them
+static hipError_t launch_streaming(FfnParams P, int phases, hipStream_t s) {
     if ((phases & 1) && P.fmt == W_INT4 && P.H == 2816 && P.FF % (16 * GUD_TPW) == 0) {
         const GudLds L = gud_lds(P.H);
         const dim3 grid(P.FF / 16 / GUD_TPW, P.E);

@@ -107,6 +107,8 @@ constexpr int GEMM_T_MIN = GEMM_GROUP_MIN > GEMM_T_MIN_DEF ? GEMM_GROUP_MIN : GE
 bool int4_gemm_eligible(const FfnParams& p);
 hipError_t launch_int4_gemm(const FfnParams& p, int phases, hipStream_t s);
 
-hipError_t launch_ffn(const FfnParams& p, int phases /*1 gate_up, 2 down, 3 both*/, hipStream_t s);
+// fork: the grouped GEMM may run on a second stream of the device, joined
+// back into s before the call returns (0 for callers that must create nothing)
+hipError_t launch_ffn(const FfnParams& p, int phases /*1 gate_up, 2 down, 3 both*/, hipStream_t s, bool fork);
 
 }  // namespace moe
