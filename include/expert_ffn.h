@@ -22,6 +22,12 @@
  *     the unpack kernel until the stream reaches them).
  *   - stream is a hipStream_t (NULL = the legacy default stream).  Every call
  *     only enqueues work on that stream and returns; nothing synchronises.
+ *     (The int4 expert FFN calls may also run their grouped GEMM on a second
+ *     stream the library keeps per device, created with its two events on the
+ *     first such call: it waits for `stream` through one event and `stream`
+ *     waits for it through the other before the call returns, so the work
+ *     stays ordered on `stream`, and under HIP graph capture it is a fork and
+ *     join inside the captured graph.)
  *   - Arguments are checked on the host before anything is enqueued.  A call
  *     that returns a status other than MOE_OK has enqueued nothing, and
  *     moe_last_error() describes why as "<function>: <what>".  MOE_E_HIP
@@ -259,6 +265,10 @@ moe_status moe_min_weight(const int32_t* topk_ids, const float* topk_w, int32_t 
  * moe_ffn_gate_up and moe_ffn_down are its two halves, for callers that time
  * or schedule them apart: gate_up leaves h in ws, down reads it from there;
  * gate_up ignores out_routes, down ignores x (both accept NULL for them).
+ * int4 weights: each expert group is computed by one of two kernel families
+ * chosen on the device from its size (more than 16 routes, when T > 32: the
+ * grouped MFMA GEMM; otherwise the streaming kernels); the result does not
+ * depend on the stream arrangement above.
  */
 moe_status moe_expert_ffn(const void* pool, uint64_t slot_bytes, const int32_t* slot_of, int32_t E,
                           int32_t H, int32_t FF, int32_t wfmt, int32_t act, const void* x,
