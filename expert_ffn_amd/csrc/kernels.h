@@ -89,12 +89,15 @@ FfnWorkspace ffn_workspace(int T, int k, int H, int FF);
 // grouped GEMM when m_e > GEMM_GROUP_MIN, else the streaming kernels (which
 // take the routes 4 at a time against weights held in registers).  The GEMM
 // family is launched only when T > GEMM_T_MIN (m_e <= T, and at decode sizes
-// its launches would find no work).  Measured at the Gemma shape, T = 64 to
-// 1024: thresholds of 32 to 128 routes per group were slower at every size
-// from T = 256 on, and launching the GEMM from T > 32 on took a T = 64 layer
-// with Zipf routing from 179 to 140 us.
+// its launches would find no work); it runs on a second stream, beside the
+// streaming kernels.  Measured at the Gemma shape, T = 64 to 1024, per layer:
+// with the two families overlapped, 8 beat 16 by 17-27 % at T = 128-256 and by
+// 7 % at T = 1024 with Zipf routing (a group of 9-16 routes is 3-4 sequential
+// route tiles for the streaming kernels); 4 and 6 were no better, and 4 was
+// 4 % slower at T = 1024.  Launching the GEMM from T > 32 rather than T > 64
+// took a T = 64 layer with Zipf routing from 179 to 140 us.
 #ifndef GEMM_GROUP_MIN_DEF
-#define GEMM_GROUP_MIN_DEF 16
+#define GEMM_GROUP_MIN_DEF 8
 #endif
 constexpr int GEMM_GROUP_MIN = GEMM_GROUP_MIN_DEF;
 #ifndef GEMM_T_MIN_DEF

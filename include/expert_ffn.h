@@ -266,7 +266,7 @@ moe_status moe_min_weight(const int32_t* topk_ids, const float* topk_w, int32_t 
  * or schedule them apart: gate_up leaves h in ws, down reads it from there;
  * gate_up ignores out_routes, down ignores x (both accept NULL for them).
  * int4 weights: each expert group is computed by one of two kernel families
- * chosen on the device from its size (more than 16 routes, when T > 32: the
+ * chosen on the device from its size (more than 8 routes, when T > 32: the
  * grouped MFMA GEMM; otherwise the streaming kernels); the result does not
  * depend on the stream arrangement above.
  */

@@ -118,7 +118,7 @@ def test_all_dropped(L):
 
 # -------------------------------------------------- Gemma-shaped layers ----
 G = synth.GEMMA
-GEMM_GROUP_MIN, GEMM_T_MIN = 16, 32     # the library's dispatch thresholds (csrc/kernels.h)
+GEMM_GROUP_MIN, GEMM_T_MIN = 8, 32      # the library's dispatch thresholds (csrc/kernels.h)
 
 
 @pytest.mark.parametrize("T", [1, 4, 16, 64])
@@ -159,7 +159,7 @@ def test_gemma_int4_prefill(L, zipf):
              T=1024, zipf=zipf)
 
 
-# The int4 grouped-GEMM path (groups of more than 16 routes) on small shapes:
+# The int4 grouped-GEMM path (groups of more than 8 routes) on small shapes:
 # partial and multiple 128-route tiles, wide 64-route tiles, odd group counts,
 # ragged N tiles, and calls where both kernel families take groups.
 GEMM_CASES = [
