@@ -154,7 +154,7 @@ __host__ __device__ constexpr int gemm_nstage(int NW) { return NW == 4 ? 3 : 2; 
 
 __host__ __device__ inline size_t gemm_lds_bytes(int E, int G, int NW) {
     return gemm_nstage(NW) * static_cast<size_t>(NW / 4) * GM_GBUF + static_cast<size_t>(64 * NW) * G * 2 + 16 +
-           static_cast<size_t>(E + 1) * 8;
+           static_cast<size_t>(E + 1) * 12;
 }
 
 template <int MODE, int DC, int NW>
@@ -172,7 +172,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void ffn_int4_gemm_kernel(FfnParam
     const int E = P.E, G = S.G, GP = S.GP, NC = S.NC, NT = S.NT;
     uint8_t* xbuf = lds;                                                   // [NSTG][XBUF]
     uint16_t* ssc = reinterpret_cast<uint16_t*>(lds + NSTG * XBUF);        // [NTH][G] bf16 scales of the tile
-    int* pre = reinterpret_cast<int*>(lds + NSTG * XBUF + ((NTH * G * 2 + 15) & ~15));   // [2][E+1]
+    int* pre = reinterpret_cast<int*>(lds + NSTG * XBUF + ((NTH * G * 2 + 15) & ~15));   // [3][E+1]
     // the wave index as a scalar: the LDS DMA copies take wave-derived offsets
     // in SGPRs and M0, which the compiler must know to be uniform (else each
     // copy becomes a loop over the lanes' values)
@@ -189,13 +189,16 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void ffn_int4_gemm_kernel(FfnParam
     // group of 65 to 96 routes takes one three-block tile instead of two
     // ("class A": one item of about 1.35 times the time of the others, in
     // place of two); with fewer items the two tiles run side by side and the
-    // split is faster.  Class-A items are listed first: pre / preB are
-    // per-expert prefix sums of the two classes' item counts (wave 0).
+    // split is faster.  Groups of at most 32 routes are one-block tiles
+    // ("class C", about 0.6 of a two-block item: half the MFMAs and scaling).
+    // Class-A items are listed first, class C last: pre / preB / preC are
+    // per-expert prefix sums of the three classes' item counts (wave 0).
     // Measured per layer at T = 1024 (gate/up + down): 146 + 87 -> 131 + 79 us
     // under uniform routing; Zipf routing (few such groups) and T = 128 to 512
     // unchanged within 3 us.
     const int NTW = MODE == 0 ? (P.FF + 32 * NW - 1) / (32 * NW) : (P.H + 64 * NW - 1) / (64 * NW);
     int* preB = pre + (E + 1);
+    int* preC = pre + 2 * (E + 1);
     // items of a group of me routes with 64-route wide tiles (groups of at
     // most gmin routes are the streaming kernels')
     auto split_items = [&](int me) {
@@ -222,32 +225,35 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void ffn_int4_gemm_kernel(FfnParam
         // of 65-96 routes hold at least a quarter of them (a few three-block
         // items among many others lengthen the rounds they fall in)
         const bool merge = tot > static_cast<int>(gridDim.x) && 4 * elig >= tot;
-        int runA = 0, runB = 0;
+        int runA = 0, runB = 0, runC = 0;
         for (int e0 = 0; e0 < E; e0 += 64) {
             const int e = e0 + lane;
             const int me = e < E ? pre[e + 1] : 0;
-            const bool three = merge && me > 64 && me <= GEMM_WIDE_MAX;
+            const bool three = merge && me > 64 && me <= GEMM_WIDE_MAX, one = me <= 32;
             const int cnt = three ? NTW : split_items(me);
-            int ia = three ? cnt : 0, ib = three ? 0 : cnt;
+            int ia = three ? cnt : 0, ic = one ? cnt : 0, ib = cnt - ia - ic;
 #pragma unroll
             for (int d = 1; d < 64; d <<= 1) {
-                const int oa = __shfl_up(ia, d, 64), ob = __shfl_up(ib, d, 64);
+                const int oa = __shfl_up(ia, d, 64), ob = __shfl_up(ib, d, 64), oc = __shfl_up(ic, d, 64);
                 if (lane >= d) {
                     ia += oa;
                     ib += ob;
+                    ic += oc;
                 }
             }
             if (e < E) {
                 pre[e + 1] = runA + ia;
                 preB[e + 1] = runB + ib;
+                preC[e + 1] = runC + ic;
             }
             runA += __shfl(ia, 63, 64);
             runB += __shfl(ib, 63, 64);
+            runC += __shfl(ic, 63, 64);
         }
-        if (lane == 0) pre[0] = preB[0] = 0;
+        if (lane == 0) pre[0] = preB[0] = preC[0] = 0;
     }
     __syncthreads();
-    const int nA = pre[E], nB = preB[E];
+    const int nA = pre[E], nB = preB[E], nC = preC[E];
 
     const uint64_t o_codes = MODE == 0 ? P.o13 : P.o2, o_scales = MODE == 0 ? P.os13 : P.os2;
     const int arow_stride = MODE == 0 ? P.H : P.FF;                 // elements per A row
@@ -272,19 +278,21 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void ffn_int4_gemm_kernel(FfnParam
     const int a0i = static_cast<int>(static_cast<int64_t>(nA) * xcd / nxcd);
     const int na = static_cast<int>(static_cast<int64_t>(nA) * (xcd + 1) / nxcd) - a0i;
     const int b0i = static_cast<int>(static_cast<int64_t>(nB) * xcd / nxcd);
-    const int nmine = na + static_cast<int>(static_cast<int64_t>(nB) * (xcd + 1) / nxcd) - b0i;
+    const int nb = static_cast<int>(static_cast<int64_t>(nB) * (xcd + 1) / nxcd) - b0i;
+    const int c0i = static_cast<int>(static_cast<int64_t>(nC) * xcd / nxcd);
+    const int nmine = na + nb + static_cast<int>(static_cast<int64_t>(nC) * (xcd + 1) / nxcd) - c0i;
     const bool snake = MODE == 0 && nA > 0;
     // One item at list position pos.  MBC = the route blocks its K loop
-    // computes: 3 for class A; 2 for class B, where a group of at most 32
-    // routes computes a second block of zero rows.  The two classes are two
-    // inlined copies of the whole item, run one after the other, so that
-    // no large state is live across a branch between K loops (with the
-    // choice made per item, the register allocator spilled).
+    // computes: 3 for class A, 2 for class B (a second tile of at most 32
+    // routes computes a second block of zero rows), 1 for class C.  The
+    // classes are three inlined copies of the whole item, run one after the
+    // other, so that no large state is live across a branch between K loops
+    // (with the choice made per item, the register allocator spilled).
     auto do_item = [&](auto mbc, int pos) {
         constexpr int MBC = decltype(mbc)::value;
         constexpr bool inA = MBC == 3;
-        const int item = inA ? a0i + pos : b0i + pos - na;
-        const int* pc = inA ? pre : preB;
+        const int item = inA ? a0i + pos : (MBC == 2 ? b0i + pos - na : c0i + pos - na - nb);
+        const int* pc = inA ? pre : (MBC == 2 ? preB : preC);
         int lo = 0, hi = E;   // largest e with pc[e] <= item
         while (hi - lo > 1) {
             const int mid = (lo + hi) >> 1;
@@ -299,7 +307,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void ffn_int4_gemm_kernel(FfnParam
         const int rows = wide ? (inA ? 96 : 64) : GM_ROWS;  // route rows of the tile
         const int beg = P.offsets[e] + rows * mt;
         const int end = min(P.offsets[e + 1], beg + rows);
-        const int MB = inA ? 3 : (wide ? (end - beg + 31) / 32 : 2);   // route blocks of each wave (uniform)
+        const int MB = MBC == 2 ? (wide ? (end - beg + 31) / 32 : 2) : MBC;   // route blocks of each wave (uniform)
         const uint8_t* blob = P.pool + static_cast<uint64_t>(P.slot_of[e]) * P.slot_bytes;
         const int n0 = (MODE == 0 ? 32 * NQ : 64 * NQ) * nw * nt;
         const int nsub = wide ? wave : nq;                  // this wave's column block of the tile
@@ -695,8 +703,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void ffn_int4_gemm_kernel(FfnParam
         }
         __syncthreads();   // LDS is rewritten by the next item
     };
-    // class-A positions come first in every workgroup's sequence (a
-    // workgroup's positions grow with the round)
+    // the classes' positions come in list order in every workgroup's
+    // sequence (a workgroup's positions grow with the round)
     int rnd = 0;
     for (;; ++rnd) {
         const int pos = rnd * wpx + ((snake && (rnd & 1)) ? wpx - 1 - wj : wj);
@@ -705,8 +713,13 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void ffn_int4_gemm_kernel(FfnParam
     }
     for (;; ++rnd) {
         const int pos = rnd * wpx + ((snake && (rnd & 1)) ? wpx - 1 - wj : wj);
-        if (pos >= nmine) break;   // every later round's positions are larger
+        if (pos >= na + nb) break;
         do_item(std::integral_constant<int, 2>{}, pos);
+    }
+    for (;; ++rnd) {
+        const int pos = rnd * wpx + ((snake && (rnd & 1)) ? wpx - 1 - wj : wj);
+        if (pos >= nmine) break;   // every later round's positions are larger
+        do_item(std::integral_constant<int, 1>{}, pos);
     }
 }
 
