@@ -1,9 +1,12 @@
 """moe_expert_ffn_noalloc (the FFN with the library's static scratch array as
 its workspace) against moe_expert_ffn with a caller workspace, through the C
 ABI: the same kernels run on the same inputs, so the per-route outputs must be
-identical bit for bit.  Two calls in a row on one device, the second with a
-smaller input (the array keeps the first call's contents), then a third
-format; a call too large for the array is rejected before anything runs."""
+identical bit for bit.  (With int4 weights and T > 32 the workspace call runs
+the grouped GEMM on a second stream beside the streaming kernels, the no-alloc
+call runs both on one stream: the comparison also shows that the overlap
+changes no result.)  Calls in a row on one device, each smaller than the one
+before (the array keeps the previous call's contents), then a third format; a
+call too large for the array is rejected before anything runs."""
 import ctypes
 
 import numpy as np
@@ -65,8 +68,10 @@ def test_noalloc_matches_workspace_call():
     need = lib.workspace_bytes(1024, k, E, H, FF, 2)
     assert need <= lib.NOALLOC_SCRATCH_BYTES, need
     pool, sb, slot_d = gemma_layer(lib, 2, 31)
-    # 1024 tokens (grouped GEMM and streaming kernels, most of the array), then 16
+    # 1024 tokens (grouped GEMM and streaming kernels, most of the array), then
+    # 128 with Zipf routing (both families take many groups), then 16
     both_ways(lib, pool, sb, slot_d, 2, 1024, 1.1, 32)
+    both_ways(lib, pool, sb, slot_d, 2, 128, 1.1, 36)
     both_ways(lib, pool, sb, slot_d, 2, 16, None, 33)
     del pool
     pool, sb, slot_d = gemma_layer(lib, 1, 34)
