@@ -22,11 +22,13 @@
 // -136 * sum_g s[n][g] * X[m][g].
 //
 // Work items are (expert, route tile, N tile); two workgroups of 4 waves per
-// CU walk the items (one of 8 waves is a build option).  A group of up to 96
-// routes is one route tile, each wave taking all of it (MB = 1 to 3 blocks of
-// 32 routes) times its own 64 weight rows (two 32-row blocks); a larger group
-// takes 128-route tiles, wave (mh, nq) taking routes 64 mh .. 64 mh + 63 times
-// 64 rows.  Each (route block, row block) pair is a chain of 4 MFMAs per
+// CU walk the items (one of 8 waves is a build option).  A group of up to 64
+// routes is one route tile, each wave taking all of it (one or two blocks of
+// 32 routes) times its own 64 weight rows (two 32-row blocks); a group of 65
+// to 96 routes is one three-block tile when the items outnumber the
+// workgroups, else a 64-route tile and the rest; a larger group takes
+// 128-route tiles, wave (mh, nq) taking routes 64 mh .. 64 mh + 63 times 64
+// rows.  Each (route block, row block) pair is a chain of 4 MFMAs per
 // 64-group whose partial sum is scaled into the accumulator; with three route
 // blocks this happens block by block, so that only two partial tiles are
 // live.  The K loop runs over 64-groups: a group's activations
