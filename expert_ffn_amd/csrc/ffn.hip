@@ -1282,11 +1282,17 @@ struct SideStream {
     hipEvent_t fork = nullptr, join = nullptr;
 };
 std::mutex g_side_mu;   // also orders the event records of concurrent calls
-SideStream* side_stream_locked() {
+SideStream* side_stream_locked(hipStream_t s) {
     static SideStream side[64];
     static bool tried[64];
-    int dev = 0;
+    int dev = 0, sdev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+    // the caller's stream must belong to the current device (the side stream
+    // is that device's); otherwise the call stays on the caller's stream
+    if (hipStreamGetDevice(s, &sdev) != hipSuccess || sdev != dev) {
+        (void)hipGetLastError();
+        return nullptr;
+    }
     if (!tried[dev]) {
         tried[dev] = true;
         SideStream t;
@@ -1316,7 +1322,7 @@ hipError_t launch_ffn(const FfnParams& P0, int phases, hipStream_t s, bool fork)
         SideStream* side = nullptr;
         if (fork) {
             lk.lock();
-            side = side_stream_locked();
+            side = side_stream_locked(s);
         }
         hipError_t err = hipSuccess;
         if (side) {
