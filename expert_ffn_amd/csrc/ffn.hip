@@ -1273,9 +1273,9 @@ static void launch_phases(const FfnParams& P, int phases, hipStream_t s) {
 }
 
 // A second stream per device for the grouped GEMM, with the two events that
-// fork it from and join it back into the caller's stream; created on first
-// use and kept until the process ends.  nullptr if creation failed (the call
-// then runs on one stream).
+// fork it from and join it back into the caller's stream; created on the
+// first use outside graph capture and kept until the process ends.  nullptr
+// before that, or if creation failed (the call then runs on one stream).
 namespace {
 struct SideStream {
     hipStream_t s = nullptr;
@@ -1294,6 +1294,13 @@ SideStream* side_stream_locked(hipStream_t s) {
         return nullptr;
     }
     if (!tried[dev]) {
+        // not while s is being captured into a graph (creating a stream or an
+        // event there is not a stream operation); such a call runs on one stream
+        hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+        if (hipStreamIsCapturing(s, &cap) != hipSuccess || cap != hipStreamCaptureStatusNone) {
+            (void)hipGetLastError();
+            return nullptr;
+        }
         tried[dev] = true;
         SideStream t;
         if (hipStreamCreateWithFlags(&t.s, hipStreamNonBlocking) == hipSuccess &&
