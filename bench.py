@@ -265,13 +265,20 @@ def realised_routing(lib, runner, logits):
 
 
 def kernel_source_hash():
-    """Hash of the sources the gate/up decode kernel is compiled from (its
-    file and the headers it includes): counter figures taken on other
-    sources are not used."""
+    """Hash of the sources the gate/up decode kernel is compiled from: the
+    headers it includes and the int4 section of its file (the int4 helpers
+    and kernels up to the down decode kernel; the launch code after it is not
+    part of the kernel).  Counter figures taken on other sources are not used."""
     h = hashlib.sha256()
-    for name in ("common.h", "ffn.hip", "kernels.h"):
-        with open(os.path.join(ROOT, "expert_ffn_amd", "csrc", name), "rb") as f:
+    csrc = os.path.join(ROOT, "expert_ffn_amd", "csrc")
+    for name in ("common.h", "kernels.h"):
+        with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + f.read())
+    with open(os.path.join(csrc, "ffn.hip"), "rb") as f:
+        text = f.read()
+    a = text.index(b"// ------------------------------------------------------------ int4 paths --")
+    b = text.index(b"// ------------------------------------------------------ int4 down, decode --")
+    h.update(b"ffn.hip" + text[a:b])
     return h.hexdigest()[:16]
 
 
