@@ -397,9 +397,10 @@ def summarize_counters(dirs, dest, command, kernels):
               "- s_waitcnt share = SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES, wave time spent waiting on a counter;",
               "- issued TFLOP/s = 512 x SQ_INSTS_VALU_MFMA_MOPS_BF16 / duration (padding included);",
               "- VALU/MFMA = non-MFMA VALU instructions per MFMA instruction;",
-              "- LDS conflict = SQ_LDS_BANK_CONFLICT / SQ_ACTIVE_INST_LDS.", "",
+              "- LDS conflict = SQ_LDS_BANK_CONFLICT / SQ_ACTIVE_INST_LDS;",
+              "- L2 hit = TCC_HIT_sum / (TCC_HIT_sum + TCC_MISS_sum).", "",
               "| kernel | window GHz | MFMA busy | VALU issue | waves/SIMD | s_waitcnt share | issued TFLOP/s | "
-              "VALU/MFMA | LDS conflict |", "|---|---|---|---|---|---|---|---|---|"]
+              "VALU/MFMA | LDS conflict | L2 hit |", "|---|---|---|---|---|---|---|---|---|---|"]
     for name, recs in sorted(table.items()):
         us = mean(recs, "_us")
         win = mean(recs, "GRBM_GUI_ACTIVE") / 8
@@ -412,7 +413,8 @@ def summarize_counters(dirs, dest, command, kernels):
                512 * mean(recs, "SQ_INSTS_VALU_MFMA_MOPS_BF16") / (us * 1e6),
                (mean(recs, "SQ_INSTS_VALU") - mf) / mf if mf else float("nan"),
                mean(recs, "SQ_LDS_BANK_CONFLICT") / mean(recs, "SQ_ACTIVE_INST_LDS")
-               if mean(recs, "SQ_ACTIVE_INST_LDS") else float("nan")]
+               if mean(recs, "SQ_ACTIVE_INST_LDS") else float("nan"),
+               mean(recs, "TCC_HIT_sum") / (mean(recs, "TCC_HIT_sum") + mean(recs, "TCC_MISS_sum"))]
         lines.append(f"| `{name[:60]}` | " + " | ".join(f"{v:.3g}" for v in row) + " |")
     with open(dest, "w") as f:
         f.write("\n".join(lines) + "\n")
