@@ -24,9 +24,13 @@
 // 64-element group is one step), K = 32 s + 8 q .. +7 for bf16.
 //
 // Streaming kernels (small groups, decode): one wavefront per 16-row tile and
-// K range, no LDS for operands; the first half splits K over the workgroup's
-// waves and reduces the partial sums in LDS.  Expert groups with no routes
-// leave their workgroups idle at once.
+// K range, the weights in registers; the first half splits K over the
+// workgroup's waves and reduces the partial sums in LDS.  Activations reach
+// the MFMAs through LDS where they fit (the h rows of down's 16-route tile,
+// the x rows of a gate/up tile of at most 4 routes), copied there before the
+// weights are requested, so that no activation load issued after the weights
+// waits for them in the in-order vector-memory counter.  Expert groups with
+// no routes leave their workgroups idle at once.
 #include <climits>
 #include <mutex>
 
@@ -298,25 +302,43 @@ __device__ __forceinline__ void step_gu(const typename Geo<FMT>::A& ag, const ty
     }
 }
 
+// A tile of at most SMALL_RT routes (the usual case in decode) copies its
+// tokens' x rows into LDS by LDS DMA, issued before the weights, and the K
+// loop takes its B fragments there; larger tiles read each lane's activation
+// row from L2 D steps ahead of the MFMAs (16 rows of H would not fit in LDS).
+constexpr int SMALL_RT = 4;
 template <int FMT, int NG, int KSPLIT>
-__global__ __launch_bounds__(64 * KSPLIT) __attribute__((amdgpu_waves_per_eu(3)))
+__host__ __device__ constexpr size_t gate_up_fast_lds() {
+    return SMALL_RT * NG * KSPLIT * Geo<FMT>::KSTEP * 2 + (KSPLIT - 1) * 8 * 64 * sizeof(float);
+}
+
+template <int FMT, int NG, int KSPLIT>
+__global__ __launch_bounds__(64 * KSPLIT) __attribute__((amdgpu_waves_per_eu(4)))
 void gate_up_fast_kernel(FfnParams P) {
     using G = Geo<FMT>;
     using AF = typename G::A;
     constexpr int MF = G::MF;
-    constexpr int D = NG < 3 ? NG : 3;          // activation prefetch depth (steps)
+    constexpr int D = NG < 3 ? NG : 3;             // activation prefetch depth (steps), larger tiles
+    constexpr int HC = NG * KSPLIT * G::KSTEP;     // H of this instantiation
+    constexpr int NCH = SMALL_RT * HC / 8;         // 16-byte chunks of SMALL_RT x rows
+    constexpr int NCP = (NCH + 63) / 64;           // 1 KB LDS DMA copies of them
+    constexpr int NCW = (NCP + KSPLIT - 1) / KSPLIT;   // per wave
     extern __shared__ float smem[];
     const int ntile = P.FF >> 4;
     const int e = blockIdx.x / ntile, tile = blockIdx.x - e * ntile;
     const int beg = P.offsets[e] + 16 * static_cast<int>(blockIdx.y), end = P.offsets[e + 1];
     if (beg >= end) return;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, r = lane & 15, q = lane >> 4;
+    // the wave index as a scalar: the LDS DMA destinations go through M0
+    const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, r = lane & 15,
+              q = lane >> 4;
     const uint8_t* blob = P.pool + static_cast<uint64_t>(P.slot_of[e]) * P.slot_bytes;
     const int n0 = tile << 4;
     const int s0 = wave * NG;
-    const int64_t rs = row_bytes<FMT>(P.H);
+    const int64_t rs = row_bytes<FMT>(HC);
     const uint8_t* ag_row = blob + P.o13 + static_cast<int64_t>(n0 + r) * rs;
     const uint8_t* au_row = ag_row + static_cast<int64_t>(P.FF) * rs;
+    uint16_t* xs = reinterpret_cast<uint16_t*>(smem);                 // [SMALL_RT][HC] bf16
+    float* s_red = reinterpret_cast<float*>(xs + SMALL_RT * HC);      // [KSPLIT-1][8][64]
 
     // The vector-memory counter retires loads in issue order, so the loads go
     // out in the order they are needed: the activations (they sit in L2 and
@@ -327,7 +349,9 @@ void gate_up_fast_kernel(FfnParams P) {
     //    the last route: computed from real data and never stored)
     const int p = beg + r;
     const bool valid = p < end;
-    int route;
+    const int nr = min(end - beg, 16);
+    const bool small = nr <= SMALL_RT;   // uniform
+    int route, tk[SMALL_RT];
     {
         int rt[16];
 #pragma unroll
@@ -335,42 +359,94 @@ void gate_up_fast_kernel(FfnParams P) {
         route = rt[0];
 #pragma unroll
         for (int i = 1; i < 16; ++i) route = r == i ? rt[i] : route;
+#pragma unroll
+        for (int i = 0; i < SMALL_RT; ++i) tk[i] = route_token(rt[i], P.kmul, P.k);
     }
-    // 2. activations, D steps ahead of the MFMAs
-    const uint16_t* xrow = P.xq + static_cast<int64_t>(route_token(route, P.kmul, P.k)) * P.H;
-    u32x4 b[D][MF];
-#pragma unroll
-    for (int g = 0; g < D; ++g)
-#pragma unroll
-        for (int m = 0; m < MF; ++m) b[g][m] = *reinterpret_cast<const u32x4*>(xrow + b_off<FMT>(s0 + g, q) + 8 * m);
-    __builtin_amdgcn_sched_barrier(0);
-    // 3. the weights
+    // 2. activations (a small tile's x rows, else this lane's row D steps
+    //    ahead of the MFMAs), 3. the weights, 4. int8 row scales, then the K
+    //    loop.  The two cases are separate paths (the branch is uniform), so
+    //    that the large tiles' staging registers are not live in the other.
     AF ag[NG], au[NG];
-#pragma unroll
-    for (int g = 0; g < NG; ++g) {
-        ag[g] = *reinterpret_cast<const AF*>(ag_row + a_off<FMT>(s0 + g, q));
-        au[g] = *reinterpret_cast<const AF*>(au_row + a_off<FMT>(s0 + g, q));
-        __builtin_amdgcn_sched_barrier(0);
-    }
-    // 4. int8 row scales
-    float* s_red = smem;   // [KSPLIT-1][8][64]
     f32x4 sg_row = {0, 0, 0, 0}, su_row = {0, 0, 0, 0};
-    if constexpr (FMT == W_INT8) {
-        const float* sc = reinterpret_cast<const float*>(blob + P.os13);
-        sg_row = *reinterpret_cast<const f32x4*>(sc + n0 + 4 * q);
-        su_row = *reinterpret_cast<const f32x4*>(sc + P.FF + n0 + 4 * q);
-    }
-    __syncthreads();
-
+    auto load_weights = [&]() {
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+            ag[g] = *reinterpret_cast<const AF*>(ag_row + a_off<FMT>(s0 + g, q));
+            au[g] = *reinterpret_cast<const AF*>(au_row + a_off<FMT>(s0 + g, q));
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if constexpr (FMT == W_INT8) {
+            const float* sc = reinterpret_cast<const float*>(blob + P.os13);
+            sg_row = *reinterpret_cast<const f32x4*>(sc + n0 + 4 * q);
+            su_row = *reinterpret_cast<const f32x4*>(sc + P.FF + n0 + 4 * q);
+        }
+    };
     const f32x4 zero = {0, 0, 0, 0};
     f32x4 accg = zero, accu = zero, cc = zero;
+    if (small) {
+        // copy b = i KSPLIT + wave: lane l takes 16-byte chunk 64 b + l of the
+        // rows (row j at chunk j HC / 8; rows past nr are not read)
+        const rsrc_t xres = make_rsrc(P.xq, static_cast<uint32_t>(P.T) * HC * 2);
 #pragma unroll
-    for (int g = 0; g < NG; ++g) {
-        step_gu<FMT>(ag[g], au[g], b[g % D], accg, accu, cc);
-        if (g + D < NG) {
+        for (int i = 0; i < NCW; ++i) {
+            const int cp = i * KSPLIT + wave;
+            if (NCP % KSPLIT == 0 || cp < NCP) {
+                const int c = 64 * cp + lane, j = c / (HC / 8), col = c - j * (HC / 8);
+                const int t = j == 0 ? tk[0] : (j == 1 ? tk[1] : (j == 2 ? tk[2] : tk[3]));
+                const uint32_t off = (NCH % 64 == 0 || c < NCH) && j < nr ? static_cast<uint32_t>(t * HC + 8 * col) * 2 : NO_LANE;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    xres, reinterpret_cast<__attribute__((address_space(3))) void*>(reinterpret_cast<uintptr_t>(xs + 512 * cp)),
+                    16, off, 0, 0, 0);
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        load_weights();
+        // the copies are this wave's oldest vector-memory operations: 2 NG
+        // weight loads (and 2 scale loads for int8) follow them.  The compiler
+        // does not track LDS DMA completion, so the wait is explicit.
+        static_assert(2 * NG + (FMT == W_INT8 ? 2 : 0) == (FMT == W_INT8 ? 24 : 22),
+                      "the wait below counts the loads that follow the copies");
+        if constexpr (FMT == W_INT8)
+            __builtin_amdgcn_s_waitcnt(0x4F78);   // vmcnt(24)
+        else
+            __builtin_amdgcn_s_waitcnt(0x4F76);   // vmcnt(22)
+        __syncthreads();
+        // fragments read one step ahead (fenced: the compiler would otherwise
+        // read every step's at once and hold them in registers)
+        const uint16_t* xl = xs + min(r, nr - 1) * HC;
+        u32x4 bn[MF];
 #pragma unroll
-            for (int m = 0; m < MF; ++m)
-                b[g % D][m] = *reinterpret_cast<const u32x4*>(xrow + b_off<FMT>(s0 + g + D, q) + 8 * m);
+        for (int m = 0; m < MF; ++m) bn[m] = *reinterpret_cast<const u32x4*>(xl + b_off<FMT>(s0, q) + 8 * m);
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+            u32x4 bg[MF];
+#pragma unroll
+            for (int m = 0; m < MF; ++m) bg[m] = bn[m];
+            if (g + 1 < NG) {
+#pragma unroll
+                for (int m = 0; m < MF; ++m) bn[m] = *reinterpret_cast<const u32x4*>(xl + b_off<FMT>(s0 + g + 1, q) + 8 * m);
+            }
+            step_gu<FMT>(ag[g], au[g], bg, accg, accu, cc);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    } else {
+        const uint16_t* xrow = P.xq + static_cast<int64_t>(route_token(route, P.kmul, P.k)) * HC;
+        u32x4 b[D][MF];
+#pragma unroll
+        for (int g = 0; g < D; ++g)
+#pragma unroll
+            for (int m = 0; m < MF; ++m) b[g][m] = *reinterpret_cast<const u32x4*>(xrow + b_off<FMT>(s0 + g, q) + 8 * m);
+        __builtin_amdgcn_sched_barrier(0);
+        load_weights();
+        __syncthreads();
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+            step_gu<FMT>(ag[g], au[g], b[g % D], accg, accu, cc);
+            if (g + D < NG) {
+#pragma unroll
+                for (int m = 0; m < MF; ++m)
+                    b[g % D][m] = *reinterpret_cast<const u32x4*>(xrow + b_off<FMT>(s0 + g + D, q) + 8 * m);
+            }
         }
     }
     if constexpr (FMT == W_INT8) {
@@ -403,7 +479,18 @@ void gate_up_fast_kernel(FfnParams P) {
 }
 
 // Workgroup = 4 waves = (4 / KS) tiles of 16 rows of H x KS parts of K = FF,
-// one tile of 16 routes (blockIdx.y).
+// one tile of 16 routes (blockIdx.y).  Every wave multiplies the same 16 h
+// rows, so the workgroup copies them (16 x FF bf16) into LDS once, with loads
+// issued before the weights, and the K loop reads its B fragments there: no
+// activation load waits behind the weights in the in-order vector-memory
+// counter, and each h row is read from L2 once per workgroup, not per wave.
+template <int FMT, int NG, int KS>
+__host__ __device__ constexpr int down_fast_hs() { return NG * KS * Geo<FMT>::KSTEP + 8; }   // LDS row stride
+template <int FMT, int NG, int KS>
+__host__ __device__ constexpr size_t down_fast_lds() {
+    return 16 * down_fast_hs<FMT, NG, KS>() * 2 + (KS > 1 ? 3 * 4 * 64 * sizeof(float) : 0);
+}
+
 template <int FMT, int NG, int KS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3)))
 void down_fast_kernel(FfnParams P) {
@@ -411,29 +498,38 @@ void down_fast_kernel(FfnParams P) {
     using AF = typename G::A;
     constexpr int MF = G::MF;
     constexpr int RTW = 4 / KS;
-    constexpr int D = NG < 3 ? NG : 3;
+    constexpr int FFC = NG * KS * G::KSTEP;          // FF of this instantiation
+    constexpr int HS = down_fast_hs<FMT, NG, KS>();  // row stride 16 bytes past a multiple of 128: rows on distinct banks
+    constexpr int NCH = 16 * FFC / 8;                // 16-byte chunks of the tile's h rows
+    constexpr int NPT = (NCH + 255) / 256;
     extern __shared__ float smem[];
     const int nblk = P.H / (16 * RTW);
     const int e = blockIdx.x / nblk, blk = blockIdx.x - e * nblk;
     const int beg = P.offsets[e] + 16 * static_cast<int>(blockIdx.y), end = P.offsets[e + 1];
     if (beg >= end) return;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, r = lane & 15, q = lane >> 4;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r = lane & 15, q = lane >> 4;
     const int rt = wave / KS, kp = wave - rt * KS;
     const uint8_t* blob = P.pool + static_cast<uint64_t>(P.slot_of[e]) * P.slot_bytes;
     const int m0 = (blk * RTW + rt) * 16;
     const int s0 = kp * NG;
-    const uint8_t* a_row = blob + P.o2 + static_cast<int64_t>(m0 + r) * row_bytes<FMT>(P.FF);
+    const uint8_t* a_row = blob + P.o2 + static_cast<int64_t>(m0 + r) * row_bytes<FMT>(FFC);
+    uint16_t* hs = reinterpret_cast<uint16_t*>(smem);                 // [16][HS] bf16
+    float* s_red = reinterpret_cast<float*>(hs + 16 * HS);            // [3][4][64] when K is split
 
     const int p = beg + r;
     const bool valid = p < end;
-    // loads in the order of need (the in-order vector-memory counter): the h
-    // rows (in L2), then the weights in the order of use, then the row scales
-    const uint16_t* hrow = P.h + static_cast<int64_t>(valid ? p : beg) * P.FF;
-    u32x4 b[D][MF];
+    // loads in the order of need: the tile's h rows (in L2; rows past the
+    // group repeat its last row: computed, never stored), then the weights
+    // in the order of use, then the row scales
+    u32x4 hr[NPT];
 #pragma unroll
-    for (int g = 0; g < D; ++g)
-#pragma unroll
-        for (int m = 0; m < MF; ++m) b[g][m] = *reinterpret_cast<const u32x4*>(hrow + b_off<FMT>(s0 + g, q) + 8 * m);
+    for (int i = 0; i < NPT; ++i) {
+        const int idx = tid + 256 * i;
+        if (NCH % 256 == 0 || idx < NCH) {
+            const int row = idx / (FFC / 8), c = idx - row * (FFC / 8);
+            hr[i] = *reinterpret_cast<const u32x4*>(P.h + static_cast<int64_t>(min(beg + row, end - 1)) * FFC + 8 * c);
+        }
+    }
     __builtin_amdgcn_sched_barrier(0);
     AF a[NG];
 #pragma unroll
@@ -441,18 +537,28 @@ void down_fast_kernel(FfnParams P) {
         a[g] = *reinterpret_cast<const AF*>(a_row + a_off<FMT>(s0 + g, q));
         __builtin_amdgcn_sched_barrier(0);
     }
-    float* s_red = smem;   // [3][4][64] when K is split
     f32x4 s_row = {0, 0, 0, 0};
     if constexpr (FMT == W_INT8) {
         s_row = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(blob + P.os2) + m0 + 4 * q);
+    }
+#pragma unroll
+    for (int i = 0; i < NPT; ++i) {
+        const int idx = tid + 256 * i;
+        if (NCH % 256 == 0 || idx < NCH) {
+            const int row = idx / (FFC / 8), c = idx - row * (FFC / 8);
+            *reinterpret_cast<u32x4*>(hs + row * HS + 8 * c) = hr[i];
+        }
     }
     __syncthreads();
 
     const f32x4 zero = {0, 0, 0, 0};
     f32x4 acc = zero, cc = zero;
+    const uint16_t* hrow = hs + r * HS;
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
-        const u32x4* bg = b[g % D];
+        u32x4 bg[MF];
+#pragma unroll
+        for (int m = 0; m < MF; ++m) bg[m] = *reinterpret_cast<const u32x4*>(hrow + b_off<FMT>(s0 + g, q) + 8 * m);
         if constexpr (FMT == W_INT8) {
             const u32x4 kb = splat(0xC300C300u);
             cc = mfma16x16x32(kb, bg[0], cc);
@@ -461,11 +567,6 @@ void down_fast_kernel(FfnParams P) {
             acc = mfma16x16x32(deq_int8(a[g][2], a[g][3]), bg[1], acc);
         } else {
             acc = mfma16x16x32(a[g], bg[0], acc);
-        }
-        if (g + D < NG) {
-#pragma unroll
-            for (int m = 0; m < MF; ++m)
-                b[g % D][m] = *reinterpret_cast<const u32x4*>(hrow + b_off<FMT>(s0 + g + D, q) + 8 * m);
         }
     }
     if constexpr (FMT == W_INT8) acc = s_row * (acc + cc);
@@ -1223,14 +1324,14 @@ static void launch_gate_up_generic(const FfnParams& P, hipStream_t s) {
 // fast-path shapes: (steps per wave, waves splitting K) with steps * waves = the step count
 template <int FMT, int NG, int KSPLIT>
 static void launch_gate_up_fast(const FfnParams& P, hipStream_t s) {
-    const size_t smem = (KSPLIT - 1) * 8 * 64 * sizeof(float);
+    const size_t smem = gate_up_fast_lds<FMT, NG, KSPLIT>();
     hipLaunchKernelGGL((gate_up_fast_kernel<FMT, NG, KSPLIT>), dim3(P.E * (P.FF / 16), (P.T + 15) / 16), dim3(64 * KSPLIT),
                        smem, s, P);
 }
 
 template <int FMT, int NG, int KS>
 static void launch_down_fast(const FfnParams& P, hipStream_t s) {
-    const size_t smem = (KS > 1 ? 3 * 4 * 64 * sizeof(float) : 0);
+    const size_t smem = down_fast_lds<FMT, NG, KS>();
     hipLaunchKernelGGL((down_fast_kernel<FMT, NG, KS>), dim3(P.E * (P.H / (16 * (4 / KS))), (P.T + 15) / 16), dim3(256),
                        smem, s, P);
 }
