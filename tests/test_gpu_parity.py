@@ -37,14 +37,16 @@ def _x(seed, layer, T, H, kind):
 
 
 def run_case(L, name, *, E, k, H, FF, fmt, T, act=0, x_kind="bf16", y_dtype=torch.bfloat16,
-             zipf=None, slot_of=None, n_sample=None, seed=0, layer=0, out_dtype=torch.float32, gemm=None):
+             zipf=None, slot_of=None, n_sample=None, seed=0, layer=0, out_dtype=torch.float32, gemm=None,
+             logits=None):
     from expert_ffn_amd.layer import MoeLayer
     log(f"[case] {name}: E={E} k={k} H={H} FF={FF} fmt={fmt} T={T} act={act} zipf={zipf}")
     f = FMT[fmt]
     if slot_of is None:
         slot_of = np.arange(E, dtype=np.int32)
     slot_of = np.asarray(slot_of, np.int32)
-    logits = synth.logits(seed, layer, T, E, zipf)
+    if logits is None:
+        logits = synth.logits(seed, layer, T, E, zipf)
     x_d, x_f32 = _x(seed, layer, T, H, x_kind)
     pool, sb = build_pool(seed, layer, E, H, FF, f, slot_of)
     slot_d = torch.from_numpy(slot_of).cuda()
@@ -139,6 +141,47 @@ def test_gemma_int4_decode(L):
     slot_of = synth.slot_table(0, 1, G["E"])[0]
     run_case(L, "gemma-int4-T16", E=G["E"], k=G["k"], H=G["H"], FF=G["FF"], fmt="int4", T=16,
              slot_of=slot_of)
+
+
+def _logits_for_group_sizes(T, E, k, sizes, seed):
+    """Logits whose top-k gives expert e exactly sizes[e] routes (the rest of
+    each token's k picks spread evenly over the remaining experts): expert e goes to
+    the sizes[e] tokens with the fewest picks so far, a token's picks get
+    distinct logits 10 - 0.01 rank, all other logits are N(0,1) - 5."""
+    rng = np.random.default_rng(seed)
+    lg = (rng.standard_normal((T, E)) - 5.0).astype(np.float32)
+    picks = [[] for _ in range(T)]
+    sizes = list(sizes)
+    e = 0
+    while sum(len(p) for p in picks) < T * k:
+        left = T * k - sum(len(p) for p in picks)
+        n = sizes[e] if e < len(sizes) else -(-left // (E - e))
+        order = sorted((t for t in range(T) if len(picks[t]) < k), key=lambda t: (len(picks[t]), t))
+        for t in order[:n]:
+            picks[t].append(e)
+        e += 1
+    for t in range(T):
+        for rank, ex in enumerate(picks[t]):
+            lg[t, ex] = 10.0 - 0.01 * rank
+    return lg
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "int8"])
+@pytest.mark.parametrize("T,sizes,x_kind", [
+    (16, (16, 5, 4, 3, 2, 1, 8, 6), "bf16"),
+    (40, (40, 17, 5, 4, 4, 1, 33), "f32"),
+])
+def test_streaming_tile_sizes(L, fmt, T, sizes, x_kind):
+    """The bf16 / int8 streaming kernels at the Gemma shape on groups of chosen
+    sizes: 4 routes (the last size whose gate/up tile takes x from LDS), 5
+    (the first that reads it per lane from L2), 16 and more (down's full
+    16-route tile, and more than one route tile per group)."""
+    lg = _logits_for_group_sizes(T, G["E"], G["k"], sizes, seed=7)
+    ml, *_ = run_case(L, f"gemma-{fmt}-T{T}-sizes", E=G["E"], k=G["k"], H=G["H"], FF=G["FF"], fmt=fmt, T=T,
+                      x_kind=x_kind, logits=lg)
+    m = np.diff(to_np(ml.views(T)["offsets"]))
+    for n in sizes:
+        assert n in m, f"no group of {n} routes"
 
 
 @pytest.mark.parametrize("T,zipf", [(1, None), (5, None), (16, 1.1), (37, None)])
