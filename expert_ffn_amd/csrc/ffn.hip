@@ -479,16 +479,21 @@ void gate_up_fast_kernel(FfnParams P) {
 }
 
 // Workgroup = 4 waves = (4 / KS) tiles of 16 rows of H x KS parts of K = FF,
-// one tile of 16 routes (blockIdx.y).  Every wave multiplies the same 16 h
-// rows, so the workgroup copies them (16 x FF bf16) into LDS once, with loads
-// issued before the weights, and the K loop reads its B fragments there: no
-// activation load waits behind the weights in the in-order vector-memory
-// counter, and each h row is read from L2 once per workgroup, not per wave.
+// one tile of 16 routes (blockIdx.y).  With KS = 1 every wave multiplies the
+// same 16 h rows over the whole FF, so the workgroup copies them (16 x FF
+// bf16) into LDS once, with loads issued before the weights, and the K loop
+// reads its B fragments there: no activation load waits behind the weights in
+// the in-order vector-memory counter, and each h row is read from L2 once per
+// workgroup, not per wave (int8: 21.7 -> 15.7 us per layer under Zipf routing
+// at T = 16).  With K split (bf16) each lane reads its row from L2 D steps
+// ahead of the MFMAs, which measured 1-3 % faster there.
+template <int KS>
+__host__ __device__ constexpr bool down_fast_stage() { return KS == 1; }
 template <int FMT, int NG, int KS>
 __host__ __device__ constexpr int down_fast_hs() { return NG * KS * Geo<FMT>::KSTEP + 8; }   // LDS row stride
 template <int FMT, int NG, int KS>
 __host__ __device__ constexpr size_t down_fast_lds() {
-    return 16 * down_fast_hs<FMT, NG, KS>() * 2 + (KS > 1 ? 3 * 4 * 64 * sizeof(float) : 0);
+    return (down_fast_stage<KS>() ? 16 * down_fast_hs<FMT, NG, KS>() * 2 : 0) + (KS > 1 ? 3 * 4 * 64 * sizeof(float) : 0);
 }
 
 template <int FMT, int NG, int KS>
@@ -500,8 +505,10 @@ void down_fast_kernel(FfnParams P) {
     constexpr int RTW = 4 / KS;
     constexpr int FFC = NG * KS * G::KSTEP;          // FF of this instantiation
     constexpr int HS = down_fast_hs<FMT, NG, KS>();  // row stride 16 bytes past a multiple of 128: rows on distinct banks
+    constexpr bool STAGE = down_fast_stage<KS>();
     constexpr int NCH = 16 * FFC / 8;                // 16-byte chunks of the tile's h rows
-    constexpr int NPT = (NCH + 255) / 256;
+    constexpr int NPT = STAGE ? (NCH + 255) / 256 : 1;
+    constexpr int D = NG < 3 ? NG : 3;               // prefetch depth (steps) without staging
     extern __shared__ float smem[];
     const int nblk = P.H / (16 * RTW);
     const int e = blockIdx.x / nblk, blk = blockIdx.x - e * nblk;
@@ -513,22 +520,31 @@ void down_fast_kernel(FfnParams P) {
     const int m0 = (blk * RTW + rt) * 16;
     const int s0 = kp * NG;
     const uint8_t* a_row = blob + P.o2 + static_cast<int64_t>(m0 + r) * row_bytes<FMT>(FFC);
-    uint16_t* hs = reinterpret_cast<uint16_t*>(smem);                 // [16][HS] bf16
-    float* s_red = reinterpret_cast<float*>(hs + 16 * HS);            // [3][4][64] when K is split
+    uint16_t* hs = reinterpret_cast<uint16_t*>(smem);                        // [16][HS] bf16 (staging)
+    float* s_red = reinterpret_cast<float*>(hs + (STAGE ? 16 * HS : 0));     // [3][4][64] when K is split
 
     const int p = beg + r;
     const bool valid = p < end;
     // loads in the order of need: the tile's h rows (in L2; rows past the
-    // group repeat its last row: computed, never stored), then the weights
-    // in the order of use, then the row scales
+    // group repeat its last row: computed, never stored) or this lane's row
+    // D steps ahead, then the weights in the order of use, then the row scales
     u32x4 hr[NPT];
+    u32x4 b[D][MF];
+    const uint16_t* hg = P.h + static_cast<int64_t>(valid ? p : beg) * FFC;
+    if constexpr (STAGE) {
 #pragma unroll
-    for (int i = 0; i < NPT; ++i) {
-        const int idx = tid + 256 * i;
-        if (NCH % 256 == 0 || idx < NCH) {
-            const int row = idx / (FFC / 8), c = idx - row * (FFC / 8);
-            hr[i] = *reinterpret_cast<const u32x4*>(P.h + static_cast<int64_t>(min(beg + row, end - 1)) * FFC + 8 * c);
+        for (int i = 0; i < NPT; ++i) {
+            const int idx = tid + 256 * i;
+            if (NCH % 256 == 0 || idx < NCH) {
+                const int row = idx / (FFC / 8), c = idx - row * (FFC / 8);
+                hr[i] = *reinterpret_cast<const u32x4*>(P.h + static_cast<int64_t>(min(beg + row, end - 1)) * FFC + 8 * c);
+            }
         }
+    } else {
+#pragma unroll
+        for (int g = 0; g < D; ++g)
+#pragma unroll
+            for (int m = 0; m < MF; ++m) b[g][m] = *reinterpret_cast<const u32x4*>(hg + b_off<FMT>(s0 + g, q) + 8 * m);
     }
     __builtin_amdgcn_sched_barrier(0);
     AF a[NG];
@@ -541,12 +557,14 @@ void down_fast_kernel(FfnParams P) {
     if constexpr (FMT == W_INT8) {
         s_row = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(blob + P.os2) + m0 + 4 * q);
     }
+    if constexpr (STAGE) {
 #pragma unroll
-    for (int i = 0; i < NPT; ++i) {
-        const int idx = tid + 256 * i;
-        if (NCH % 256 == 0 || idx < NCH) {
-            const int row = idx / (FFC / 8), c = idx - row * (FFC / 8);
-            *reinterpret_cast<u32x4*>(hs + row * HS + 8 * c) = hr[i];
+        for (int i = 0; i < NPT; ++i) {
+            const int idx = tid + 256 * i;
+            if (NCH % 256 == 0 || idx < NCH) {
+                const int row = idx / (FFC / 8), c = idx - row * (FFC / 8);
+                *reinterpret_cast<u32x4*>(hs + row * HS + 8 * c) = hr[i];
+            }
         }
     }
     __syncthreads();
@@ -557,8 +575,18 @@ void down_fast_kernel(FfnParams P) {
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
         u32x4 bg[MF];
+        if constexpr (STAGE) {
 #pragma unroll
-        for (int m = 0; m < MF; ++m) bg[m] = *reinterpret_cast<const u32x4*>(hrow + b_off<FMT>(s0 + g, q) + 8 * m);
+            for (int m = 0; m < MF; ++m) bg[m] = *reinterpret_cast<const u32x4*>(hrow + b_off<FMT>(s0 + g, q) + 8 * m);
+        } else {
+#pragma unroll
+            for (int m = 0; m < MF; ++m) bg[m] = b[g % D][m];
+            if (g + D < NG) {
+#pragma unroll
+                for (int m = 0; m < MF; ++m)
+                    b[g % D][m] = *reinterpret_cast<const u32x4*>(hg + b_off<FMT>(s0 + g + D, q) + 8 * m);
+            }
+        }
         if constexpr (FMT == W_INT8) {
             const u32x4 kb = splat(0xC300C300u);
             cc = mfma16x16x32(kb, bg[0], cc);
