@@ -88,6 +88,12 @@ __device__ __forceinline__ int perm8(int j) { return (j >> 1) | ((j & 1) << 2); 
 // each dword into v_and + v_or.  With the mask in an SGPR and the magic in a
 // VGPR it emits one v_and_or_b32 per dword and tracks the VALU -> MFMA operand
 // hazards itself (it does not for VGPRs written by inline asm instructions).
+// s_waitcnt immediate (gfx9 encoding) that waits until at most n vector-memory
+// operations of the wave are outstanding, leaving the LDS/scalar and export
+// counters unwaited: vmcnt bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]
+__host__ __device__ constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
+static_assert(waitcnt_vm(8) == 0x0F78 && waitcnt_vm(0) == 0x0F70 && waitcnt_vm(24) == 0x4F78, "s_waitcnt encoding");
+
 __device__ __forceinline__ u32x4 deq_int4(uint32_t d) {
     uint32_t M = 0x000F000Fu, C = 0x43004300u;
     asm("" : "+s"(M));

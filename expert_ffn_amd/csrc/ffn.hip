@@ -404,12 +404,9 @@ void gate_up_fast_kernel(FfnParams P) {
         // the copies are this wave's oldest vector-memory operations: 2 NG
         // weight loads (and 2 scale loads for int8) follow them.  The compiler
         // does not track LDS DMA completion, so the wait is explicit.
-        static_assert(2 * NG + (FMT == W_INT8 ? 2 : 0) == (FMT == W_INT8 ? 24 : 22),
-                      "the wait below counts the loads that follow the copies");
-        if constexpr (FMT == W_INT8)
-            __builtin_amdgcn_s_waitcnt(0x4F78);   // vmcnt(24)
-        else
-            __builtin_amdgcn_s_waitcnt(0x4F76);   // vmcnt(22)
+        constexpr int NAFTER = 2 * NG + (FMT == W_INT8 ? 2 : 0);
+        static_assert(NAFTER < 64, "vmcnt holds 6 bits");
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(NAFTER));
         __syncthreads();
         // fragments read one step ahead (fenced: the compiler would otherwise
         // read every step's at once and hold them in registers)

@@ -520,7 +520,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void ffn_int4_gemm_kernel(FfnParam
                         // wave, and also ends the reads of stage c - 1, whose buffer
                         // stage c + 2 now takes.  (The compiler does not track LDS DMA
                         // completion itself.)
-                        __builtin_amdgcn_s_waitcnt(0x0F78);   // vmcnt(8), lgkm/exp not waited
+                        __builtin_amdgcn_s_waitcnt(waitcnt_vm(8));
                         __builtin_amdgcn_s_barrier();
                         dma_stage(min(c + 2, NC - 1), bcur == 0 ? 2 : bcur - 1);
                     } else {
@@ -629,7 +629,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void ffn_int4_gemm_kernel(FfnParam
         kloop(mbc);
         if (XD) {
             // every copy into the ring has landed before the epilogue reuses it
-            __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+            __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
             __syncthreads();
         }
 
