@@ -1142,8 +1142,10 @@ def main():
         graph = None
         use_graph = not args.no_graph
         if use_graph:
+            # the warmup steps again as replays of the graph the timed region
+            # replays (its first replays after capture run slower)
             graph = run.capture(stream)
-            for _ in range(3):
+            for _ in range(max(3, args.warmup)):
                 graph.replay()
         torch.cuda.synchronize()
         # timed region: K steps
@@ -1202,7 +1204,8 @@ def main():
             runp.step()
             gp = runp.capture(stream) if use_graph else None
             stepp = gp.replay if gp is not None else runp.step
-            stepp()
+            for _ in range(3):   # warm replays before the timed ones
+                stepp()
             torch.cuda.synchronize()
             tp = time.perf_counter()
             for _ in range(args.prefill_steps):
