@@ -156,7 +156,7 @@ __host__ __device__ constexpr int gemm_nstage(int NW) { return NW == 4 ? 3 : 2; 
 
 __host__ __device__ inline size_t gemm_lds_bytes(int E, int G, int NW) {
     return gemm_nstage(NW) * static_cast<size_t>(NW / 4) * GM_GBUF + static_cast<size_t>(64 * NW) * G * 2 + 16 +
-           static_cast<size_t>(E + 1) * 12;
+           static_cast<size_t>(E + 1) * 20;   // prefix arrays [3][E+1], offsets [E+1], slots [E]
 }
 
 template <int MODE, int DC, int NW>
@@ -175,6 +175,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void ffn_int4_gemm_kernel(FfnParam
     uint8_t* xbuf = lds;                                                   // [NSTG][XBUF]
     uint16_t* ssc = reinterpret_cast<uint16_t*>(lds + NSTG * XBUF);        // [NTH][G] bf16 scales of the tile
     int* pre = reinterpret_cast<int*>(lds + NSTG * XBUF + ((NTH * G * 2 + 15) & ~15));   // [3][E+1]
+    int* offs = pre + 3 * (E + 1);    // [E+1] group offsets, copied by the prefix pass
+    int* slots = offs + (E + 1);      // [E] expert slots, likewise
     // the wave index as a scalar: the LDS DMA copies take wave-derived offsets
     // in SGPRs and M0, which the compiler must know to be uniform (else each
     // copy becomes a loop over the lanes' values)
@@ -208,12 +210,20 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void ffn_int4_gemm_kernel(FfnParam
     };
     if (wave == 0) {
         // one round of global loads: the group sizes wait in pre[] for the
-        // second pass, which overwrites each entry after reading it
+        // second pass, which overwrites each entry after reading it; the
+        // offsets and slots stay in LDS for the items' headers
         int tot = 0, elig = 0;
         for (int e0 = 0; e0 < E; e0 += 64) {
             const int e = e0 + lane;
-            const int me = e < E ? P.offsets[e + 1] - P.offsets[e] : 0;
-            if (e < E) pre[e + 1] = me;
+            const int o0 = e < E ? P.offsets[e] : 0, o1 = e < E ? P.offsets[e + 1] : 0;
+            const int sl = e < E ? P.slot_of[e] : 0;
+            const int me = o1 - o0;
+            if (e < E) {
+                pre[e + 1] = me;
+                offs[e] = o0;
+                slots[e] = sl;
+                if (e == E - 1) offs[E] = o1;
+            }
             int c = split_items(me), ce = me > 64 && me <= GEMM_WIDE_MAX ? c : 0;
 #pragma unroll
             for (int d = 1; d < 64; d <<= 1) {
@@ -301,17 +311,30 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void ffn_int4_gemm_kernel(FfnParam
             if (pc[mid] <= item) lo = mid; else hi = mid;
         }
         const int e = lo, li = item - pc[e];
-        const int me = P.offsets[e + 1] - P.offsets[e];
+        const int o0 = offs[e], o1 = offs[e + 1];
+        const int me = o1 - o0;
         const bool wide = me <= GEMM_WIDE_MAX;
         const int nw = wide ? 2 : 1;                        // N tile width in narrow tiles
         const int ntl = wide ? NTW : NT;
         const int mt = li / ntl, nt = li - mt * ntl;
         const int rows = wide ? (inA ? 96 : 64) : GM_ROWS;  // route rows of the tile
-        const int beg = P.offsets[e] + rows * mt;
-        const int end = min(P.offsets[e + 1], beg + rows);
+        const int beg = o0 + rows * mt;
+        const int end = min(o1, beg + rows);
         const int MB = MBC == 2 ? (wide ? (end - beg + 31) / 32 : 2) : MBC;   // route blocks of each wave (uniform)
-        const uint8_t* blob = P.pool + static_cast<uint64_t>(P.slot_of[e]) * P.slot_bytes;
+        const uint8_t* blob = P.pool + static_cast<uint64_t>(slots[e]) * P.slot_bytes;
         const int n0 = (MODE == 0 ? 32 * NQ : 64 * NQ) * nw * nt;
+        // the tile's route indices (gate/up), requested together before the
+        // scales: rows beg + 32 mb4 + c32 (bias, register staging) and the LDS
+        // DMA rows; rows past the group read the group's last route
+        int srt[4], srd[4];
+        if (MODE == 0) {
+#pragma unroll
+            for (int mb4 = 0; mb4 < 4; ++mb4) srt[mb4] = P.sorted_route[min(beg + 32 * mb4 + c32, end - 1)];
+            if (XD) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) srd[i] = P.sorted_route[min(beg + 32 * (wave & 3) + 8 * i + (lane >> 3), end - 1)];
+            }
+        }
         const int nsub = wide ? wave : nq;                  // this wave's column block of the tile
         const int mbase = wide ? 0 : 64 * mh;               // this wave's first route row of the tile
         // ---- scales of the tile's 256 rows -> LDS (16-byte copies; rows past the matrix read as 0)
@@ -370,7 +393,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void ffn_int4_gemm_kernel(FfnParam
         for (int mb4 = 0; mb4 < 4; ++mb4) {
             const int p = beg + 32 * mb4 + c32;
             const bool ok = p < end;
-            const int r = ok ? (MODE == 0 ? P.sorted_route[p] / P.k : p) : 0;
+            const int r = MODE == 0 ? srt[mb4] / P.k : p;
             aoff[mb4] = ok ? static_cast<uint32_t>((r * arow_stride + 16 * ss + 8 * hh) * 2) : NO_LANE;
         }
         // LDS DMA staging (4-wave workgroups): a stage is [128 tile rows][128 B]
@@ -385,7 +408,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void ffn_int4_gemm_kernel(FfnParam
             const int R = 32 * (wave & 3) + 8 * i + (lane >> 3);
             const int p = beg + R;
             const bool ok = p < end;
-            const int r = ok ? (MODE == 0 ? P.sorted_route[p] / P.k : p) : 0;
+            const int r = MODE == 0 ? srd[i] / P.k : p;
             const int j = (lane & 7) ^ ((lane >> 3) & 7) ^ i;
             adm[i] = ok ? static_cast<uint32_t>((r * arow_stride + 8 * j) * 2) : NO_LANE;
         }
@@ -455,8 +478,9 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void ffn_int4_gemm_kernel(FfnParam
                 u32x4 ah[MBC], al[MBC];
 #pragma unroll
                 for (int mb = 0; mb < MBC; ++mb) {
-                    const int p = min(beg + mbase + 32 * mb + c32, end - 1);
-                    const int r = MODE == 0 ? P.sorted_route[p] / P.k : p;
+                    const int sb = (wide ? 0 : 2 * mh) + mb;   // the block's index among srt
+                    const int r = MODE == 0 ? (sb == 0 ? srt[0] : sb == 1 ? srt[1] : sb == 2 ? srt[2] : srt[3]) / P.k
+                                            : min(beg + mbase + 32 * mb + c32, end - 1);
                     const uint16_t* sh = asum + static_cast<int64_t>(r) * GP + 16 * t + 8 * hh;
                     const uint16_t* sl = sh + static_cast<int64_t>(asum_rows) * GP;
                     ah[mb] = *reinterpret_cast<const u32x4*>(sh);
