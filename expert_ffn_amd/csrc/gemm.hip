@@ -324,8 +324,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void ffn_int4_gemm_kernel(FfnParam
         const uint8_t* blob = P.pool + static_cast<uint64_t>(slots[e]) * P.slot_bytes;
         const int n0 = (MODE == 0 ? 32 * NQ : 64 * NQ) * nw * nt;
         // the tile's route indices (gate/up), requested together before the
-        // scales: rows beg + 32 mb4 + c32 (bias, register staging) and the LDS
-        // DMA rows; rows past the group read the group's last route
+        // scales, as tokens: rows beg + 32 mb4 + c32 (bias, register staging)
+        // and the LDS DMA rows; rows past the group read the group's last route
         int srt[4], srd[4];
         if (MODE == 0) {
 #pragma unroll
@@ -334,35 +334,44 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void ffn_int4_gemm_kernel(FfnParam
 #pragma unroll
                 for (int i = 0; i < 4; ++i) srd[i] = P.sorted_route[min(beg + 32 * (wave & 3) + 8 * i + (lane >> 3), end - 1)];
             }
+            // routes -> tokens (a multiply, not a division by k)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                srt[i] = route_token(srt[i], P.kmul, P.k);
+                if (XD) srd[i] = route_token(srd[i], P.kmul, P.k);
+            }
         }
         const int nsub = wide ? wave : nq;                  // this wave's column block of the tile
         const int mbase = wide ? 0 : 64 * mh;               // this wave's first route row of the tile
-        // ---- scales of the tile's 256 rows -> LDS (16-byte copies; rows past the matrix read as 0)
-        {
-            const uint8_t* sblk = blob + o_scales;
-            const int half = (MODE == 0 ? 32 * NQ : 64 * NQ) * nw * G * 2;    // bytes of one contiguous row run
-            const int nruns = MODE == 0 ? 2 : 1;
-            // batches of up to 3 chunks per thread: the loads of a batch, then its stores
-            const int nch = nruns * half / 16;
-            for (int i0 = 0; i0 < nch; i0 += 3 * NTH) {
-                u32x4 v[3];
+        // ---- scales of the tile's 256 rows -> LDS (16-byte copies; rows past
+        // the matrix read as 0): the first batch of loads now, its stores after
+        // the bias and weight requests below, so that one wait covers them
+        const uint8_t* sblk = blob + o_scales;
+        const int shalf = (MODE == 0 ? 32 * NQ : 64 * NQ) * nw * G * 2;   // bytes of one contiguous row run
+        const int cpr = shalf / 16, nch = (MODE == 0 ? 2 : 1) * cpr;   // chunks per run, in all
+        constexpr int SB = MODE == 0 ? 6 : 2;   // chunks per thread and batch (one batch at the Gemma shapes)
+        // chunk i (< nch) of the tile: run i / cpr, byte 16 (i % cpr) of it;
+        // chunks past the matrix (or the tile) read as 0 without a memory access
+        const rsrc_t sres = make_rsrc(sblk, static_cast<uint32_t>(S.nrows) * G * 2);
+        auto scale_src = [&](int i) {
+            const int run = MODE == 0 && i >= cpr ? 1 : 0;   // (i < 2 cpr)
+            const int r0 = MODE == 0 ? run * P.FF + n0 : n0;  // first matrix row of the run
+            const int src = r0 * G * 2 + (i - run * cpr) * 16;
+            return i < nch && src + 16 <= S.nrows * G * 2 ? static_cast<uint32_t>(src) : NO_LANE;
+        };
+        u32x4 sv[SB];
 #pragma unroll
-                for (int j = 0; j < 3; ++j) {
-                    const int i = i0 + tid + NTH * j;
-                    const int run = i / (half / 16), o = (i - run * (half / 16)) * 16;
-                    const int r0 = MODE == 0 ? run * P.FF + n0 : n0;            // first matrix row of the run
-                    const int64_t src = static_cast<int64_t>(r0) * G * 2 + o;
-                    const bool ok = i < nch && src + 16 <= static_cast<int64_t>(S.nrows) * G * 2;
-                    v[j] = ok ? *reinterpret_cast<const u32x4*>(sblk + src) : u32x4{0, 0, 0, 0};
-                }
+        for (int j = 0; j < SB; ++j) sv[j] = bload16(sres, scale_src(tid + NTH * j));
+        // the LDS copy is contiguous: chunk i at byte 16 i
+        auto scale_stores = [&]() {
 #pragma unroll
-                for (int j = 0; j < 3; ++j) {
-                    const int i = i0 + tid + NTH * j;
-                    const int run = i / (half / 16), o = (i - run * (half / 16)) * 16;
-                    if (i < nch) *reinterpret_cast<u32x4*>(reinterpret_cast<uint8_t*>(ssc) + run * half + o) = v[j];
-                }
+            for (int j = 0; j < SB; ++j) {
+                const int i = tid + NTH * j;
+                if (i < nch) *reinterpret_cast<u32x4*>(reinterpret_cast<uint8_t*>(ssc) + 16 * i) = sv[j];
             }
-        }
+            for (int i = SB * NTH + tid; i < nch; i += NTH)   // shapes beyond one batch
+                *reinterpret_cast<u32x4*>(reinterpret_cast<uint8_t*>(ssc) + 16 * i) = bload16(sres, scale_src(i));
+        };
 
         // ---- this wave's weight rows and activation rows
         const bool nact = MODE == 0 ? (n0 + 32 * nsub < P.FF) : (n0 + 64 * nsub < P.H);
@@ -393,7 +402,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void ffn_int4_gemm_kernel(FfnParam
         for (int mb4 = 0; mb4 < 4; ++mb4) {
             const int p = beg + 32 * mb4 + c32;
             const bool ok = p < end;
-            const int r = MODE == 0 ? srt[mb4] / P.k : p;
+            const int r = MODE == 0 ? srt[mb4] : p;
             aoff[mb4] = ok ? static_cast<uint32_t>((r * arow_stride + 16 * ss + 8 * hh) * 2) : NO_LANE;
         }
         // LDS DMA staging (4-wave workgroups): a stage is [128 tile rows][128 B]
@@ -408,7 +417,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void ffn_int4_gemm_kernel(FfnParam
             const int R = 32 * (wave & 3) + 8 * i + (lane >> 3);
             const int p = beg + R;
             const bool ok = p < end;
-            const int r = MODE == 0 ? srd[i] / P.k : p;
+            const int r = MODE == 0 ? srd[i] : p;
             const int j = (lane & 7) ^ ((lane >> 3) & 7) ^ i;
             adm[i] = ok ? static_cast<uint32_t>((r * arow_stride + 8 * j) * 2) : NO_LANE;
         }
@@ -450,8 +459,25 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void ffn_int4_gemm_kernel(FfnParam
             wr[d][0] = *reinterpret_cast<const u32x4*>(wp0 + 1024 * g);
             wr[d][1] = *reinterpret_cast<const u32x4*>(wp1 + 1024 * g);
         };
+        // group sums of the bias for 16-group step t: the rows of the wave's
+        // MBC blocks, clamped to the group
+        const int GPT = GP / 16;
+        auto bias_loads = [&](int t, u32x4* h, u32x4* l) {
+#pragma unroll
+            for (int mb = 0; mb < MBC; ++mb) {
+                const int sb = (wide ? 0 : 2 * mh) + mb;   // the block's index among srt
+                const int r = MODE == 0 ? (sb == 0 ? srt[0] : sb == 1 ? srt[1] : sb == 2 ? srt[2] : srt[3])
+                                        : min(beg + mbase + 32 * mb + c32, end - 1);
+                const uint16_t* sh = asum + static_cast<int64_t>(r) * GP + 16 * t + 8 * hh;
+                h[mb] = *reinterpret_cast<const u32x4*>(sh);
+                l[mb] = *reinterpret_cast<const u32x4*>(sh + static_cast<int64_t>(asum_rows) * GP);
+            }
+        };
+        u32x4 ah[MBC], al[MBC];
+        bias_loads(0, ah, al);
 #pragma unroll
         for (int d = 0; d < D - 2; ++d) fill(d);
+        scale_stores();
         if (!XD) store_stage(0, xr);
         __syncthreads();   // scales (and stage 0) in LDS
 
@@ -463,7 +489,10 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void ffn_int4_gemm_kernel(FfnParam
             const f32x16 z = {};
 #pragma unroll
             for (int mb = 0; mb < MBC; ++mb) acc[mb][0] = acc[mb][1] = z;
-            for (int t = 0; t < GP / 16; ++t) {
+#pragma unroll 1
+            for (int t = 0; t < GPT; ++t) {
+                u32x4 nh[MBC], nl[MBC];
+                if (t + 1 < GPT) bias_loads(t + 1, nh, nl);   // the next step's, one step ahead
                 u32x4 bs[2];
 #pragma unroll
                 for (int nb = 0; nb < 2; ++nb) {
@@ -475,16 +504,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void ffn_int4_gemm_kernel(FfnParam
                         bs[nb][j] = a | (b << 16);
                     }
                 }
-                u32x4 ah[MBC], al[MBC];
 #pragma unroll
                 for (int mb = 0; mb < MBC; ++mb) {
-                    const int sb = (wide ? 0 : 2 * mh) + mb;   // the block's index among srt
-                    const int r = MODE == 0 ? (sb == 0 ? srt[0] : sb == 1 ? srt[1] : sb == 2 ? srt[2] : srt[3]) / P.k
-                                            : min(beg + mbase + 32 * mb + c32, end - 1);
-                    const uint16_t* sh = asum + static_cast<int64_t>(r) * GP + 16 * t + 8 * hh;
-                    const uint16_t* sl = sh + static_cast<int64_t>(asum_rows) * GP;
-                    ah[mb] = *reinterpret_cast<const u32x4*>(sh);
-                    al[mb] = *reinterpret_cast<const u32x4*>(sl);
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {   // groups past G: zero (the padding is not trusted)
                         const int g0 = 16 * t + 8 * hh + 2 * j;
@@ -492,9 +513,6 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void ffn_int4_gemm_kernel(FfnParam
                         ah[mb][j] &= m;
                         al[mb][j] &= m;
                     }
-                }
-#pragma unroll
-                for (int mb = 0; mb < MBC; ++mb) {
                     if (mb < MB) {
 #pragma unroll
                         for (int nb = 0; nb < 2; ++nb) {
@@ -502,6 +520,11 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void ffn_int4_gemm_kernel(FfnParam
                             acc[mb][nb] = mfma32(al[mb], bs[nb], acc[mb][nb]);
                         }
                     }
+                }
+#pragma unroll
+                for (int mb = 0; mb < MBC; ++mb) {
+                    ah[mb] = nh[mb];
+                    al[mb] = nl[mb];
                 }
             }
 #pragma unroll
