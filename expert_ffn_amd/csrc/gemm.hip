@@ -729,6 +729,35 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void ffn_int4_gemm_kernel(FfnParam
                     P.hsum[(static_cast<int64_t>(R) + beg + r) * GP2 + gidx] = f32_to_bf16(sum - bf16_to_f32(shi));
                 }
             }
+        } else if (NW == 4 && P.out_dt != F32) {
+            // bf16 rows of out: the tile [tile rows][64 NQ nw columns] (at most
+            // 96 x 256, 48 KB) through LDS (the activation ring is free), then
+            // 16-byte stores along the rows; per-element 2-byte stores cost down
+            // about a fifth of its time
+            uint16_t* tile = reinterpret_cast<uint16_t*>(xbuf);
+            const int tw = 64 * NQ * nw, trows = wide ? 32 * MB : GM_ROWS;
+            if (nact && mact) {
+#pragma unroll
+                for (int mb = 0; mb < MBC; ++mb) {
+                    if (mb < MB) {
+#pragma unroll
+                        for (int v = 0; v < 16; ++v) {
+                            const int r = mbase + 32 * mb + 8 * (v >> 2) + 4 * hh + (v & 3);
+#pragma unroll
+                            for (int nb = 0; nb < 2; ++nb)
+                                tile[r * tw + 64 * nsub + 32 * nb + c32] = f32_to_bf16(acc[mb][nb][v]);
+                        }
+                    }
+                }
+            }
+            __syncthreads();
+            const int ncol = min(tw, P.H - n0);
+            for (int i = tid; i < trows * (tw / 8); i += NTH) {
+                const int r = i / (tw / 8), c8 = i - r * (tw / 8);
+                if (beg + r < end && 8 * c8 < ncol)
+                    *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(P.out) + static_cast<int64_t>(beg + r) * P.H + n0 + 8 * c8) =
+                        *reinterpret_cast<const u32x4*>(tile + r * tw + 8 * c8);
+            }
         } else if (nact && mact) {
 #pragma unroll
             for (int mb = 0; mb < MBC; ++mb) {
@@ -738,13 +767,9 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void ffn_int4_gemm_kernel(FfnParam
                         const int p = beg + mbase + 32 * mb + 8 * (v >> 2) + 4 * hh + (v & 3);
                         if (p < end) {
 #pragma unroll
-                            for (int nb = 0; nb < 2; ++nb) {
-                                const int64_t o = static_cast<int64_t>(p) * P.H + n0 + 64 * nsub + 32 * nb + c32;
-                                if (P.out_dt == F32)
-                                    static_cast<float*>(P.out)[o] = acc[mb][nb][v];
-                                else
-                                    static_cast<uint16_t*>(P.out)[o] = f32_to_bf16(acc[mb][nb][v]);
-                            }
+                            for (int nb = 0; nb < 2; ++nb)
+                                static_cast<float*>(P.out)[static_cast<int64_t>(p) * P.H + n0 + 64 * nsub + 32 * nb + c32] =
+                                    acc[mb][nb][v];
                         }
                     }
                 }
