@@ -51,6 +51,10 @@ __device__ __forceinline__ f32x16 mfma32(const u32x4& a, const u32x4& b, const f
                                                     0, 0, 0);
 }
 
+// fp32 -> bf16 (round to nearest even) by the gfx950 conversion instruction:
+// one VALU where f32_to_bf16 takes five; the two differ only in NaN payloads
+__device__ __forceinline__ uint16_t bf16_cvt(float f) { return static_cast<uint16_t>(pack_bf16x2(f, 0.0f)); }
+
 // position of element f (0..63) of a 64-group in the M32 operand order
 __host__ __device__ __forceinline__ int m32_pos(int f) {
     const int h = f >> 5, s = (f >> 3) & 3, e = f & 7;
@@ -695,7 +699,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void ffn_int4_gemm_kernel(FfnParam
                             const int r = mbase + 32 * mb + 8 * (v >> 2) + 4 * hh + (v & 3);
                             const int col = 32 * nsub + c32;
                             const float hv = act_fn(P.act, acc[mb][0][v]) * acc[mb][1][v];
-                            tile[r * tw + 64 * (col >> 6) + m32_pos(col & 63)] = f32_to_bf16(hv);
+                            tile[r * tw + 64 * (col >> 6) + m32_pos(col & 63)] = bf16_cvt(hv);
                         }
                     }
                 }
@@ -745,7 +749,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void ffn_int4_gemm_kernel(FfnParam
                             const int r = mbase + 32 * mb + 8 * (v >> 2) + 4 * hh + (v & 3);
 #pragma unroll
                             for (int nb = 0; nb < 2; ++nb)
-                                tile[r * tw + 64 * nsub + 32 * nb + c32] = f32_to_bf16(acc[mb][nb][v]);
+                                tile[r * tw + 64 * nsub + 32 * nb + c32] = bf16_cvt(acc[mb][nb][v]);
                         }
                     }
                 }
