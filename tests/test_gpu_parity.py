@@ -216,6 +216,11 @@ GEMM_CASES = [
     dict(name="mixed-E32-H256-FF192-T80-zipf", E=32, k=2, H=256, FF=192, T=80, zipf=1.1, gemm=(True, True)),
     dict(name="mixed-E24-H384-FF128-T70-zipf-f32x", E=24, k=3, H=384, FF=128, T=70, zipf=1.1, x_kind="f32",
          gemm=(True, True)),
+    # H = 3328 (52 groups), FF = 1152 (18): the item set-up's scale tile takes more than one batch
+    # in both halves and the bias more than three 16-group steps; wide tiles of 49-70 routes,
+    # then 128-route tiles
+    dict(name="gemm-E4-H3328-FF1152-T120", E=4, k=2, H=3328, FF=1152, T=120, out_dtype=torch.bfloat16),
+    dict(name="gemm-E2-H3328-FF1152-T250-narrow", E=2, k=1, H=3328, FF=1152, T=250),
 ]
 
 
