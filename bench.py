@@ -1081,6 +1081,8 @@ def main():
     ap.add_argument("--slot-fill", action="store_true",
                     help="instead of the stack step: int4 expert slot fill rates (one JSON line)")
     args = ap.parse_args()
+    if (args.summarize_pmc or args.summarize_trace or args.summarize_counters) and not args.command.strip():
+        raise SystemExit("--command: the profiled command is recorded in the summary and must be given")
     if args.summarize_pmc:
         summarize_pmc(*args.summarize_pmc, commands=args.command)
         return
