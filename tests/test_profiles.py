@@ -1,5 +1,7 @@
-"""The committed rocprofv3 summaries name the command that made them, and the
-gate/up traffic figures belong to the current kernel sources (CPU only)."""
+"""The committed rocprofv3 summaries name the command that made them, the
+gate/up traffic figures belong to the current kernel sources, and bench.py's
+host-side refusals (more than one GPU, a summary without its command) hold
+(CPU only)."""
 import glob
 import json
 import os
@@ -29,3 +31,20 @@ def test_traffic_file_names_its_commands_and_kernel_sources():
     # bench.py reports these bytes as roofline.traffic only while the kernel
     # sources match the ones the counters were taken on
     assert t["kernel_hash"] == bench.kernel_source_hash(), "gate/up sources changed since the counters were taken"
+
+
+def test_bench_refuses_more_than_one_gpu():
+    import subprocess
+    import sys
+    for argv, env in ((["--gpus", "2"], {}), (["--gpus", "1"], {"WORLD_SIZE": "2"})):
+        r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), *argv], capture_output=True, text=True,
+                           timeout=120, cwd=ROOT, env={**os.environ, **env})
+        assert r.returncode == 2 and "one GPU only" in r.stderr, (argv, r.returncode, r.stderr[-300:])
+
+
+def test_bench_summarizers_require_the_command():
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--summarize-trace", "/nonexistent", "/dev/null"],
+                       capture_output=True, text=True, timeout=120, cwd=ROOT)
+    assert r.returncode != 0 and "--command" in r.stderr
